@@ -1,0 +1,244 @@
+"""O2: the SegmentPageTable and the page pool, written out from the rules --
+TEST INFRASTRUCTURE.
+
+Rules (SegPagedAttention runtime explainer, section 3: a three-level table
+(layer, head, segment) -> contiguous virtual pages; local heads get pages for
+sink + recent tokens only, global heads for the whole context; local heads keep
+only visible tokens; retrieval heads fetch pages on demand):
+
+* Retention, for the rows q0..N-1 that will read the table: a key is kept iff
+  it is visible to at least one of those rows.
+    GLOBAL / DENSE   one segment [0, N)
+    LOCAL(s, W)      [0, min(s, N))  and  [max(min(s, N), q0 - W + 1), N),
+                     one merged segment when the two touch
+    RETRIEVAL(R)     one gathered segment holding R in order
+* Packing (KV-cache guide section 4.3, block tables): token t of a segment sits
+  in the segment's page t // P at slot t % P; every segment starts on a fresh
+  page; unused tail slots hold zeros.
+* Page ids: units in order u = (l * B + b) * Hkv + h, segments in order, pages
+  in order, each taking the next id of the free list (identity by default).
+
+Table format, version 1 (all int32):
+    header  16 ints  magic 0x53475054, version 1, num_seqs, num_layers, Hq, Hkv,
+                     D, P, num_units, num_pages, num_retr, off_seqs, off_units,
+                     off_pages, off_retr, table_len
+    seqs     4 ints per sequence  N_b, q0_b, dense K/V row offset, Q row offset
+    units   16 ints per unit      class (DENSE stored as GLOBAL), b, l, h, N_b, q0_b,
+                                  sink, window, kv_len, nseg, seg0_pos, seg0_len,
+                                  seg1_pos, seg1_len, page_off, retr_off
+                                  (gathered segment: seg0_pos = -1;
+                                  retr_off = -1 for non-RETRIEVAL units)
+    pages   page id of each table page
+    retr    retrieval positions, units in order
+
+Pool layout (bf16 bits):
+    K page  [D/8][P][8]   K_pool[p, d // 8, slot, d % 8]
+    V page  [P/8][D][8]   V_pool[p, slot // 8, d, slot % 8]
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Tuple
+
+import numpy as np
+
+from workloads import DENSE, GLOBAL, LOCAL, RETRIEVAL, Spec
+
+MAGIC = 0x53475054
+VERSION = 1
+HEADER_INTS, SEQ_INTS, UNIT_INTS = 16, 4, 16
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def retained_segments(kind: int, sink: int, window: int, n: int, q0: int, retr) -> List:
+    """List of segments; a contiguous segment is (pos0, length), a gathered one is
+    ('gathered', positions)."""
+    if kind in (GLOBAL, DENSE):
+        return [(0, n)] if n > 0 else []
+    if kind == LOCAL:
+        a = min(sink, n)
+        w0 = max(a, q0 - window + 1)
+        segs = []
+        if a > 0:
+            segs.append((0, a))
+        if n > w0:
+            if segs and w0 == a:
+                segs = [(0, n)]
+            else:
+                segs.append((w0, n - w0))
+        return segs
+    if kind == RETRIEVAL:
+        r = np.asarray(retr if retr is not None else [], dtype=np.int32)
+        return [("gathered", r)] if len(r) else []
+    raise ValueError(kind)
+
+
+def segment_positions(seg) -> np.ndarray:
+    if seg[0] == "gathered":
+        return np.asarray(seg[1], dtype=np.int64)
+    return np.arange(seg[0], seg[0] + seg[1], dtype=np.int64)
+
+
+def units(spec: Spec):
+    """(u, b, l, h) in table order."""
+    out = []
+    B, H = spec.num_seqs, spec.num_kv_heads
+    for l in range(spec.num_layers):
+        for b in range(B):
+            for h in range(H):
+                out.append(((l * B + b) * H + h, b, l, h))
+    return out
+
+
+def unit_segments(spec: Spec, b: int, l: int, h: int) -> List:
+    kind, sink, window = spec.head_class(l, h)
+    return retained_segments(kind, sink, window, spec.seq_len[b], spec.first_query_pos[b],
+                             spec.retrieval.get((b, l, h)))
+
+
+def table(spec: Spec) -> np.ndarray:
+    """The expected table ints (int32)."""
+    P = spec.page_size
+    B = spec.num_seqs
+    recs, page_ids, retr = [], [], []
+    free = spec.free_list
+    nxt = 0
+    for (u, b, l, h) in units(spec):
+        kind, sink, window = spec.head_class(l, h)
+        segs = unit_segments(spec, b, l, h)
+        rec = [GLOBAL if kind == DENSE else kind, b, l, h, spec.seq_len[b],
+               spec.first_query_pos[b], sink, window, 0, len(segs), 0, 0, 0, 0,
+               len(page_ids), -1]
+        if kind == RETRIEVAL:
+            rec[15] = len(retr)
+        kv_len = 0
+        for si, seg in enumerate(segs):
+            if seg[0] == "gathered":
+                pos0, ln = -1, len(seg[1])
+                retr.extend(int(x) for x in seg[1])
+            else:
+                pos0, ln = seg
+            rec[10 + 2 * si] = pos0
+            rec[11 + 2 * si] = ln
+            kv_len += ln
+            for _ in range(ceil_div(ln, P)):
+                page_ids.append(nxt if free is None else int(free[nxt]))
+                nxt += 1
+        rec[8] = kv_len
+        recs.append(rec)
+    off_seqs = HEADER_INTS
+    off_units = off_seqs + SEQ_INTS * B
+    off_pages = off_units + UNIT_INTS * len(recs)
+    off_retr = off_pages + len(page_ids)
+    total = off_retr + len(retr)
+    hdr = [MAGIC, VERSION, B, spec.num_layers, spec.num_q_heads, spec.num_kv_heads,
+           spec.head_dim, P, len(recs), len(page_ids), len(retr), off_seqs, off_units,
+           off_pages, off_retr, total]
+    seqs = []
+    kvo, qo = spec.kv_row_offsets(), spec.q_row_offsets()
+    for b in range(B):
+        seqs += [spec.seq_len[b], spec.first_query_pos[b], kvo[b], qo[b]]
+    flat = hdr + seqs + [x for r in recs for x in r] + page_ids + retr
+    return np.asarray(flat, dtype=np.int64).astype(np.int32)
+
+
+def num_pages(spec: Spec) -> int:
+    return int(table(spec)[9])
+
+
+def unit_page_ids(spec: Spec, b: int, l: int, h: int, t: np.ndarray = None
+                  ) -> List[Tuple[np.ndarray, List[int]]]:
+    """[(segment positions, [page ids])] for one unit, from the oracle's own table
+    (pass `t = table(spec)` to avoid rebuilding it)."""
+    t = table(spec) if t is None else t
+    off_units, off_pages = int(t[12]), int(t[13])
+    u = (l * spec.num_seqs + b) * spec.num_kv_heads + h
+    rec = t[off_units + UNIT_INTS * u: off_units + UNIT_INTS * (u + 1)]
+    segs = unit_segments(spec, b, l, h)
+    out, p = [], int(rec[14])
+    for seg in segs:
+        pos = segment_positions(seg)
+        npg = ceil_div(len(pos), spec.page_size)
+        out.append((pos, [int(x) for x in t[off_pages + p: off_pages + p + npg]]))
+        p += npg
+    return out
+
+
+def pool_loops(spec: Spec, layer: int, k_bits: np.ndarray, v_bits: np.ndarray,
+               pool_pages: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Expected pool contents after building `layer`, element by element: (K_pool
+    uint16 [pool_pages, D/8, P, 8], V_pool uint16 [pool_pages, P/8, D, 8],
+    written bool [pool_pages]). Pages of other layers are not written (zeros)."""
+    P, D = spec.page_size, spec.head_dim
+    kp = np.zeros((pool_pages, D // 8, P, 8), dtype=np.uint16)
+    vp = np.zeros((pool_pages, P // 8, D, 8), dtype=np.uint16)
+    written = np.zeros(pool_pages, dtype=bool)
+    kvo = spec.kv_row_offsets()
+    tab = table(spec)
+    for b in range(spec.num_seqs):
+        for h in range(spec.num_kv_heads):
+            for pos, pids in unit_page_ids(spec, b, layer, h, tab):
+                for pi, pid in enumerate(pids):
+                    written[pid] = True
+                    for slot in range(P):
+                        t = pi * P + slot
+                        if t >= len(pos):
+                            break  # tail slots stay zero
+                        row = kvo[b] + int(pos[t])
+                        for d in range(D):
+                            kp[pid, d // 8, slot, d % 8] = k_bits[row, h, d]
+                            vp[pid, slot // 8, d, slot % 8] = v_bits[row, h, d]
+    return kp, vp, written
+
+
+def pool(spec: Spec, layer: int, k_bits: np.ndarray, v_bits: np.ndarray,
+         pool_pages: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Same result as pool_loops, one page at a time: the page's token rows
+    [P, D] (zero rows past the segment's end) are regrouped into the K
+    [D/8][P][8] and V [P/8][D][8] layouts."""
+    P, D = spec.page_size, spec.head_dim
+    kp = np.zeros((pool_pages, D // 8, P, 8), dtype=np.uint16)
+    vp = np.zeros((pool_pages, P // 8, D, 8), dtype=np.uint16)
+    written = np.zeros(pool_pages, dtype=bool)
+    kvo = spec.kv_row_offsets()
+    tab = table(spec)
+    for b in range(spec.num_seqs):
+        for h in range(spec.num_kv_heads):
+            for pos, pids in unit_page_ids(spec, b, layer, h, tab):
+                for pi, pid in enumerate(pids):
+                    written[pid] = True
+                    rows = kvo[b] + pos[pi * P:(pi + 1) * P]
+                    kt = np.zeros((P, D), dtype=np.uint16)
+                    vt = np.zeros((P, D), dtype=np.uint16)
+                    kt[:len(rows)] = k_bits[rows, h]
+                    vt[:len(rows)] = v_bits[rows, h]
+                    # K: element (slot, d) -> [d // 8][slot][d % 8]
+                    kp[pid] = kt.reshape(P, D // 8, 8).transpose(1, 0, 2)
+                    # V: element (slot, d) -> [slot // 8][d][slot % 8]
+                    vp[pid] = vt.reshape(P // 8, 8, D).transpose(0, 2, 1)
+    return kp, vp, written
+
+
+def kv_len_total(spec: Spec, layers=None) -> int:
+    """Retained tokens summed over all units (of the given layers)."""
+    tot = 0
+    for (u, b, l, h) in units(spec):
+        if layers is not None and l not in layers:
+            continue
+        for seg in unit_segments(spec, b, l, h):
+            tot += len(segment_positions(seg))
+    return tot
+
+
+def dense_kv_bytes(num_layers: int, num_kv_heads: int, head_dim: int, tokens: int,
+                   bytes_per_elem: int = 2) -> int:
+    """KV-cache size of a dense cache (KV-guide section 3.2):
+    2 (K and V) x layers x KV heads x head dim x tokens x bytes per element."""
+    return 2 * num_layers * num_kv_heads * head_dim * tokens * bytes_per_elem
+
+
+def retained_kv_bytes(spec: Spec, bytes_per_elem: int = 2) -> int:
+    """K and V bytes the SegPaged cache keeps (tail padding excluded)."""
+    return 2 * spec.head_dim * bytes_per_elem * kv_len_total(spec)
