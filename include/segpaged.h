@@ -1,0 +1,217 @@
+/*
+ * segpaged.h -- SegPagedAttention for AMD Instinct MI355X (gfx950).
+ *
+ * A KV cache paged per (layer, KV head, segment) and mask-free attention that
+ * reads each head's own page list and length.
+ *
+ * Sources (the method this library implements):
+ *   [RT]  "How different attention heads see different contexts: RedKnot
+ *         SegPagedAttention paged-attention runtime design" (m.nxbn.cn/news/186605)
+ *         -- section 2: the four per-(layer, KV head) policies; section 3: the
+ *         (layer, head, segment) -> contiguous virtual pages table, the page
+ *         pool, building per-head storage from dense KV; section 4: the
+ *         mask-free fused varlen kernel and the dense+mask equivalence check;
+ *         section 5: layout must be built once at KV-write time.
+ *   [SUM] RedKnot summary (m.youleyou.com/wenzhang/3087667.html) -- head-class
+ *         sparsification; SegPagedAttention as storage + execution substrate.
+ *   [KV]  KV-cache guide (zhangjiuzhi.com/?p=3078) -- section 4.3 block tables,
+ *         section 5.3 GQA grouping, section 10.2 online softmax.
+ *
+ * Conventions for every call:
+ *   - All functions are C, never throw, and return a segpaged_status (0 = OK,
+ *     negative = error). Arguments are validated before any GPU work is enqueued;
+ *     on error nothing is enqueued and outputs are untouched.
+ *   - The library never allocates or frees device memory and never synchronises
+ *     a stream. Device buffers (pools, table, Q, O, LSE, workspace, dense K/V)
+ *     are owned by the caller. `stream` is a hipStream_t passed as void*
+ *     (NULL = the null stream) on the current HIP device.
+ *   - Asynchronous kernel faults surface at the caller's next synchronisation.
+ *   - bf16 tensors are raw IEEE bfloat16 bits, row-major, 16-byte aligned.
+ *   - A plan is immutable after creation; concurrent calls that share a plan are
+ *     safe. A plan must outlive all work enqueued with it.
+ */
+#ifndef SEGPAGED_H
+#define SEGPAGED_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SEGPAGED_API __attribute__((visibility("default")))
+
+typedef enum {
+  SEGPAGED_OK = 0,
+  SEGPAGED_EINVAL = -1,        /* invalid argument (null/misaligned pointer, bad spec value) */
+  SEGPAGED_EUNSUPPORTED = -2,  /* valid but not supported by this build (head_dim, page size, group) */
+  SEGPAGED_ENOSPACE = -3,      /* pool capacity, free list, table or workspace too small */
+  SEGPAGED_EHIP = -4,          /* a HIP runtime call or kernel launch failed */
+  SEGPAGED_ESTATE = -5         /* call does not fit the plan (e.g. layer out of range) */
+} segpaged_status;
+
+/* Head classes, one per (layer, KV head) [RT section 2]. All are causal (key j <= query i).
+ *   GLOBAL      every earlier token
+ *   LOCAL       the first `sink` tokens and the `window` most recent ones
+ *               (j < sink  or  i - window < j), the current token included
+ *   RETRIEVAL   only a given sorted set of token positions
+ *   DENSE       attends like GLOBAL (its RoPE re-alignment is outside attention) */
+typedef enum {
+  SEGPAGED_GLOBAL = 0,
+  SEGPAGED_LOCAL = 1,
+  SEGPAGED_RETRIEVAL = 2,
+  SEGPAGED_DENSE = 3
+} segpaged_kind;
+
+/* What to plan. All pointers are HOST memory and are read only during
+ * segpaged_plan_create. Units are u = (l * num_seqs + b) * num_kv_heads + h. */
+typedef struct {
+  int32_t num_seqs;             /* B >= 1 */
+  int32_t num_layers;           /* >= 1 */
+  int32_t num_q_heads;          /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;         /* Hkv >= 1; query head hq reads KV head hq / (Hq/Hkv) [KV 5.3] */
+  int32_t head_dim;             /* D in {64, 128} */
+  int32_t page_size;            /* P in {16, 32, 64, 128} tokens per page */
+  const int32_t* seq_len;       /* [B]  N_b >= 0 tokens in the cache, current token included */
+  const int32_t* first_query_pos; /* [B] q0_b in [0, max(N_b-1, 0)]: lowest query position that
+                                    will read this table (0 = prefill form, N_b-1 = decode form) */
+  const int32_t* kind;          /* [L*Hkv] segpaged_kind, index l * Hkv + h */
+  const int32_t* sink;          /* [L*Hkv] sink tokens >= 0 (LOCAL) */
+  const int32_t* window;        /* [L*Hkv] window >= 1 (LOCAL) */
+  const int64_t* retr_offsets;  /* [U+1] CSR over units into retr_pos; NULL if no RETRIEVAL head */
+  const int32_t* retr_pos;      /* sorted unique positions in [0, N_b) per RETRIEVAL unit */
+  const int32_t* free_list;     /* page ids in allocation order, NULL = 0, 1, 2, ... */
+  int64_t free_list_len;        /* entries in free_list */
+  int64_t capacity_pages;       /* pages of the pool the caller provides; 0 = exactly the pages needed.
+                                   Every page id must be < capacity. */
+  int32_t decode_split_tokens;  /* keys per decode work item, a multiple of 64; 0 = automatic */
+  int32_t reserved;
+} segpaged_spec;
+
+/* Sizes the caller allocates. */
+typedef struct {
+  int64_t num_pages;        /* pages the table uses */
+  int64_t pool_pages;       /* pages each pool tensor must hold (= capacity) */
+  int64_t pool_bytes;       /* bytes of ONE pool tensor: pool_pages * P * D * 2 */
+  int64_t table_int32s;     /* int32 elements of the device table (table + work lists) */
+  int64_t table_len;        /* leading int32s that form the SegmentPageTable proper */
+  int64_t num_units;        /* L * B * Hkv */
+  int64_t q_rows;           /* T_q = sum_b (N_b - q0_b): rows of one layer's Q / O / LSE */
+  int64_t kv_rows;          /* T_total = sum_b N_b: rows of one layer's dense K / V */
+  int64_t decode_items;     /* decode work items, all layers */
+  int64_t prefill_items;    /* prefill work items, all layers */
+  int64_t decode_workspace_bytes;  /* workspace a decode call over all layers needs */
+  int64_t prefill_workspace_bytes; /* workspace a prefill call needs (0 in this version) */
+} segpaged_sizes;
+
+/* Algorithmic work of one layer (or all layers when layer = -1), for throughput
+ * and roofline accounting. */
+typedef struct {
+  int64_t units;
+  int64_t pages;
+  int64_t retained_tokens;   /* keys stored in the pool, summed over units (padding excluded) */
+  int64_t decode_tokens;     /* keys the decode row (position N_b - 1) sees, summed over units */
+  int64_t prefill_pairs;     /* visible (query row, key) pairs per KV-head unit over rows q0..N-1;
+                                times G gives pairs over Q heads; flops = 4 * D * G * pairs */
+  int64_t q_rows;            /* query rows over units (each row serves G query heads) */
+  int64_t decode_items;
+  int64_t prefill_items;
+} segpaged_stats;
+
+typedef struct segpaged_plan segpaged_plan;  /* opaque, host heap */
+
+/* Plan a SegmentPageTable from a spec [RT section 3]: per unit, the retained
+ * segments (keys visible to some row >= q0: GLOBAL/DENSE all N; LOCAL the sink
+ * and the window reaching back from q0, merged when they touch; RETRIEVAL the
+ * given set, gathered), ceil(len / P) pages per segment packed from the segment
+ * start, page ids taken in unit/segment/page order from the free list; plus the
+ * per-head varlen work lists of the prefill and decode kernels [RT section 4].
+ * Host only: makes no HIP call, so it runs without a GPU. The layout is built
+ * once here and reused by every call [RT section 5].
+ * Returns EINVAL for a bad spec, EUNSUPPORTED for an unsupported D/P/group,
+ * ENOSPACE when the free list or capacity is too small. *plan is NULL on error. */
+SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan** plan,
+                                      segpaged_sizes* sizes);
+
+SEGPAGED_API void segpaged_plan_destroy(segpaged_plan* plan);
+
+SEGPAGED_API int segpaged_plan_sizes(const segpaged_plan* plan, segpaged_sizes* sizes);
+
+/* Host copy of the whole device table image (int32 [table_int32s]). The first
+ * table_len ints are the SegmentPageTable, format version 1:
+ *   header  16: magic 0x53475054, version 1, B, L, Hq, Hkv, D, P, num_units,
+ *               num_pages, num_retr, off_seqs, off_units, off_pages, off_retr, table_len
+ *   seqs    4 per sequence: N_b, q0_b, dense K/V row offset, Q row offset
+ *   units   16 per unit: class (DENSE stored as GLOBAL), b, l, h, N_b, q0_b, sink,
+ *           window, kv_len, nseg, seg0_pos, seg0_len, seg1_pos, seg1_len, page_off,
+ *           retr_off (seg0_pos = -1 for a gathered RETRIEVAL segment; retr_off = -1
+ *           for other classes; unused segment fields 0)
+ *   pages   page id of each table page (a unit's pages start at page_off)
+ *   retr    positions of the RETRIEVAL segments, units in order
+ * The ints after table_len are the kernels' work lists (not part of the format).
+ * ENOSPACE if n < table_int32s. */
+SEGPAGED_API int segpaged_plan_table_host(const segpaged_plan* plan, int32_t* out, int64_t n);
+
+/* Work counts of one layer (layer = -1: all layers). ESTATE if layer is out of range. */
+SEGPAGED_API int segpaged_plan_stats(const segpaged_plan* plan, int32_t layer,
+                                     segpaged_stats* stats);
+
+/* build_segpaged_cache [RT section 3]: upload the table slice of `layer` (or the
+ * whole table when layer = -1) into d_table, then scatter that layer's retained
+ * tokens from dense K/V into their pages:
+ *   K page p: bf16 [D/8][P][8], element (slot, d) at ((d/8)*P + slot)*8 + d%8
+ *   V page p: bf16 [P/8][D][8], element (slot, d) at ((slot/8)*D + d)*8 + slot%8
+ * Unused tail slots are written as zero. Pages of other layers are untouched.
+ *   k_dense, v_dense  device bf16 [T_total][Hkv][D] of this layer
+ *                     ([L][T_total][Hkv][D] when layer = -1); sequences packed
+ *                     in order, sequence b at rows sum_{b'<b} N_b'
+ *   d_table           device int32 [table_int32s]
+ *   k_pool, v_pool    device bf16, pool_bytes each
+ * The upload reads the plan's host memory; keep the plan alive. */
+SEGPAGED_API int segpaged_build(const segpaged_plan* plan, int32_t layer,
+                                const void* k_dense, const void* v_dense, int32_t* d_table,
+                                void* k_pool, void* v_pool, void* stream);
+
+/* Mask-free prefill [RT section 4]: for every query row i in [q0_b, N_b) of every
+ * sequence and every Q head hq (KV head h = hq / G):
+ *     O = sum_{j in vis(i)} softmax_j(scale * q_i . k_j) v_j,   LSE = log sum exp
+ * reading only the pages of (layer, b, h); blocks no row of a tile can see are
+ * never read, and no mask tensor exists.
+ *   q     device bf16 [T_q][Hq][D] (rows q0_b..N_b-1 of each sequence, packed in
+ *         sequence order); [L][T_q][Hq][D] when layer = -1
+ *   o     device bf16, same shape as q (written)
+ *   lse   device fp32 [T_q][Hq] natural-log LSE ([L][T_q][Hq] when layer = -1), or NULL
+ *   scale softmax scale, typically 1/sqrt(D)
+ *   workspace/workspace_bytes: prefill_workspace_bytes (may be NULL when 0)
+ * d_table, k_pool, v_pool must hold what segpaged_build wrote for this layer.
+ * A row whose visible set is empty (RETRIEVAL only) gets O = 0, LSE = -inf. */
+SEGPAGED_API int segpaged_prefill(const segpaged_plan* plan, int32_t layer, const void* q,
+                                  const int32_t* d_table, const void* k_pool,
+                                  const void* v_pool, float scale, void* o, float* lse,
+                                  void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Split-K decode [RT section 4; KV section 10.2]: the query at position N_b - 1 of
+ * each sequence attends to every key it can see. Work items are (unit, key
+ * range) slices; each writes fp32 partials (running max, normaliser, unnormalised
+ * output) for the G query heads of its unit into `workspace`, and a combine pass
+ * merges them with the log-sum-exp rule into O and LSE.
+ *   q     device bf16 [B][Hq][D] ([L][B][Hq][D] when layer = -1)
+ *   o     device bf16, same shape (written)
+ *   lse   device fp32 [B][Hq] ([L][B][Hq]), or NULL
+ *   workspace  device memory of at least decode_workspace_bytes (ENOSPACE otherwise)
+ * Works on any plan form; a decode-form plan (q0 = N-1) stores only what the row sees. */
+SEGPAGED_API int segpaged_decode(const segpaged_plan* plan, int32_t layer, const void* q,
+                                 const int32_t* d_table, const void* k_pool, const void* v_pool,
+                                 float scale, void* o, float* lse, void* workspace,
+                                 int64_t workspace_bytes, void* stream);
+
+SEGPAGED_API const char* segpaged_status_str(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+SEGPAGED_API int segpaged_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEGPAGED_H */

@@ -1,0 +1,13 @@
+"""SegPagedAttention on AMD MI355X (gfx950).
+
+A KV cache paged per (layer, KV head, segment) -- global heads keep the whole
+context, local heads only their sink and recent window, retrieval heads a given
+token set -- and mask-free prefill/decode kernels that read each head's own
+pages. The compute path is libsegpaged.so (HIP, gfx950); this package is its
+ctypes binding.
+"""
+from .segpaged import (DENSE, GLOBAL, LIB_PATH, LOCAL, RETRIEVAL, Plan, SegPagedError,
+                       Sizes, Stats, build, decode, library, prefill)
+
+__all__ = ["Plan", "build", "prefill", "decode", "library", "SegPagedError", "Sizes", "Stats",
+           "GLOBAL", "LOCAL", "RETRIEVAL", "DENSE", "LIB_PATH"]

@@ -1,0 +1,772 @@
+// SegPagedAttention kernels for MI355X (gfx950, wave64, bf16 MFMA) and the C-ABI
+// entry points that launch them.
+//
+//   build_kernel           build_segpaged_cache: dense K/V rows -> per-head pages
+//   decode_partial_kernel  split-K decode: one wave per (unit, key range) item
+//   decode_combine_kernel  log-sum-exp merge of the items of each unit
+//   prefill_kernel         GQA flash-style prefill over each head's own pages
+//
+// Method: SegPagedAttention runtime explainer, section 3 (per-(layer, head,
+// segment) page table and pool; local heads keep only sink + recent tokens) and
+// section 4 (one fused varlen pass, each head at its own length, no mask).
+// Online softmax recurrence: KV-cache guide, section 10.2.
+//
+// Pool layout (bf16): K page [D/8][P][8] and V page [P/8][D][8]. Every MFMA
+// operand a lane needs is then one 16-byte load: 8 consecutive head dims of a
+// key (K) or 8 consecutive keys of one head dim (V).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "plan.hpp"
+
+using namespace segpaged;
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// decode partial per (item, query column): D floats of unnormalised output, then
+// the running max (log2 units) and the normaliser; padded to keep float4 stores aligned
+template <int D>
+constexpr int kWsStride = D + 4;
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+// ---------------------------------------------------------------------------
+// build: one workgroup per page. Rows are read coalesced into LDS, then written
+// out in the K [D/8][P][8] and V [P/8][D][8] page layouts. Tail slots are zero.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void build_kernel(
+    const int32_t* __restrict__ tab, int32_t off_seqs, int32_t off_units, int32_t off_pages,
+    int32_t off_retr, int32_t unit_b, int32_t unit_e, int32_t page_b, int32_t Hkv, int32_t P,
+    int32_t log2P, const uint16_t* __restrict__ kd, const uint16_t* __restrict__ vd,
+    int64_t dense_layer_stride, uint16_t* __restrict__ kp, uint16_t* __restrict__ vp) {
+  constexpr int KCH = D / 8;        // 16-byte chunks per row
+  constexpr int PITCH = D + 8;      // LDS row pitch (elements), breaks bank aliasing
+  __shared__ __attribute__((aligned(16))) uint16_t rows[128 * PITCH];
+
+  const int32_t pg = page_b + (int32_t)blockIdx.x;  // page slot in the table
+  // owning unit: last unit in [unit_b, unit_e) whose page_off <= pg
+  int32_t lo = unit_b, hi = unit_e - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (tab[off_units + kUnitInts * mid + U_PAGEOFF] <= pg) lo = mid; else hi = mid - 1;
+  }
+  const int32_t* ur = tab + off_units + kUnitInts * lo;
+  const int32_t b = ur[U_B], l = ur[U_L], h = ur[U_H];
+  const int32_t pr = pg - ur[U_PAGEOFF];
+  const int32_t np0 = (ur[U_S0LEN] + P - 1) >> log2P;
+  const int sg = pr < np0 ? 0 : 1;
+  const int32_t t0 = (sg == 0 ? pr : pr - np0) << log2P;  // first segment token of this page
+  const int32_t pos0 = ur[U_S0POS + 2 * sg], len = ur[U_S0LEN + 2 * sg];
+  const int32_t count = min(P, len - t0);
+  const bool gathered = pos0 < 0;
+  const int32_t* rpos = tab + off_retr + ur[U_RETROFF] + t0;
+  const int64_t kvrow0 = tab[off_seqs + kSeqInts * b + S_KVOFF];
+  const int64_t lstride = (int64_t)l * dense_layer_stride;
+  const int32_t pid = tab[off_pages + pg];
+  uint16_t* kpage = kp + (int64_t)pid * P * D;
+  uint16_t* vpage = vp + (int64_t)pid * P * D;
+  const int nchunk = P * KCH;
+
+  for (int pass = 0; pass < 2; ++pass) {
+    const uint16_t* src = pass == 0 ? kd : vd;
+    for (int c = threadIdx.x; c < nchunk; c += 256) {
+      const int slot = c / KCH, dc = c % KCH;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (slot < count) {
+        const int64_t pos = gathered ? rpos[slot] : pos0 + t0 + slot;
+        v = ld16(src + lstride + ((kvrow0 + pos) * Hkv + h) * D + dc * 8);
+      }
+      st16(&rows[slot * PITCH + dc * 8], v);
+    }
+    __syncthreads();
+    if (pass == 0) {
+      for (int c = threadIdx.x; c < nchunk; c += 256) {  // K: chunk (dc, slot)
+        const int dc = c >> log2P, slot = c & (P - 1);
+        st16(kpage + ((int64_t)dc * P + slot) * 8, ld16(&rows[slot * PITCH + dc * 8]));
+      }
+    } else {
+      for (int c = threadIdx.x; c < nchunk; c += 256) {  // V: chunk (tc, d)
+        const int tc = c / D, d = c % D;
+        u32x4 v;
+        v.x = rows[(8 * tc + 0) * PITCH + d] | ((uint32_t)rows[(8 * tc + 1) * PITCH + d] << 16);
+        v.y = rows[(8 * tc + 2) * PITCH + d] | ((uint32_t)rows[(8 * tc + 3) * PITCH + d] << 16);
+        v.z = rows[(8 * tc + 4) * PITCH + d] | ((uint32_t)rows[(8 * tc + 5) * PITCH + d] << 16);
+        v.w = rows[(8 * tc + 6) * PITCH + d] | ((uint32_t)rows[(8 * tc + 7) * PITCH + d] << 16);
+        st16(vpage + ((int64_t)tc * D + d) * 8, v);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode, split-K. One wave per work item (unit, slots [lo, hi)), all of which
+// the decode row sees. Per 32-key step, with v_mfma_f32_16x16x32_bf16:
+//   S^T[16 keys][16 cols] = K[keys][D] . Q^T[D][cols]   (cols = the G query heads)
+//   O^T[16 dims][16 cols] += V^T[dims][32 keys] . P^T[32 keys][cols]
+// The key order inside an S^T tile is permuted so that the 8 keys a lane holds
+// after the softmax are 8 consecutive slots: exactly one V brick.
+// Writes (unnormalised O^T, running max in log2 units, normaliser) per column.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void decode_partial_kernel(
+    const int32_t* __restrict__ tab, int32_t off_units, int32_t off_pages, int32_t off_dec,
+    int32_t item_b, int32_t item_e, const uint16_t* __restrict__ q, int64_t q_layer_stride,
+    const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, float* __restrict__ ws,
+    int32_t G, int32_t Hq, int32_t P, int32_t log2P, float c) {
+  constexpr int KS = D / 32;  // k-steps of the QK^T contraction
+  constexpr int DT = D / 16;  // 16-row tiles of O^T
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int32_t it = item_b + (int32_t)blockIdx.x * 4 + wave;
+  if (it >= item_e) return;
+  const int32_t* item = tab + off_dec + kDecItemInts * it;
+  const int32_t u = item[0], lo = item[1], hi = item[2];
+  const int32_t* ur = tab + off_units + kUnitInts * u;
+  const int32_t b = ur[U_B], l = ur[U_L], h = ur[U_H];
+  const int32_t* pages = tab + off_pages + ur[U_PAGEOFF];
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t PD = (int64_t)P * D;
+
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qrow = q + (int64_t)l * q_layer_stride + ((int64_t)b * Hq + h * G + n) * D + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (n < G) v = ld16(qrow + ks * 32);
+      qf[ks] = as_bf16x8(v);
+    }
+  }
+
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int r = lane & 15;
+  const int koff = 8 * (r >> 2) + (r & 3);  // key of S^T row r in tile t: koff + 4t
+
+  for (int32_t s0 = lo & ~7; s0 < hi; s0 += 32) {
+    // K operand: row r of tile t <- key s0 + koff + 4t, dims (4ks + g)*8 .. +7
+    bf16x8 kf[2][KS];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int32_t key = s0 + koff + 4 * t;
+      const bool ok = key < hi;
+      const int32_t pid = ok ? pages[key >> log2P] : 0;
+      const uint16_t* base = kp + pid * PD + (int64_t)(key & (P - 1)) * 8 + (int64_t)g * P * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (ok) v = ld16(base + (int64_t)ks * 4 * P * 8);
+        kf[t][ks] = as_bf16x8(v);
+      }
+    }
+    // V operand: row (dim) 16dt + r, keys s0 + 8g .. +7 (one brick)
+    bf16x8 vf[DT];
+    {
+      const int32_t key = s0 + 8 * g;
+      const bool ok = key < hi;
+      const int32_t pid = ok ? pages[key >> log2P] : 0;
+      const uint16_t* base = vp + pid * PD + ((int64_t)((key & (P - 1)) >> 3) * D + r) * 8;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (ok) v = ld16(base + dt * 16 * 8);
+        vf[dt] = as_bf16x8(v);
+      }
+    }
+    f32x4 st[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][ks], qf[ks], st[t], 0, 0, 0);
+    }
+    // lane (n, g) reg i of tile t holds key s0 + 8g + 4t + i
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t key = s0 + 8 * g + 4 * t + i;
+        if (key < lo || key >= hi) st[t][i] = -INFINITY;
+        mx = fmaxf(mx, st[t][i]);
+      }
+    mx = wave_max_xor(mx, 16);
+    mx = wave_max_xor(mx, 32);
+    const float m_new = fmaxf(m, mx * c);  // every step holds a visible key: finite
+    const float alpha = fast_exp2(m - m_new);
+    float p[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[4 * t + i] = fast_exp2(fmaf(st[t][i], c, -m_new));
+        ps += p[4 * t + i];
+      }
+    lsum = lsum * alpha + ps;
+    m = m_new;
+    u32x4 pw;
+    pw.x = pack_bf16x2(p[0], p[1]);
+    pw.y = pack_bf16x2(p[2], p[3]);
+    pw.z = pack_bf16x2(p[4], p[5]);
+    pw.w = pack_bf16x2(p[6], p[7]);
+    const bf16x8 pf = as_bf16x8(pw);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      acc[dt] *= alpha;
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf, acc[dt], 0, 0, 0);
+    }
+  }
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (n < G) {
+    float* w = ws + ((int64_t)(it - item_b) * G + n) * kWsStride<D>;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4*>(w + 16 * dt + 4 * g) = acc[dt];  // dims 16dt + 4g + i
+    if (g == 0) {
+      w[D] = m;
+      w[D + 1] = lsum;
+    }
+  }
+}
+
+// One wave per (unit, query head of its group): merge the unit's item partials.
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(
+    const int32_t* __restrict__ tab, int32_t off_units, int32_t off_decunits, int32_t unit_b,
+    int32_t unit_e, int32_t item_b, const float* __restrict__ ws, int32_t G, int32_t Hq,
+    int32_t B, uint16_t* __restrict__ o, float* __restrict__ lse, int32_t all_layers) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t idx = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t u = unit_b + idx / G;
+  const int j = (int)(idx % G);
+  if (u >= unit_e) return;
+  const int32_t* ur = tab + off_units + kUnitInts * u;
+  const int32_t b = ur[U_B], l = ur[U_L], h = ur[U_H];
+  const int32_t ib = tab[off_decunits + 2 * u], ie = tab[off_decunits + 2 * u + 1];
+  const int64_t row = (all_layers ? (int64_t)l * B * Hq : 0) + (int64_t)b * Hq + h * G + j;
+  constexpr int PER = D / 64;
+  float m = -INFINITY;
+  for (int32_t it = ib; it < ie; ++it)
+    m = fmaxf(m, ws[((int64_t)(it - item_b) * G + j) * kWsStride<D> + D]);
+  float accv[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) accv[k] = 0.f;
+  float lsum = 0.f;
+  for (int32_t it = ib; it < ie; ++it) {
+    const float* w = ws + ((int64_t)(it - item_b) * G + j) * kWsStride<D>;
+    const float sc = fast_exp2(w[D] - m);
+    lsum += w[D + 1] * sc;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) accv[k] += w[lane + 64 * k] * sc;
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+    o[row * D + lane + 64 * k] = __builtin_bit_cast(uint16_t, (__bf16)(accv[k] * inv));
+  if (lse && lane == 0) lse[row] = lsum > 0.f ? (m + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// prefill. One workgroup (4 waves) per tile of 128 query rows = the G query
+// heads of one KV head x (128 / G) consecutive positions, so every staged K/V
+// block serves all G heads. Keys stream in blocks of 64 slots through LDS
+// (double-buffered; the LDS tiles have the page layouts, so a P = 64 page is
+// copied verbatim). Per block and wave (32 query rows), v_mfma_f32_32x32x16_bf16:
+//   S^T[32 keys][32 rows] = K . Q^T    (2 tiles cover the 64 keys)
+//   O^T[32 dims][32 rows] += V^T . P^T  (D/32 tiles)
+// Only blocks that some row of the tile can see are visited; blocks every row
+// sees entirely skip the per-element predicate.
+// ---------------------------------------------------------------------------
+// Up to four runs of consecutive key blocks, kept in named scalars (no
+// dynamically indexed private array).
+struct Runs {
+  int32_t n = 0;
+  int32_t s0 = 0, a0 = 0, c0 = 0, s1 = 0, a1 = 0, c1 = 0, s2 = 0, a2 = 0, c2 = 0, s3 = 0, a3 = 0;
+  int32_t total = 0;  // blocks over all runs; c_k = blocks before run k + 1
+  __device__ void add(int32_t seg, int32_t kb0, int32_t kb1) {
+    const int32_t cnt = kb1 - kb0;
+    if (n == 0) { s0 = seg; a0 = kb0; c0 = cnt; }
+    else if (n == 1) { s1 = seg; a1 = kb0; c1 = c0 + cnt; }
+    else if (n == 2) { s2 = seg; a2 = kb0; c2 = c1 + cnt; }
+    else { s3 = seg; a3 = kb0; }
+    total += cnt;
+    ++n;
+  }
+  // block k of the sequence -> (segment, block index within the segment)
+  __device__ void at(int32_t k, int& seg, int32_t& kb) const {
+    if (k < c0 || n == 1) { seg = s0; kb = a0 + k; }
+    else if (k < c1 || n == 2) { seg = s1; kb = a1 + k - c0; }
+    else if (k < c2 || n == 3) { seg = s2; kb = a2 + k - c1; }
+    else { seg = s3; kb = a3 + k - c2; }
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_kernel(
+    const int32_t* __restrict__ tab, int32_t off_seqs, int32_t off_units, int32_t off_pages,
+    int32_t off_retr, int32_t off_pre, int32_t item_b, int32_t item_e,
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ o, float* __restrict__ lse,
+    int64_t q_layer_stride, int64_t lse_layer_stride, const uint16_t* __restrict__ kp,
+    const uint16_t* __restrict__ vp, int32_t G, int32_t Hq, int32_t P, int32_t log2P, float c) {
+  constexpr int KCH = D / 8;          // 16 B chunks per key row
+  constexpr int KSTEP = D / 16;       // k-steps of QK^T
+  constexpr int MD = D / 32;          // O^T tiles
+  constexpr int KLOAD = KCH * 64 / 256;  // K chunks per thread per block
+  constexpr int VLOAD = 8 * D / 256;     // V chunks per thread per block
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][KCH * 64 * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][8 * D * 8];
+
+  const int32_t it = item_b + (int32_t)blockIdx.x;
+  if (it >= item_e) return;
+  const int32_t u = tab[off_pre + kPreItemInts * it];
+  const int32_t r0 = tab[off_pre + kPreItemInts * it + 1];
+  const int32_t* ur = tab + off_units + kUnitInts * u;
+  const int32_t kind = ur[U_KIND], b = ur[U_B], l = ur[U_L], h = ur[U_H], N = ur[U_N];
+  const int32_t q0 = ur[U_Q0], sink = ur[U_SINK], win = ur[U_WIN], nseg = ur[U_NSEG];
+  const int32_t* pages = tab + off_pages + ur[U_PAGEOFF];
+  const int32_t* rpos = tab + off_retr + ur[U_RETROFF];
+  const int32_t qrow0 = tab[off_seqs + kSeqInts * b + S_QOFF];
+  const int32_t BQ = kPrefillRows / G;
+  const int32_t r1 = min(N, r0 + BQ), rmax = r1 - 1;
+  const int64_t PD = (int64_t)P * D;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, g = lane >> 5;
+  const int row = 32 * wave + n;
+  const int32_t pq = row / G, j = row % G;
+  const int32_t qpos = r0 + pq;
+  const bool row_ok = pq < r1 - r0;
+  const int64_t orow = (int64_t)qrow0 + (qpos - q0);
+  const int hq = h * G + j;
+
+  bf16x8 qf[KSTEP];
+  {
+    const uint16_t* qp = q + (int64_t)l * q_layer_stride + (orow * Hq + hq) * D + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEP; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row_ok) v = ld16(qp + ks * 16);
+      qf[ks] = as_bf16x8(v);
+    }
+  }
+
+  // ---- block runs this tile visits (uniform across the workgroup)
+  const int32_t sp0 = ur[U_S0POS], sl0 = ur[U_S0LEN];
+  const int32_t sp1 = ur[U_S1POS], sl1 = ur[U_S1LEN];
+  const int32_t sb1 = ((sl0 + P - 1) >> log2P) << log2P;  // slot base of segment 1
+  Runs runs;
+  for (int s = 0; s < nseg; ++s) {
+    const int32_t pos0 = s ? sp1 : sp0, len = s ? sl1 : sl0;
+    if (pos0 < 0) {  // gathered: keys with position <= rmax form a prefix
+      int32_t a = 0, z = len;
+      while (a < z) {
+        const int32_t mid = (a + z) >> 1;
+        if (rpos[mid] <= rmax) a = mid + 1; else z = mid;
+      }
+      if (a > 0) runs.add(s, 0, (a + 63) >> 6);
+    } else if (kind == SEGPAGED_LOCAL) {
+      const int32_t ahi = min(len, min(sink, rmax + 1) - pos0);
+      const int32_t blo = max(0, r0 - win + 1 - pos0);
+      const int32_t bhi = min(len, rmax + 1 - pos0);
+      const int32_t A1 = ahi > 0 ? (ahi + 63) >> 6 : 0;
+      const int32_t B0 = blo >> 6, B1 = bhi > blo ? (bhi + 63) >> 6 : B0;
+      if (A1 > 0 && B1 > B0 && B0 <= A1) {
+        runs.add(s, 0, max(A1, B1));
+      } else {
+        if (A1 > 0) runs.add(s, 0, A1);
+        if (B1 > B0) runs.add(s, B0, B1);
+      }
+    } else {
+      const int32_t hi = min(len, rmax + 1 - pos0);
+      if (hi > 0) runs.add(s, 0, (hi + 63) >> 6);
+    }
+  }
+  const int32_t nblocks = runs.total;
+
+  f32x16 oacc[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[md][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // ---- staging: global -> registers -> LDS
+  u32x4 kreg[KLOAD], vreg[VLOAD];
+  auto stage_load = [&](int s, int32_t kb) {
+    const int32_t len = s ? sl1 : sl0, base = s ? sb1 : 0;
+#pragma unroll
+    for (int i = 0; i < KLOAD; ++i) {
+      const int cidx = tid + 256 * i;
+      const int t = cidx & 63, dc = cidx >> 6;
+      const int32_t off = kb * 64 + t;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (off < len) {
+        const int32_t slot = base + off;
+        v = ld16(kp + pages[slot >> log2P] * PD + ((int64_t)dc * P + (slot & (P - 1))) * 8);
+      }
+      kreg[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < VLOAD; ++i) {
+      const int cidx = tid + 256 * i;
+      const int d = cidx % D, tc = cidx / D;
+      const int32_t off = kb * 64 + 8 * tc;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (off < len) {
+        const int32_t slot = base + off;
+        v = ld16(vp + pages[slot >> log2P] * PD + ((int64_t)((slot & (P - 1)) >> 3) * D + d) * 8);
+      }
+      vreg[i] = v;
+    }
+  };
+  auto stage_store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KLOAD; ++i) st16(&sK[buf][(tid + 256 * i) * 8], kreg[i]);
+#pragma unroll
+    for (int i = 0; i < VLOAD; ++i) st16(&sV[buf][(tid + 256 * i) * 8], vreg[i]);
+  };
+
+  // S^T row rho of a 32-key tile <- key 16(q'/2) + 8gg + 4(q'%2) + e', rho = 8q' + 4gg + e'
+  const int rq = n >> 3, rgg = (n >> 2) & 1, re = n & 3;
+  const int tokA = 16 * (rq >> 1) + 8 * rgg + 4 * (rq & 1) + re;
+
+  if (nblocks > 0) {
+    int s;
+    int32_t kb;
+    runs.at(0, s, kb);
+    stage_load(s, kb);
+    stage_store(0);
+    __syncthreads();
+  }
+  for (int32_t blk = 0; blk < nblocks; ++blk) {
+    const int buf = blk & 1;
+    int s;
+    int32_t cur_kb;
+    runs.at(blk, s, cur_kb);
+    const bool has_next = blk + 1 < nblocks;
+    if (has_next) {
+      int ns;
+      int32_t nkb;
+      runs.at(blk + 1, ns, nkb);
+      stage_load(ns, nkb);
+    }
+
+    // ---- S^T = K . Q^T
+    f32x16 sacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[mt][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KSTEP; ++ks) {
+        const bf16x8 a = as_bf16x8(ld16(&sK[buf][((2 * ks + g) * 64 + 32 * mt + tokA) * 8]));
+        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
+      }
+    }
+    // lane (n, g), reg i of tile mt holds key 32mt + 16(i/8) + 8g + (i%8) of the block
+    const int32_t len = s ? sl1 : sl0, pos0 = s ? sp1 : sp0;
+    const int32_t o0 = cur_kb * 64;
+    bool interior = false;
+    if (pos0 >= 0 && o0 + 64 <= len) {
+      const int32_t kp0 = pos0 + o0, kp1 = kp0 + 63;
+      interior = kp1 <= r0;
+      if (kind == SEGPAGED_LOCAL) interior = interior && (kp1 < sink || kp0 > rmax - win);
+    }
+    if (!interior) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int32_t off = o0 + 32 * mt + 16 * (i >> 3) + 8 * g + (i & 7);
+          bool vis = off < len;
+          if (vis) {
+            const int32_t kpos = pos0 >= 0 ? pos0 + off : rpos[off];
+            vis = kpos <= qpos;
+            if (kind == SEGPAGED_LOCAL) vis = vis && (kpos < sink || kpos > qpos - win);
+          }
+          if (!vis) sacc[mt][i] = -INFINITY;
+        }
+    }
+    // ---- online softmax (log2 domain)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][i]);
+    mx = wave_max_xor(mx, 32);
+    const float m_new = fmaxf(m_run, mx * c);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float ps = 0.f;
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = fast_exp2(fmaf(sacc[mt][i], c, -m_use));
+        ps += p[i];
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 w;
+        w.x = pack_bf16x2(p[8 * kk + 0], p[8 * kk + 1]);
+        w.y = pack_bf16x2(p[8 * kk + 2], p[8 * kk + 3]);
+        w.z = pack_bf16x2(p[8 * kk + 4], p[8 * kk + 5]);
+        w.w = pack_bf16x2(p[8 * kk + 6], p[8 * kk + 7]);
+        pf[mt][kk] = as_bf16x8(w);
+      }
+    }
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    // ---- O^T += V^T . P^T
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      oacc[md] *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 a =
+              as_bf16x8(ld16(&sV[buf][((4 * mt + 2 * kk + g) * D + 32 * md + n) * 8]));
+          oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[mt][kk], oacc[md], 0, 0, 0);
+        }
+    }
+    if (has_next) stage_store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (row_ok) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* op = o + (int64_t)l * q_layer_stride + (orow * Hq + hq) * D;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        u32x2 w;
+        w.x = pack_bf16x2(oacc[md][4 * qd + 0] * inv, oacc[md][4 * qd + 1] * inv);
+        w.y = pack_bf16x2(oacc[md][4 * qd + 2] * inv, oacc[md][4 * qd + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + 32 * md + 8 * qd + 4 * g) = w;
+      }
+    if (lse && g == 0)
+      lse[(int64_t)l * lse_layer_stride + orow * Hq + hq] =
+          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host helpers
+// ---------------------------------------------------------------------------
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int check_launch() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? SEGPAGED_OK : SEGPAGED_EHIP;
+}
+
+struct Span {
+  int64_t unit_b, unit_e, page_b, page_e, retr_b, retr_e, dec_b, dec_e, pre_b, pre_e;
+};
+
+Span span_of(const segpaged_plan* pl, int32_t layer) {
+  if (layer >= 0) {
+    const LayerRange& r = pl->layers[layer];
+    return {r.unit_b, r.unit_e, r.page_b, r.page_e, r.retr_b, r.retr_e,
+            r.dec_b, r.dec_e, r.pre_b, r.pre_e};
+  }
+  return {0, pl->num_units, 0, pl->num_pages, 0, pl->num_retr, 0, pl->n_dec, 0, pl->n_pre};
+}
+
+int upload(const segpaged_plan* pl, int32_t* d_table, int64_t off, int64_t count,
+           hipStream_t st) {
+  if (count <= 0) return SEGPAGED_OK;
+  const hipError_t e = hipMemcpyAsync(d_table + off, pl->buf.data() + off, count * sizeof(int32_t),
+                                      hipMemcpyHostToDevice, st);
+  return e == hipSuccess ? SEGPAGED_OK : SEGPAGED_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+SEGPAGED_API int segpaged_build(const segpaged_plan* pl, int32_t layer, const void* k_dense,
+                                const void* v_dense, int32_t* d_table, void* k_pool,
+                                void* v_pool, void* stream) {
+  if (!pl || !k_dense || !v_dense || !d_table || !k_pool || !v_pool) return SEGPAGED_EINVAL;
+  if (!aligned16(k_dense) || !aligned16(v_dense) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned4(d_table))
+    return SEGPAGED_EINVAL;
+  if (layer < -1 || layer >= pl->L) return SEGPAGED_ESTATE;
+  hipStream_t st = (hipStream_t)stream;
+  const Span sp = span_of(pl, layer);
+  int rc;
+  if (layer < 0) {
+    rc = upload(pl, d_table, 0, pl->total_ints, st);
+    if (rc) return rc;
+  } else {
+    const int64_t U = kUnitInts;
+    if ((rc = upload(pl, d_table, 0, pl->off_units, st))) return rc;
+    if ((rc = upload(pl, d_table, pl->off_units + U * sp.unit_b, U * (sp.unit_e - sp.unit_b), st)))
+      return rc;
+    if ((rc = upload(pl, d_table, pl->off_pages + sp.page_b, sp.page_e - sp.page_b, st))) return rc;
+    if ((rc = upload(pl, d_table, pl->off_retr + sp.retr_b, sp.retr_e - sp.retr_b, st))) return rc;
+    if ((rc = upload(pl, d_table, pl->off_decunits + 2 * sp.unit_b, 2 * (sp.unit_e - sp.unit_b),
+                     st)))
+      return rc;
+    if ((rc = upload(pl, d_table, pl->off_dec + kDecItemInts * sp.dec_b,
+                     kDecItemInts * (sp.dec_e - sp.dec_b), st)))
+      return rc;
+    if ((rc = upload(pl, d_table, pl->off_pre + kPreItemInts * sp.pre_b,
+                     kPreItemInts * (sp.pre_e - sp.pre_b), st)))
+      return rc;
+  }
+  const int64_t npages = sp.page_e - sp.page_b;
+  if (npages == 0) return SEGPAGED_OK;
+  const int64_t dstride = layer < 0 ? pl->kv_rows * pl->Hkv * pl->D : 0;
+  auto* kd = (const uint16_t*)k_dense;
+  auto* vd = (const uint16_t*)v_dense;
+  auto* kpp = (uint16_t*)k_pool;
+  auto* vpp = (uint16_t*)v_pool;
+  const dim3 grid((unsigned)npages), block(256);
+  if (pl->D == 128)
+    hipLaunchKernelGGL(build_kernel<128>, grid, block, 0, st, d_table, (int32_t)pl->off_seqs,
+                       (int32_t)pl->off_units, (int32_t)pl->off_pages, (int32_t)pl->off_retr,
+                       (int32_t)sp.unit_b, (int32_t)sp.unit_e, (int32_t)sp.page_b, pl->Hkv, pl->P,
+                       pl->log2P, kd, vd, dstride, kpp, vpp);
+  else
+    hipLaunchKernelGGL(build_kernel<64>, grid, block, 0, st, d_table, (int32_t)pl->off_seqs,
+                       (int32_t)pl->off_units, (int32_t)pl->off_pages, (int32_t)pl->off_retr,
+                       (int32_t)sp.unit_b, (int32_t)sp.unit_e, (int32_t)sp.page_b, pl->Hkv, pl->P,
+                       pl->log2P, kd, vd, dstride, kpp, vpp);
+  return check_launch();
+}
+
+SEGPAGED_API int segpaged_prefill(const segpaged_plan* pl, int32_t layer, const void* q,
+                                  const int32_t* d_table, const void* k_pool, const void* v_pool,
+                                  float scale, void* o, float* lse, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!pl || !q || !d_table || !k_pool || !v_pool || !o) return SEGPAGED_EINVAL;
+  if (!aligned16(q) || !aligned16(o) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned4(d_table) || (lse && !aligned4(lse)))
+    return SEGPAGED_EINVAL;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return SEGPAGED_EINVAL;
+  if (layer < -1 || layer >= pl->L) return SEGPAGED_ESTATE;
+  const Span sp = span_of(pl, layer);
+  const int64_t nitems = sp.pre_e - sp.pre_b;
+  if (nitems == 0) return SEGPAGED_OK;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t qstride = layer < 0 ? pl->q_rows * pl->Hq * pl->D : 0;
+  const int64_t lstride = layer < 0 ? pl->q_rows * pl->Hq : 0;
+  const float c = scale * kLog2e;
+  const dim3 grid((unsigned)nitems), block(256);
+  auto* qq = (const uint16_t*)q;
+  auto* oo = (uint16_t*)o;
+  auto* kpp = (const uint16_t*)k_pool;
+  auto* vpp = (const uint16_t*)v_pool;
+  if (pl->D == 128)
+    hipLaunchKernelGGL(prefill_kernel<128>, grid, block, 0, st, d_table, (int32_t)pl->off_seqs,
+                       (int32_t)pl->off_units, (int32_t)pl->off_pages, (int32_t)pl->off_retr,
+                       (int32_t)pl->off_pre, (int32_t)sp.pre_b, (int32_t)sp.pre_e, qq, oo, lse,
+                       qstride, lstride, kpp, vpp, pl->G, pl->Hq, pl->P, pl->log2P, c);
+  else
+    hipLaunchKernelGGL(prefill_kernel<64>, grid, block, 0, st, d_table, (int32_t)pl->off_seqs,
+                       (int32_t)pl->off_units, (int32_t)pl->off_pages, (int32_t)pl->off_retr,
+                       (int32_t)pl->off_pre, (int32_t)sp.pre_b, (int32_t)sp.pre_e, qq, oo, lse,
+                       qstride, lstride, kpp, vpp, pl->G, pl->Hq, pl->P, pl->log2P, c);
+  return check_launch();
+}
+
+SEGPAGED_API int segpaged_decode(const segpaged_plan* pl, int32_t layer, const void* q,
+                                 const int32_t* d_table, const void* k_pool, const void* v_pool,
+                                 float scale, void* o, float* lse, void* workspace,
+                                 int64_t workspace_bytes, void* stream) {
+  if (!pl || !q || !d_table || !k_pool || !v_pool || !o) return SEGPAGED_EINVAL;
+  if (!aligned16(q) || !aligned16(o) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned4(d_table) || (lse && !aligned4(lse)))
+    return SEGPAGED_EINVAL;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return SEGPAGED_EINVAL;
+  if (layer < -1 || layer >= pl->L) return SEGPAGED_ESTATE;
+  const Span sp = span_of(pl, layer);
+  const int64_t nitems = sp.dec_e - sp.dec_b;
+  const int64_t need = nitems * (int64_t)pl->G * (pl->D + 4) * 4;
+  if (need > 0 && (!workspace || !aligned16(workspace))) return SEGPAGED_EINVAL;
+  if (workspace_bytes < need) return SEGPAGED_ENOSPACE;
+  const int64_t nunits = sp.unit_e - sp.unit_b;
+  if (nunits == 0) return SEGPAGED_OK;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t qstride = layer < 0 ? (int64_t)pl->B * pl->Hq * pl->D : 0;
+  const float c = scale * kLog2e;
+  auto* qq = (const uint16_t*)q;
+  auto* kpp = (const uint16_t*)k_pool;
+  auto* vpp = (const uint16_t*)v_pool;
+  auto* ws = (float*)workspace;
+  if (nitems > 0) {
+    const dim3 grid((unsigned)((nitems + 3) / 4)), block(256);
+    if (pl->D == 128)
+      hipLaunchKernelGGL(decode_partial_kernel<128>, grid, block, 0, st, d_table,
+                         (int32_t)pl->off_units, (int32_t)pl->off_pages, (int32_t)pl->off_dec,
+                         (int32_t)sp.dec_b, (int32_t)sp.dec_e, qq, qstride, kpp, vpp, ws, pl->G,
+                         pl->Hq, pl->P, pl->log2P, c);
+    else
+      hipLaunchKernelGGL(decode_partial_kernel<64>, grid, block, 0, st, d_table,
+                         (int32_t)pl->off_units, (int32_t)pl->off_pages, (int32_t)pl->off_dec,
+                         (int32_t)sp.dec_b, (int32_t)sp.dec_e, qq, qstride, kpp, vpp, ws, pl->G,
+                         pl->Hq, pl->P, pl->log2P, c);
+    int rc = check_launch();
+    if (rc) return rc;
+  }
+  const int64_t waves = nunits * pl->G;
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  auto* oo = (uint16_t*)o;
+  if (pl->D == 128)
+    hipLaunchKernelGGL(decode_combine_kernel<128>, grid, block, 0, st, d_table,
+                       (int32_t)pl->off_units, (int32_t)pl->off_decunits, (int32_t)sp.unit_b,
+                       (int32_t)sp.unit_e, (int32_t)sp.dec_b, ws, pl->G, pl->Hq, pl->B, oo, lse,
+                       (int32_t)(layer < 0));
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<64>, grid, block, 0, st, d_table,
+                       (int32_t)pl->off_units, (int32_t)pl->off_decunits, (int32_t)sp.unit_b,
+                       (int32_t)sp.unit_e, (int32_t)sp.dec_b, ws, pl->G, pl->Hq, pl->B, oo, lse,
+                       (int32_t)(layer < 0));
+  return check_launch();
+}
+
+}  // extern "C"

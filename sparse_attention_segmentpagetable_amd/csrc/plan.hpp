@@ -1,0 +1,54 @@
+// Internal plan representation shared by the host planner and the kernel launchers.
+// Not part of the public ABI (include/segpaged.h is).
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "segpaged.h"
+
+namespace segpaged {
+
+// SegmentPageTable format, version 1 (documented in segpaged.h).
+constexpr int32_t kMagic = 0x53475054;
+constexpr int32_t kVersion = 1;
+constexpr int kHeaderInts = 16;
+constexpr int kSeqInts = 4;
+constexpr int kUnitInts = 16;
+
+enum SeqField { S_N = 0, S_Q0 = 1, S_KVOFF = 2, S_QOFF = 3 };
+enum UnitField {
+  U_KIND = 0, U_B, U_L, U_H, U_N, U_Q0, U_SINK, U_WIN, U_KVLEN, U_NSEG,
+  U_S0POS, U_S0LEN, U_S1POS, U_S1LEN, U_PAGEOFF, U_RETROFF
+};
+
+// Work lists that follow the table in the device image.
+constexpr int kDecItemInts = 4;   // unit, slot_lo, slot_hi, 0
+constexpr int kPreItemInts = 2;   // unit, first query position of the tile
+constexpr int kPrefillRows = 128; // query rows per prefill tile: G heads x (128 / G) positions
+constexpr int kBlockN = 64;       // keys per prefill block
+constexpr int kMaxGroup = 16;     // Q heads per KV head the decode kernel supports
+
+struct LayerRange {
+  int64_t unit_b, unit_e;   // units
+  int64_t page_b, page_e;   // page-id slots of the table
+  int64_t retr_b, retr_e;   // retrieval positions
+  int64_t dec_b, dec_e;     // decode items
+  int64_t pre_b, pre_e;     // prefill items
+};
+
+}  // namespace segpaged
+
+struct segpaged_plan {
+  int32_t B = 0, L = 0, Hq = 0, Hkv = 0, D = 0, P = 0, G = 0, log2P = 0;
+  int32_t split = 0;            // decode keys per item
+  int64_t num_units = 0, num_pages = 0, pool_pages = 0, num_retr = 0;
+  int64_t q_rows = 0, kv_rows = 0;
+  int64_t off_seqs = 0, off_units = 0, off_pages = 0, off_retr = 0, table_len = 0;
+  int64_t off_decunits = 0, off_dec = 0, off_pre = 0, total_ints = 0;
+  int64_t n_dec = 0, n_pre = 0;
+  std::vector<int32_t> buf;                  // device image: table ++ work lists
+  std::vector<segpaged::LayerRange> layers;  // per-layer slices of buf
+  std::vector<segpaged_stats> stats;         // per-layer work counts
+  segpaged_stats total{};
+};

@@ -1,0 +1,453 @@
+// Host planner: spec validation, SegmentPageTable construction, page allocation
+// and the per-head varlen work lists. Host code only -- no HIP call, so it runs
+// (and is tested) without a GPU.
+//
+// Retention and table rules: SegPagedAttention runtime explainer, section 3
+// (per-(layer, head, segment) pages; local heads keep sink + recent pages,
+// global heads the whole context; local heads are cut to visible tokens) and
+// section 5 (the layout is built once, when KV is written, and reused).
+#include <algorithm>
+#include <cstring>
+#include <limits>
+#include <new>
+#include <numeric>
+#include <vector>
+
+#include "plan.hpp"
+
+using namespace segpaged;
+
+namespace {
+
+struct Seg {
+  int64_t pos0;  // first logical position, -1 for a gathered (retrieval) segment
+  int64_t len;
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Keys visible to at least one query row in [q0, n): see segpaged_plan_create.
+int retained(int kind, int64_t sink, int64_t window, int64_t n, int64_t q0, int64_t retr_len,
+             Seg out[2]) {
+  if (kind == SEGPAGED_GLOBAL || kind == SEGPAGED_DENSE) {
+    if (n <= 0) return 0;
+    out[0] = {0, n};
+    return 1;
+  }
+  if (kind == SEGPAGED_RETRIEVAL) {
+    if (retr_len <= 0) return 0;
+    out[0] = {-1, retr_len};
+    return 1;
+  }
+  // LOCAL: sink [0, a) and window [w0, n), w0 = max(a, q0 - window + 1)
+  const int64_t a = std::min(sink, n);
+  const int64_t w0 = std::max(a, q0 - window + 1);
+  int cnt = 0;
+  if (a > 0) out[cnt++] = {0, a};
+  if (n > w0) {
+    if (cnt == 1 && w0 == a) {
+      out[0] = {0, n};
+    } else {
+      out[cnt++] = {w0, n - w0};
+    }
+  }
+  return cnt;
+}
+
+// Visible (row, key) pairs over rows q0..n-1 of one head.
+int64_t pairs_global(int64_t n, int64_t q0) { return (n * (n + 1) - q0 * (q0 + 1)) / 2; }
+
+int64_t pairs_local(int64_t n, int64_t q0, int64_t s, int64_t w) {
+  // row i sees min(i + 1, s + w) keys
+  const int64_t a = s + w;
+  int64_t tot = 0;
+  const int64_t lo_end = std::min(n, a);  // rows i < lo_end see i + 1 keys
+  if (lo_end > q0) tot += (lo_end * (lo_end + 1) - q0 * (q0 + 1)) / 2;
+  const int64_t hi_begin = std::max(q0, a);
+  if (n > hi_begin) tot += (n - hi_begin) * a;
+  return tot;
+}
+
+int64_t pairs_retrieval(int64_t n, int64_t q0, const int32_t* r, int64_t cnt) {
+  int64_t tot = 0;
+  for (int64_t k = 0; k < cnt; ++k) tot += n - std::max<int64_t>(r[k], q0);
+  return tot;
+}
+
+// Keys the decode row n - 1 sees: count and slot ranges (at most 3).
+struct SlotRange { int64_t lo, hi; };
+
+int decode_ranges(int kind, int64_t sink, int64_t window, int64_t n, const Seg* segs, int nseg,
+                  int64_t P, SlotRange out[4]) {
+  int cnt = 0;
+  int64_t slot_base = 0;
+  for (int s = 0; s < nseg; ++s) {
+    const Seg& sg = segs[s];
+    if (sg.pos0 < 0 || kind == SEGPAGED_GLOBAL || kind == SEGPAGED_DENSE) {
+      out[cnt++] = {slot_base, slot_base + sg.len};
+    } else {
+      // LOCAL: positions [pos0, pos0+len) intersected with [0, sink) U [n - window, n)
+      int64_t alo = std::max<int64_t>(sg.pos0, 0), ahi = std::min(sg.pos0 + sg.len, sink);
+      int64_t blo = std::max(sg.pos0, n - window), bhi = sg.pos0 + sg.len;
+      const bool a_ok = ahi > alo, b_ok = bhi > blo;
+      if (a_ok && b_ok && blo <= ahi) {
+        alo = std::min(alo, blo);
+        ahi = std::max(ahi, bhi);
+        out[cnt++] = {slot_base + alo - sg.pos0, slot_base + ahi - sg.pos0};
+      } else {
+        if (a_ok) out[cnt++] = {slot_base + alo - sg.pos0, slot_base + ahi - sg.pos0};
+        if (b_ok) out[cnt++] = {slot_base + blo - sg.pos0, slot_base + bhi - sg.pos0};
+      }
+    }
+    slot_base += ceil_div(sg.len, P) * P;
+  }
+  return cnt;
+}
+
+// KV blocks a prefill tile visits (cost model for heaviest-first ordering).
+int64_t tile_cost(int kind, int64_t sink, int64_t window, int64_t r0, int64_t r1,
+                  const Seg* segs, int nseg, const int32_t* retr) {
+  int64_t blocks = 0;
+  for (int s = 0; s < nseg; ++s) {
+    const Seg& sg = segs[s];
+    if (sg.pos0 < 0) {  // gathered
+      const int64_t c = std::upper_bound(retr, retr + sg.len, (int32_t)(r1 - 1)) - retr;
+      blocks += ceil_div(c, kBlockN);
+      continue;
+    }
+    const int64_t end = std::min(sg.pos0 + sg.len, r1);
+    if (kind == SEGPAGED_LOCAL) {
+      const int64_t a_hi = std::min(end, sink);
+      if (a_hi > sg.pos0) blocks += ceil_div(a_hi - sg.pos0, kBlockN);
+      const int64_t b_lo = std::max(sg.pos0, std::max(sink, r0 - window + 1));
+      if (end > b_lo) blocks += ceil_div(end - b_lo, kBlockN) + 1;
+    } else if (end > sg.pos0) {
+      blocks += ceil_div(end - sg.pos0, kBlockN);
+    }
+  }
+  return blocks;
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan** plan_out,
+                                      segpaged_sizes* sizes) {
+  if (plan_out) *plan_out = nullptr;
+  if (!spec || !plan_out) return SEGPAGED_EINVAL;
+  const segpaged_spec& s = *spec;
+  if (s.num_seqs < 1 || s.num_layers < 1 || s.num_kv_heads < 1 || s.num_q_heads < 1)
+    return SEGPAGED_EINVAL;
+  if (s.num_q_heads % s.num_kv_heads != 0) return SEGPAGED_EINVAL;
+  if (s.head_dim <= 0 || s.page_size <= 0) return SEGPAGED_EINVAL;
+  if (s.head_dim != 64 && s.head_dim != 128) return SEGPAGED_EUNSUPPORTED;
+  if (s.page_size != 16 && s.page_size != 32 && s.page_size != 64 && s.page_size != 128)
+    return SEGPAGED_EUNSUPPORTED;
+  const int32_t G = s.num_q_heads / s.num_kv_heads;
+  if (G > kMaxGroup) return SEGPAGED_EUNSUPPORTED;
+  if (!s.seq_len || !s.first_query_pos || !s.kind || !s.sink || !s.window) return SEGPAGED_EINVAL;
+  if (s.decode_split_tokens < 0 || s.decode_split_tokens % 64 != 0) return SEGPAGED_EINVAL;
+  if (s.capacity_pages < 0 || s.free_list_len < 0) return SEGPAGED_EINVAL;
+
+  const int64_t B = s.num_seqs, L = s.num_layers, Hkv = s.num_kv_heads, P = s.page_size;
+  const int64_t U = L * B * Hkv;
+  const int64_t kI32Max = std::numeric_limits<int32_t>::max();
+  if (U > kI32Max / kUnitInts) return SEGPAGED_EINVAL;
+
+  int64_t kv_rows = 0, q_rows = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t n = s.seq_len[b], q0 = s.first_query_pos[b];
+    if (n < 0 || q0 < 0 || q0 > std::max<int64_t>(n - 1, 0)) return SEGPAGED_EINVAL;
+    kv_rows += n;
+    q_rows += n - q0;
+  }
+  if (kv_rows > kI32Max || q_rows > kI32Max) return SEGPAGED_EINVAL;
+
+  bool any_retr = false;
+  for (int64_t i = 0; i < L * Hkv; ++i) {
+    const int k = s.kind[i];
+    if (k < SEGPAGED_GLOBAL || k > SEGPAGED_DENSE) return SEGPAGED_EINVAL;
+    if (k == SEGPAGED_LOCAL && (s.sink[i] < 0 || s.window[i] < 1)) return SEGPAGED_EINVAL;
+    if (k == SEGPAGED_RETRIEVAL) any_retr = true;
+  }
+  if (any_retr && (!s.retr_offsets || !s.retr_pos)) return SEGPAGED_EINVAL;
+  if (s.retr_offsets) {
+    if (s.retr_offsets[0] != 0) return SEGPAGED_EINVAL;
+    for (int64_t l = 0; l < L; ++l)
+      for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < Hkv; ++h) {
+          const int64_t u = (l * B + b) * Hkv + h;
+          const int64_t o0 = s.retr_offsets[u], o1 = s.retr_offsets[u + 1];
+          if (o1 < o0) return SEGPAGED_EINVAL;
+          if (s.kind[l * Hkv + h] != SEGPAGED_RETRIEVAL) {
+            if (o1 != o0) return SEGPAGED_EINVAL;
+            continue;
+          }
+          if (o1 - o0 > kI32Max) return SEGPAGED_EINVAL;
+          for (int64_t k = o0; k < o1; ++k) {
+            const int32_t p = s.retr_pos[k];
+            if (p < 0 || p >= s.seq_len[b]) return SEGPAGED_EINVAL;
+            if (k > o0 && p <= s.retr_pos[k - 1]) return SEGPAGED_EINVAL;
+          }
+        }
+  }
+
+  segpaged_plan* pl = new (std::nothrow) segpaged_plan();
+  if (!pl) return SEGPAGED_ENOSPACE;
+  pl->B = (int32_t)B; pl->L = (int32_t)L; pl->Hq = s.num_q_heads; pl->Hkv = (int32_t)Hkv;
+  pl->D = s.head_dim; pl->P = (int32_t)P; pl->G = G;
+  pl->log2P = 0;
+  while ((1 << pl->log2P) < P) ++pl->log2P;
+  pl->num_units = U; pl->q_rows = q_rows; pl->kv_rows = kv_rows;
+
+  // ---- pass 1: segments per unit, page counts, retrieval totals
+  std::vector<Seg> segs(U * 2);
+  std::vector<int> nseg(U);
+  int64_t num_pages = 0, num_retr = 0;
+  for (int64_t l = 0; l < L; ++l)
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t h = 0; h < Hkv; ++h) {
+        const int64_t u = (l * B + b) * Hkv + h, c = l * Hkv + h;
+        const int64_t rl = s.retr_offsets ? s.retr_offsets[u + 1] - s.retr_offsets[u] : 0;
+        nseg[u] = retained(s.kind[c], s.sink[c], s.window[c], s.seq_len[b],
+                           s.first_query_pos[b], rl, &segs[2 * u]);
+        for (int k = 0; k < nseg[u]; ++k) {
+          if (segs[2 * u + k].len > kI32Max / 2) { delete pl; return SEGPAGED_EINVAL; }
+          num_pages += ceil_div(segs[2 * u + k].len, P);
+        }
+        if (s.kind[c] == SEGPAGED_RETRIEVAL) num_retr += rl;
+      }
+  if (num_pages > kI32Max || num_retr > kI32Max) { delete pl; return SEGPAGED_EINVAL; }
+
+  int64_t capacity = s.capacity_pages ? s.capacity_pages : num_pages;
+  if (capacity < num_pages) { delete pl; return SEGPAGED_ENOSPACE; }
+  if (capacity > kI32Max) { delete pl; return SEGPAGED_EINVAL; }
+  if (s.free_list) {
+    if (s.free_list_len < num_pages) { delete pl; return SEGPAGED_ENOSPACE; }
+    std::vector<uint8_t> seen(capacity, 0);
+    for (int64_t i = 0; i < num_pages; ++i) {
+      const int32_t id = s.free_list[i];
+      if (id < 0 || id >= capacity || seen[id]) { delete pl; return SEGPAGED_EINVAL; }
+      seen[id] = 1;
+    }
+  }
+  pl->num_pages = num_pages;
+  pl->pool_pages = capacity;
+  pl->num_retr = num_retr;
+
+  // ---- table layout
+  pl->off_seqs = kHeaderInts;
+  pl->off_units = pl->off_seqs + kSeqInts * B;
+  pl->off_pages = pl->off_units + kUnitInts * U;
+  pl->off_retr = pl->off_pages + num_pages;
+  pl->table_len = pl->off_retr + num_retr;
+
+  // decode split: automatic = enough items to fill the GPU several times over
+  int64_t dec_tokens_all = 0;
+  for (int64_t u = 0; u < U; ++u) {
+    const int64_t l = u / (B * Hkv), b = (u / Hkv) % B, h = u % Hkv, c = l * Hkv + h;
+    SlotRange rr[4];
+    const int nr = decode_ranges(s.kind[c], s.sink[c], s.window[c], s.seq_len[b], &segs[2 * u],
+                                 nseg[u], P, rr);
+    for (int k = 0; k < nr; ++k) dec_tokens_all += rr[k].hi - rr[k].lo;
+  }
+  int64_t split = s.decode_split_tokens;
+  if (split == 0) {
+    split = 1024;
+    while (split > 64 && dec_tokens_all / split < 8192) split /= 2;
+  }
+  pl->split = (int32_t)split;
+
+  std::vector<int32_t>& t = pl->buf;
+  t.assign(pl->table_len + 2 * U, 0);
+  pl->off_decunits = pl->table_len;
+
+  // header and sequences
+  const int32_t hdr[kHeaderInts] = {kMagic, kVersion, (int32_t)B, (int32_t)L, s.num_q_heads,
+                                    (int32_t)Hkv, s.head_dim, (int32_t)P, (int32_t)U,
+                                    (int32_t)num_pages, (int32_t)num_retr, (int32_t)pl->off_seqs,
+                                    (int32_t)pl->off_units, (int32_t)pl->off_pages,
+                                    (int32_t)pl->off_retr, (int32_t)pl->table_len};
+  std::memcpy(t.data(), hdr, sizeof(hdr));
+  {
+    int64_t kvo = 0, qo = 0;
+    for (int64_t b = 0; b < B; ++b) {
+      int32_t* r = &t[pl->off_seqs + kSeqInts * b];
+      r[S_N] = s.seq_len[b]; r[S_Q0] = s.first_query_pos[b];
+      r[S_KVOFF] = (int32_t)kvo; r[S_QOFF] = (int32_t)qo;
+      kvo += s.seq_len[b];
+      qo += s.seq_len[b] - s.first_query_pos[b];
+    }
+  }
+
+  // ---- pass 2: unit records, page ids, retrieval positions, work lists, stats
+  std::vector<int32_t> dec_items, pre_items;
+  pl->layers.resize(L);
+  pl->stats.assign(L, segpaged_stats{});
+  int64_t page_cursor = 0, retr_cursor = 0;
+  const int64_t BQ = kPrefillRows / G;
+  for (int64_t l = 0; l < L; ++l) {
+    LayerRange& lr = pl->layers[l];
+    segpaged_stats& st = pl->stats[l];
+    lr.unit_b = l * B * Hkv; lr.unit_e = (l + 1) * B * Hkv;
+    lr.page_b = page_cursor; lr.retr_b = retr_cursor;
+    lr.dec_b = (int64_t)dec_items.size() / kDecItemInts;
+    lr.pre_b = (int64_t)pre_items.size() / kPreItemInts;
+    struct PreTile { int64_t cost, unit, r0; };
+    std::vector<PreTile> tiles;
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t h = 0; h < Hkv; ++h) {
+        const int64_t u = (l * B + b) * Hkv + h, c = l * Hkv + h;
+        const int kind = s.kind[c];
+        const int eff = kind == SEGPAGED_DENSE ? SEGPAGED_GLOBAL : kind;
+        const int64_t n = s.seq_len[b], q0 = s.first_query_pos[b];
+        int32_t* r = &t[pl->off_units + kUnitInts * u];
+        r[U_KIND] = eff; r[U_B] = (int32_t)b; r[U_L] = (int32_t)l; r[U_H] = (int32_t)h;
+        r[U_N] = (int32_t)n; r[U_Q0] = (int32_t)q0; r[U_SINK] = s.sink[c]; r[U_WIN] = s.window[c];
+        r[U_NSEG] = nseg[u];
+        r[U_PAGEOFF] = (int32_t)page_cursor;
+        r[U_RETROFF] = -1;
+        const int32_t* rpos = nullptr;
+        int64_t rl = 0;
+        if (kind == SEGPAGED_RETRIEVAL) {
+          r[U_RETROFF] = (int32_t)retr_cursor;
+          rl = s.retr_offsets[u + 1] - s.retr_offsets[u];
+          rpos = s.retr_pos + s.retr_offsets[u];
+          std::copy(rpos, rpos + rl, t.begin() + pl->off_retr + retr_cursor);
+          retr_cursor += rl;
+        }
+        int64_t kv_len = 0;
+        for (int k = 0; k < nseg[u]; ++k) {
+          const Seg& sg = segs[2 * u + k];
+          r[U_S0POS + 2 * k] = (int32_t)sg.pos0;
+          r[U_S0LEN + 2 * k] = (int32_t)sg.len;
+          kv_len += sg.len;
+          const int64_t np = ceil_div(sg.len, P);
+          for (int64_t p = 0; p < np; ++p, ++page_cursor)
+            t[pl->off_pages + page_cursor] = s.free_list ? s.free_list[page_cursor]
+                                                          : (int32_t)page_cursor;
+        }
+        r[U_KVLEN] = (int32_t)kv_len;
+
+        // stats
+        st.units += 1;
+        st.retained_tokens += kv_len;
+        st.q_rows += n - q0;
+        if (eff == SEGPAGED_GLOBAL) {
+          st.prefill_pairs += pairs_global(n, q0);
+        } else if (eff == SEGPAGED_LOCAL) {
+          st.prefill_pairs += pairs_local(n, q0, s.sink[c], s.window[c]);
+        } else {
+          st.prefill_pairs += pairs_retrieval(n, q0, rpos, rl);
+        }
+
+        // decode items: visible slot ranges of row n - 1, cut into <= split keys
+        int32_t* du = &t[pl->off_decunits + 2 * u];
+        du[0] = (int32_t)(dec_items.size() / kDecItemInts);
+        SlotRange rr[4];
+        const int nr = decode_ranges(kind, s.sink[c], s.window[c], n, &segs[2 * u], nseg[u], P, rr);
+        for (int k = 0; k < nr; ++k) {
+          st.decode_tokens += rr[k].hi - rr[k].lo;
+          for (int64_t lo = rr[k].lo; lo < rr[k].hi; lo += split) {
+            dec_items.push_back((int32_t)u);
+            dec_items.push_back((int32_t)lo);
+            dec_items.push_back((int32_t)std::min(lo + split, rr[k].hi));
+            dec_items.push_back(0);
+          }
+        }
+        du[1] = (int32_t)(dec_items.size() / kDecItemInts);
+
+        // prefill tiles
+        for (int64_t r0 = q0; r0 < n; r0 += BQ) {
+          const int64_t r1 = std::min(n, r0 + BQ);
+          tiles.push_back({tile_cost(eff, s.sink[c], s.window[c], r0, r1, &segs[2 * u], nseg[u],
+                                     rpos),
+                           u, r0});
+        }
+      }
+    std::stable_sort(tiles.begin(), tiles.end(),
+                     [](const PreTile& a, const PreTile& b) { return a.cost > b.cost; });
+    for (const PreTile& tl : tiles) {
+      pre_items.push_back((int32_t)tl.unit);
+      pre_items.push_back((int32_t)tl.r0);
+    }
+    lr.page_e = page_cursor; lr.retr_e = retr_cursor;
+    lr.dec_e = (int64_t)dec_items.size() / kDecItemInts;
+    lr.pre_e = (int64_t)pre_items.size() / kPreItemInts;
+    st.pages = lr.page_e - lr.page_b;
+    st.decode_items = lr.dec_e - lr.dec_b;
+    st.prefill_items = lr.pre_e - lr.pre_b;
+  }
+  pl->n_dec = (int64_t)dec_items.size() / kDecItemInts;
+  pl->n_pre = (int64_t)pre_items.size() / kPreItemInts;
+  pl->off_dec = pl->off_decunits + 2 * U;
+  pl->off_pre = pl->off_dec + (int64_t)dec_items.size();
+  pl->total_ints = pl->off_pre + (int64_t)pre_items.size();
+  if (pl->total_ints > kI32Max) { delete pl; return SEGPAGED_EINVAL; }
+  t.insert(t.end(), dec_items.begin(), dec_items.end());
+  t.insert(t.end(), pre_items.begin(), pre_items.end());
+
+  segpaged_stats& tot = pl->total;
+  tot = segpaged_stats{};
+  for (const segpaged_stats& st : pl->stats) {
+    tot.units += st.units; tot.pages += st.pages; tot.retained_tokens += st.retained_tokens;
+    tot.decode_tokens += st.decode_tokens; tot.prefill_pairs += st.prefill_pairs;
+    tot.q_rows += st.q_rows; tot.decode_items += st.decode_items;
+    tot.prefill_items += st.prefill_items;
+  }
+  *plan_out = pl;
+  if (sizes) segpaged_plan_sizes(pl, sizes);
+  return SEGPAGED_OK;
+}
+
+SEGPAGED_API void segpaged_plan_destroy(segpaged_plan* plan) { delete plan; }
+
+SEGPAGED_API int segpaged_plan_sizes(const segpaged_plan* pl, segpaged_sizes* z) {
+  if (!pl || !z) return SEGPAGED_EINVAL;
+  z->num_pages = pl->num_pages;
+  z->pool_pages = pl->pool_pages;
+  z->pool_bytes = pl->pool_pages * (int64_t)pl->P * pl->D * 2;
+  z->table_int32s = pl->total_ints;
+  z->table_len = pl->table_len;
+  z->num_units = pl->num_units;
+  z->q_rows = pl->q_rows;
+  z->kv_rows = pl->kv_rows;
+  z->decode_items = pl->n_dec;
+  z->prefill_items = pl->n_pre;
+  z->decode_workspace_bytes = pl->n_dec * (int64_t)pl->G * (pl->D + 4) * 4;
+  z->prefill_workspace_bytes = 0;
+  return SEGPAGED_OK;
+}
+
+SEGPAGED_API int segpaged_plan_table_host(const segpaged_plan* pl, int32_t* out, int64_t n) {
+  if (!pl || !out) return SEGPAGED_EINVAL;
+  if (n < pl->total_ints) return SEGPAGED_ENOSPACE;
+  std::memcpy(out, pl->buf.data(), sizeof(int32_t) * pl->total_ints);
+  return SEGPAGED_OK;
+}
+
+SEGPAGED_API int segpaged_plan_stats(const segpaged_plan* pl, int32_t layer, segpaged_stats* st) {
+  if (!pl || !st) return SEGPAGED_EINVAL;
+  if (layer < -1 || layer >= pl->L) return SEGPAGED_ESTATE;
+  *st = layer < 0 ? pl->total : pl->stats[layer];
+  return SEGPAGED_OK;
+}
+
+SEGPAGED_API const char* segpaged_status_str(int status) {
+  switch (status) {
+    case SEGPAGED_OK: return "ok";
+    case SEGPAGED_EINVAL: return "invalid argument";
+    case SEGPAGED_EUNSUPPORTED: return "unsupported shape";
+    case SEGPAGED_ENOSPACE: return "insufficient space";
+    case SEGPAGED_EHIP: return "HIP runtime error";
+    case SEGPAGED_ESTATE: return "call does not fit the plan";
+    default: return "unknown status";
+  }
+}
+
+SEGPAGED_API int segpaged_version(void) { return 100; }
+
+}  // extern "C"

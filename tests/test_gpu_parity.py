@@ -1,0 +1,319 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle, element by
+element, on seeded inputs. Sizes span several tiles and ragged tails; the
+full-size workloads are covered on sampled rows in test_gpu_fullsize.py."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention as OA
+from oracle import layout as OL
+from tests.gpu_util import lse_parity, parity, to_bits, to_dev, to_f64
+
+sp = pytest.importorskip("sparse_attention_segmentpagetable_amd")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _mixed(q0=(0, 30), free=None, cap=0, n=(37, 45), hd=64, ps=16):
+    kind = [W.GLOBAL, W.LOCAL, W.RETRIEVAL, W.LOCAL, W.DENSE, W.RETRIEVAL]
+    retr = {(0, 1, 0): np.array([1, 2, 30, 31, 32], np.int32),
+            (1, 1, 0): np.array([], np.int32),
+            (0, 2, 1): np.array([3, 17], np.int32),
+            (1, 2, 1): np.array([0, 1, 2, 3, 4, 5, 6, 7, 8, 40, 41], np.int32)}
+    return W.Spec(name="mixed", num_layers=3, num_q_heads=4, num_kv_heads=2, head_dim=hd,
+                  page_size=ps, seq_len=list(n), first_query_pos=list(q0), kind=kind,
+                  sink=[2, 3, 0, 4, 0, 0], window=[1, 9, 1, 5, 1, 1], retrieval=retr,
+                  free_list=free, capacity_pages=cap, seed=11)
+
+
+def _long_mixed(form, hd=128, ps=64):
+    """Several tiles, ragged tails, two-segment local heads, page boundaries."""
+    kind = [W.GLOBAL, W.LOCAL, W.LOCAL, W.RETRIEVAL]
+    lens = [700, 333, 1029]
+    retr = W.seeded_retrieval_sets(lens, kind, 1, 4, 7, 0.1)
+    s = W.Spec(name="long-mixed", num_layers=1, num_q_heads=32, num_kv_heads=4, head_dim=hd,
+               page_size=ps, seq_len=lens, first_query_pos=[0, 0, 0], kind=kind,
+               sink=[4, 4, 0, 0], window=[1, 130, 64, 1], retrieval=retr, seed=12)
+    if form == "decode":
+        return W.decode_form(s)
+    if form == "mid":
+        return replace(s, first_query_pos=[350, 0, 900])
+    return s
+
+
+def _run_layer(spec, layer, form, split=0, plan=None, bufs=None):
+    plan = plan or sp.Plan(spec, decode_split_tokens=split)
+    bufs = bufs or plan.allocate(DEV)
+    kb, vb = W.kv_bits(spec, layer)
+    qb = W.q_bits(spec, layer)
+    sp.build(plan, layer, to_dev(kb), to_dev(vb), bufs["table"], bufs["k_pool"], bufs["v_pool"])
+    q = to_dev(qb)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device=DEV)
+    scale = 1.0 / np.sqrt(spec.head_dim)
+    if form == "prefill":
+        sp.prefill(plan, layer, q, bufs["table"], bufs["k_pool"], bufs["v_pool"], scale, o, lse)
+    else:
+        sp.decode(plan, layer, q, bufs["table"], bufs["k_pool"], bufs["v_pool"], scale, o, lse,
+                  workspace=bufs["workspace"])
+    torch.cuda.synchronize()
+    return plan, bufs, (qb, kb, vb), to_f64(o), lse.cpu().numpy()
+
+
+POOL_SPECS = [
+    ("tiny-prefill", lambda: W.tiny("prefill")),
+    ("tiny-decode", lambda: W.tiny("decode")),
+    ("mixed-free", lambda: _mixed(free=W.seeded_free_list(300, 4), cap=300)),
+    ("mixed-q0", lambda: _mixed(q0=(10, 44), hd=128, ps=32)),
+    ("long-mixed-p128", lambda: _long_mixed("decode", ps=128)),
+    ("mistral-small-decode", lambda: W.mistral_layer("decode", seqs=2, n=900, window=200)),
+]
+
+
+@pytest.mark.parametrize("name,mk", POOL_SPECS, ids=[p[0] for p in POOL_SPECS])
+def test_build_table_and_pool_bit_exact(name, mk):
+    spec = mk()
+    plan = sp.Plan(spec)
+    bufs = plan.allocate(DEV)
+    P, D = spec.page_size, spec.head_dim
+    for layer in range(spec.num_layers):
+        kb, vb = W.kv_bits(spec, layer)
+        sp.build(plan, layer, to_dev(kb), to_dev(vb), bufs["table"], bufs["k_pool"], bufs["v_pool"])
+        torch.cuda.synchronize()
+        kp_ref, vp_ref, written = OL.pool(spec, layer, kb, vb, plan.sizes.pool_pages)
+        kp = to_bits(bufs["k_pool"]).reshape(-1, D // 8, P, 8)
+        vp = to_bits(bufs["v_pool"]).reshape(-1, P // 8, D, 8)
+        assert np.array_equal(kp[written], kp_ref[written]), (name, layer)
+        assert np.array_equal(vp[written], vp_ref[written]), (name, layer)
+    dev_table = bufs["table"].cpu().numpy()
+    assert np.array_equal(dev_table, plan.table_host())
+    assert np.array_equal(dev_table[:plan.sizes.table_len], OL.table(spec))
+
+
+def test_build_all_layers_in_one_call():
+    spec = _mixed(free=W.seeded_free_list(200, 9), cap=200)
+    plan = sp.Plan(spec)
+    bufs = plan.allocate(DEV)
+    ks, vs = zip(*[W.kv_bits(spec, l) for l in range(spec.num_layers)])
+    sp.build(plan, -1, to_dev(np.stack(ks)), to_dev(np.stack(vs)), bufs["table"], bufs["k_pool"],
+             bufs["v_pool"])
+    torch.cuda.synchronize()
+    P, D = spec.page_size, spec.head_dim
+    kp = to_bits(bufs["k_pool"]).reshape(-1, D // 8, P, 8)
+    for l in range(spec.num_layers):
+        kp_ref, _, written = OL.pool(spec, l, ks[l], vs[l], plan.sizes.pool_pages)
+        assert np.array_equal(kp[written], kp_ref[written])
+
+
+PREFILL_SPECS = [
+    ("tiny-512", lambda: W.tiny("prefill")),
+    ("tiny-n1", lambda: W.tiny("prefill", n=1)),
+    ("tiny-n70", lambda: W.tiny("prefill", n=70)),
+    ("mixed", lambda: _mixed()),
+    ("mixed-d128-p32", lambda: _mixed(q0=(5, 40), hd=128, ps=32)),
+    ("long-mixed", lambda: _long_mixed("prefill")),
+    ("long-mixed-mid", lambda: _long_mixed("mid")),
+    ("long-mixed-p16", lambda: _long_mixed("prefill", ps=16)),
+    ("mistral-small", lambda: W.mistral_layer("prefill", seqs=2, n=777, window=128)),
+    ("llama-g8-small", lambda: replace(W.long_prefill(num_layers=2, n=1500, window=256),
+                                       seq_len=[1500, 260], first_query_pos=[0, 0])),
+]
+
+
+@pytest.mark.parametrize("name,mk", PREFILL_SPECS, ids=[p[0] for p in PREFILL_SPECS])
+def test_prefill_parity(name, mk):
+    spec = mk()
+    plan = bufs = None
+    for layer in range(spec.num_layers):
+        plan, bufs, (qb, kb, vb), o, lse = _run_layer(spec, layer, "prefill", plan=plan, bufs=bufs)
+        ref, ref_lse = OA.attention(spec, layer, qb, kb, vb)
+        parity(o, ref, f"{name} prefill L{layer}")
+        lse_parity(lse, ref_lse, f"{name} prefill L{layer}")
+
+
+DECODE_SPECS = [
+    ("tiny-513", lambda: W.tiny("decode")),
+    ("mixed", lambda: _mixed(q0=(36, 44))),
+    ("mixed-free", lambda: replace(_mixed(q0=(36, 44), free=W.seeded_free_list(64, 2), cap=64))),
+    ("long-mixed", lambda: _long_mixed("decode")),
+    ("long-mixed-p16", lambda: _long_mixed("decode", ps=16)),
+    ("mistral-small", lambda: W.mistral_layer("decode", seqs=3, n=2000, window=300)),
+    ("llama70b-small", lambda: W.llama70b_decode(num_layers=3, seqs=2, n=3000, window=512)),
+    ("varlen-small", lambda: W.mixed_varlen_decode(seqs=5, num_layers=2, lo=100, hi=6000,
+                                                   window=256)),
+]
+
+
+@pytest.mark.parametrize("name,mk", DECODE_SPECS, ids=[p[0] for p in DECODE_SPECS])
+@pytest.mark.parametrize("split", [0, 64, 512])
+def test_decode_parity(name, mk, split):
+    spec = mk()
+    plan = bufs = None
+    for layer in range(spec.num_layers):
+        plan, bufs, (qb, kb, vb), o, lse = _run_layer(spec, layer, "decode", split=split,
+                                                      plan=plan, bufs=bufs)
+        ref, ref_lse = OA.attention(spec, layer, qb, kb, vb)
+        parity(o, ref, f"{name} decode L{layer} split {split}")
+        lse_parity(lse, ref_lse, f"{name} decode L{layer}")
+
+
+def test_decode_on_prefill_form_uses_all_layers_call():
+    """A prefill-form table read by the decode row (window predicate ranges not
+    page aligned), all layers in one call."""
+    spec = replace(W.llama70b_decode(num_layers=2, seqs=2, n=1500, window=300),
+                   first_query_pos=[0, 0])
+    dspec = W.decode_form(spec)
+    plan = sp.Plan(spec)
+    bufs = plan.allocate(DEV)
+    kvs = [W.kv_bits(spec, l) for l in range(2)]
+    sp.build(plan, -1, to_dev(np.stack([k for k, _ in kvs])), to_dev(np.stack([v for _, v in kvs])),
+             bufs["table"], bufs["k_pool"], bufs["v_pool"])
+    qs = [W.q_bits(dspec, l) for l in range(2)]
+    q = to_dev(np.stack(qs))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    sp.decode(plan, -1, q, bufs["table"], bufs["k_pool"], bufs["v_pool"], 1 / np.sqrt(128), o, lse,
+              workspace=bufs["workspace"])
+    torch.cuda.synchronize()
+    of = to_f64(o)
+    for l in range(2):
+        ref, ref_lse = OA.attention(dspec, l, qs[l], *kvs[l])
+        parity(of[l], ref, f"decode prefill-form L{l}")
+        lse_parity(lse[l].cpu().numpy(), ref_lse, f"decode prefill-form L{l}")
+
+
+def test_prefill_all_layers_in_one_call():
+    spec = _mixed(hd=128, ps=32)
+    plan = sp.Plan(spec)
+    bufs = plan.allocate(DEV)
+    kvs = [W.kv_bits(spec, l) for l in range(3)]
+    sp.build(plan, -1, to_dev(np.stack([k for k, _ in kvs])), to_dev(np.stack([v for _, v in kvs])),
+             bufs["table"], bufs["k_pool"], bufs["v_pool"])
+    qs = [W.q_bits(spec, l) for l in range(3)]
+    q = to_dev(np.stack(qs))
+    o = torch.empty_like(q)
+    sp.prefill(plan, -1, q, bufs["table"], bufs["k_pool"], bufs["v_pool"], 0.125, o)
+    torch.cuda.synchronize()
+    of = to_f64(o)
+    for l in range(3):
+        ref, _ = OA.attention(spec, l, qs[l], *kvs[l], scale=0.125)
+        parity(of[l], ref, f"prefill all-layers L{l}")
+
+
+def test_split_count_invariance():
+    spec = W.llama70b_decode(num_layers=1, seqs=2, n=5000, window=700)
+    outs = []
+    for split in (64, 256, 4096):
+        _, _, _, o, lse = _run_layer(spec, 0, "decode", split=split)
+        outs.append((o, lse))
+    for o, lse in outs[1:]:
+        assert np.max(np.abs(o - outs[0][0])) <= 2 ** -7  # fp32 merge order only
+        assert np.max(np.abs(lse - outs[0][1])) <= 1e-4
+
+
+def test_decode_row_matches_last_prefill_row():
+    pre = _long_mixed("prefill")
+    _, _, (qb, kb, vb), o_pre, lse_pre = _run_layer(pre, 0, "prefill")
+    dec = W.decode_form(pre)
+    plan = sp.Plan(dec)
+    bufs = plan.allocate(DEV)
+    sp.build(plan, 0, to_dev(kb), to_dev(vb), bufs["table"], bufs["k_pool"], bufs["v_pool"])
+    last = np.cumsum(pre.seq_len) - 1
+    q = to_dev(qb[last])
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=DEV)
+    sp.decode(plan, 0, q, bufs["table"], bufs["k_pool"], bufs["v_pool"], 1 / np.sqrt(128), o, lse,
+              workspace=bufs["workspace"])
+    torch.cuda.synchronize()
+    parity(to_f64(o), o_pre[last], "decode vs last prefill row")
+    assert np.max(np.abs(lse.cpu().numpy() - lse_pre[last])) <= 1e-3
+
+
+def _run_kv(spec, form, kb, vb, qb, scale=0.09):
+    plan = sp.Plan(spec)
+    bufs = plan.allocate(DEV)
+    sp.build(plan, 0, to_dev(kb), to_dev(vb), bufs["table"], bufs["k_pool"], bufs["v_pool"])
+    q = to_dev(qb)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=DEV)
+    if form == "prefill":
+        sp.prefill(plan, 0, q, bufs["table"], bufs["k_pool"], bufs["v_pool"], scale, o, lse)
+    else:
+        sp.decode(plan, 0, q, bufs["table"], bufs["k_pool"], bufs["v_pool"], scale, o, lse,
+                  workspace=bufs["workspace"])
+    torch.cuda.synchronize()
+    return to_bits(o), lse.cpu().numpy()
+
+
+def test_invisible_keys_do_not_change_output_bitwise():
+    """Perturbing K/V at keys no query row sees leaves O and LSE bit-identical:
+    those keys are never stored (decode form) or never read unmasked (prefill)."""
+    base = W.Spec(name="perturb", num_layers=1, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                  page_size=64, seq_len=[3000], first_query_pos=[0], kind=[W.LOCAL, W.LOCAL],
+                  sink=[4, 0], window=[257, 64], seed=21)
+    for form in ("prefill", "decode"):
+        s = base if form == "prefill" else W.decode_form(base)
+        kb, vb = W.kv_bits(s, 0)
+        qb = W.q_bits(s, 0)
+        n = s.seq_len[0]
+        rows = np.arange(s.first_query_pos[0], n)
+        kb2, vb2 = kb.copy(), vb.copy()
+        changed = 0
+        for h in range(2):
+            kind, sk, w = s.head_class(0, h)
+            inv = ~OA.visibility_mask(kind, sk, w, None, rows, n).any(axis=0)
+            kb2[inv, h] ^= 0x1234
+            vb2[inv, h] ^= 0x0F0F
+            changed += int(inv.sum())
+        if form == "decode":
+            assert changed > 5000
+        o1, l1 = _run_kv(s, form, kb, vb, qb)
+        o2, l2 = _run_kv(s, form, kb2, vb2, qb)
+        assert np.array_equal(o1, o2), form
+        assert np.array_equal(l1, l2), form
+    # prefill: keys outside every row's window exist only relative to a row
+    # range; perturb keys invisible to rows >= 2000 and run the table planned
+    # for those rows (q0 = 2000)
+    s = replace(base, first_query_pos=[2000])
+    kb, vb = W.kv_bits(s, 0)
+    qb = W.q_bits(s, 0)
+    rows = np.arange(2000, 3000)
+    kb2, vb2 = kb.copy(), vb.copy()
+    for h in range(2):
+        kind, sk, w = s.head_class(0, h)
+        inv = ~OA.visibility_mask(kind, sk, w, None, rows, 3000).any(axis=0)
+        assert inv.sum() > 1000
+        kb2[inv, h] ^= 0x1234
+        vb2[inv, h] ^= 0x0F0F
+    o1, l1 = _run_kv(s, "prefill", kb, vb, qb)
+    o2, l2 = _run_kv(s, "prefill", kb2, vb2, qb)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_empty_and_degenerate_rows():
+    """Empty sequence, empty retrieval set, rows before the first retrieved key."""
+    kind = [W.RETRIEVAL, W.GLOBAL]
+    spec = W.Spec(name="degen", num_layers=1, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                  page_size=16, seq_len=[40, 0, 25], first_query_pos=[0, 0, 0], kind=kind,
+                  sink=[0, 0], window=[1, 1],
+                  retrieval={(0, 0, 0): np.array([7, 8, 30], np.int32),
+                             (1, 0, 0): np.array([], np.int32),
+                             (2, 0, 0): np.array([], np.int32)}, seed=5)
+    _, _, (qb, kb, vb), o, lse = _run_layer(spec, 0, "prefill")
+    ref, ref_lse = OA.attention(spec, 0, qb, kb, vb)
+    parity(o, ref, "degenerate prefill")
+    lse_parity(lse, ref_lse, "degenerate prefill")
+    assert np.all(o[:7, :2] == 0) and np.all(np.isneginf(lse[:7, :2]))
+    # decode: Q/O have one row per sequence; the empty sequence's row is O = 0, LSE = -inf
+    dspec = W.decode_form(spec)
+    qb = W.q_bits(replace(dspec, seq_len=[40, 1, 25], first_query_pos=[39, 0, 24]), 0)
+    ob, lse = _run_kv(dspec, "decode", kb, vb, qb, scale=0.125)
+    o = OA.bf16_bits_to_f64(ob)
+    ref, ref_lse = OA.attention(dspec, 0, qb[[0, 2]], kb, vb, scale=0.125)
+    parity(o[[0, 2]], ref, "degenerate decode")
+    lse_parity(lse[[0, 2]], ref_lse, "degenerate decode")
+    assert np.all(o[1] == 0) and np.all(np.isneginf(lse[1]))

@@ -1,0 +1,213 @@
+"""Host planner (C++) against the oracle, on the CPU: the SegmentPageTable must
+match bit for bit; work counts must match brute-force counts; work lists must
+cover exactly what each row sees; invalid specs must fail before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as OA
+from oracle import layout as OL
+
+sp = pytest.importorskip("sparse_attention_segmentpagetable_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _mixed(q0=(0, 30), free=None, cap=0):
+    kind = [W.GLOBAL, W.LOCAL, W.RETRIEVAL, W.LOCAL, W.DENSE, W.RETRIEVAL]
+    retr = {(0, 1, 0): np.array([1, 2, 30, 31, 32], np.int32),
+            (1, 1, 0): np.array([], np.int32),
+            (0, 2, 1): np.array([3, 17], np.int32),
+            (1, 2, 1): np.array([0, 1, 2, 3, 4, 5, 6, 7, 8, 40, 41], np.int32)}
+    return W.Spec(name="mixed", num_layers=3, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                  page_size=16, seq_len=[37, 45], first_query_pos=list(q0), kind=kind,
+                  sink=[2, 3, 0, 4, 0, 0], window=[1, 9, 1, 5, 1, 1], retrieval=retr,
+                  free_list=free, capacity_pages=cap)
+
+
+def _specs():
+    yield W.tiny("prefill")
+    yield W.tiny("decode")
+    yield W.tiny("prefill", n=1)
+    yield W.mistral_layer("decode", seqs=2, n=1000, window=100)
+    yield W.mistral_layer("prefill", seqs=3, n=700, window=64)
+    yield _mixed()
+    yield _mixed(q0=(36, 44))
+    yield _mixed(q0=(10, 0), free=W.seeded_free_list(300, 4), cap=300)
+    yield W.llama70b_decode(num_layers=3, seqs=2, n=3000, window=512)
+    yield W.mixed_varlen_decode(seqs=4, num_layers=2, lo=64, hi=5000, window=256)
+    s = W.tiny("prefill", n=50)
+    yield replace(s, seq_len=[50, 0, 7], first_query_pos=[0, 0, 6])  # empty + ragged sequences
+
+
+@pytest.mark.parametrize("spec", list(_specs()), ids=lambda s: f"{s.name}")
+def test_table_bit_exact_vs_oracle(spec):
+    plan = sp.Plan(spec)
+    got = plan.table_host()
+    ref = OL.table(spec)
+    assert plan.sizes.table_len == len(ref)
+    assert np.array_equal(got[:len(ref)], ref)
+    assert plan.sizes.num_pages == int(ref[9])
+    assert plan.sizes.q_rows == spec.total_q_rows and plan.sizes.kv_rows == spec.total_tokens
+
+
+@pytest.mark.parametrize("spec", list(_specs()), ids=lambda s: f"{s.name}")
+def test_stats_vs_bruteforce(spec):
+    plan = sp.Plan(spec)
+    for layer in range(spec.num_layers):
+        st = plan.stats(layer)
+        pairs = dec = rows = 0
+        for b, n in enumerate(spec.seq_len):
+            q0 = spec.first_query_pos[b]
+            for h in range(spec.num_kv_heads):
+                kind, s, w = spec.head_class(layer, h)
+                r = spec.retrieval.get((b, layer, h))
+                pairs += OA.visible_pairs(kind, s, w, r, n, q0)
+                if n > 0:
+                    dec += int(OA.visibility_mask(kind, s, w, r, np.array([n - 1]), n).sum())
+                rows += n - q0
+        assert st["prefill_pairs"] == pairs
+        assert st["decode_tokens"] == dec
+        assert st["q_rows"] == rows
+        assert st["retained_tokens"] == OL.kv_len_total(spec, layers={layer})
+    tot = plan.stats(-1)
+    assert tot["retained_tokens"] == OL.kv_len_total(spec)
+
+
+def _decode_items(plan):
+    t = plan.table_host()
+    z = plan.sizes
+    U = z.num_units
+    du = t[z.table_len:z.table_len + 2 * U].reshape(U, 2)
+    items = t[z.table_len + 2 * U:z.table_len + 2 * U + 4 * z.decode_items].reshape(-1, 4)
+    pre = t[z.table_len + 2 * U + 4 * z.decode_items:].reshape(-1, 2)
+    return t, du, items, pre
+
+
+@pytest.mark.parametrize("spec", list(_specs()), ids=lambda s: f"{s.name}")
+@pytest.mark.parametrize("split", [0, 64, 192])
+def test_decode_items_cover_visible_keys_once(spec, split):
+    plan = sp.Plan(spec, decode_split_tokens=split)
+    t, du, items, _ = _decode_items(plan)
+    P = spec.page_size
+    for (u, b, l, h) in OL.units(spec):
+        n = spec.seq_len[b]
+        kind, s, w = spec.head_class(l, h)
+        r = spec.retrieval.get((b, l, h))
+        seen = []
+        ib, ie = du[u]
+        slot_base = 0
+        pos_of_slot = {}
+        for seg in OL.unit_segments(spec, b, l, h):
+            for k, p in enumerate(OL.segment_positions(seg)):
+                pos_of_slot[slot_base + k] = int(p)
+            slot_base += OL.ceil_div(len(OL.segment_positions(seg)), P) * P
+        for it in range(ib, ie):
+            uu, lo, hi, _ = items[it]
+            assert uu == u and hi > lo
+            if split:
+                assert hi - lo <= split
+            seen += [pos_of_slot[x] for x in range(lo, hi)]
+        want = [] if n == 0 else list(np.nonzero(
+            OA.visibility_mask(kind, s, w, r, np.array([n - 1]), n)[0])[0])
+        assert sorted(seen) == want and len(seen) == len(set(seen))
+
+
+@pytest.mark.parametrize("spec", list(_specs()), ids=lambda s: f"{s.name}")
+def test_prefill_items_tile_every_row_once(spec):
+    plan = sp.Plan(spec)
+    _, _, _, pre = _decode_items(plan)
+    G = spec.group
+    bq = 128 // G
+    got = {}
+    for u, r0 in pre:
+        got.setdefault(int(u), []).append(int(r0))
+    for (u, b, l, h) in OL.units(spec):
+        n, q0 = spec.seq_len[b], spec.first_query_pos[b]
+        assert sorted(got.get(u, [])) == list(range(q0, n, bq))
+    assert len(pre) == plan.sizes.prefill_items
+
+
+def test_split_and_workspace_sizes():
+    spec = W.tiny("decode")
+    plan = sp.Plan(spec, decode_split_tokens=64)
+    z = plan.sizes
+    assert z.decode_workspace_bytes == z.decode_items * spec.group * (spec.head_dim + 4) * 4
+    # global unit: 513 keys -> 9 items of <= 64; local: sink 4 (1 item) + window 64 (1 item)
+    assert z.decode_items == 9 + 3 * 2
+
+
+def _rc(spec_kwargs, **plan_kwargs):
+    s = replace(W.tiny("prefill", n=40), **spec_kwargs)
+    try:
+        sp.Plan(s, **plan_kwargs)
+        return 0
+    except sp.SegPagedError as e:
+        return e.status
+
+
+def test_validation_errors():
+    assert _rc({}) == 0
+    assert _rc({"head_dim": 96}) == -2
+    assert _rc({"page_size": 48}) == -2
+    assert _rc({"page_size": 0}) == -1
+    assert _rc({"num_q_heads": 6}) == -1          # not a multiple of Hkv
+    assert _rc({"num_q_heads": 4 * 32}) == -2     # group of 32 unsupported
+    assert _rc({"window": [64, 0, 64, 64]}) == -1  # LOCAL window < 1
+    assert _rc({"sink": [4, -1, 4, 4]}) == -1
+    assert _rc({"kind": [0, 1, 9, 1]}) == -1
+    assert _rc({"first_query_pos": [40]}) == -1   # q0 beyond N-1
+    assert _rc({"seq_len": [-1]}) == -1
+    assert _rc({"kind": [0, 2, 1, 1]}) == -1      # retrieval head without positions
+    assert _rc({"kind": [0, 2, 1, 1], "retrieval": {(0, 0, 1): np.array([3, 3], np.int32)}}) == -1
+    assert _rc({"kind": [0, 2, 1, 1], "retrieval": {(0, 0, 1): np.array([5, 40], np.int32)}}) == -1
+    assert _rc({"kind": [0, 2, 1, 1], "retrieval": {(0, 0, 1): np.array([5, 39], np.int32)}}) == 0
+    assert _rc({"retrieval": {(0, 0, 1): np.array([5], np.int32)}}) == -1  # set on a LOCAL head
+    assert _rc({"capacity_pages": 5}) == -3       # needs 3 + 3*3 = 12 pages
+    assert _rc({"free_list": np.arange(5, dtype=np.int32)}) == -3
+    assert _rc({"free_list": np.array([0] * 12, np.int32), "capacity_pages": 20}) == -1
+    assert _rc({"free_list": np.arange(12, dtype=np.int32) + 10, "capacity_pages": 20}) == -1
+    assert _rc({"free_list": np.arange(12, dtype=np.int32) + 8, "capacity_pages": 20}) == 0
+    assert _rc({}, decode_split_tokens=100) == -1
+
+
+def test_call_validation_without_gpu():
+    """Entry points reject bad arguments before touching the GPU."""
+    lib = sp.library()
+    plan = sp.Plan(W.tiny("prefill", n=40))
+    vp = ctypes.c_void_p
+    fake = vp(1 << 20)  # aligned, never dereferenced: validation fails first
+    assert lib.segpaged_build(plan.handle, 0, None, fake, fake, fake, fake, None) == -1
+    assert lib.segpaged_build(plan.handle, 1, fake, fake, fake, fake, fake, None) == -5
+    assert lib.segpaged_build(plan.handle, 0, vp((1 << 20) + 2), fake, fake, fake, fake, None) == -1
+    assert lib.segpaged_prefill(plan.handle, -2, fake, fake, fake, fake, ctypes.c_float(0.1),
+                                fake, None, None, 0, None) == -5
+    assert lib.segpaged_prefill(plan.handle, 0, fake, fake, fake, fake, ctypes.c_float(-1.0),
+                                fake, None, None, 0, None) == -1
+    dplan = sp.Plan(W.tiny("decode"))
+    need = dplan.sizes.decode_workspace_bytes
+    assert lib.segpaged_decode(dplan.handle, 0, fake, fake, fake, fake, ctypes.c_float(0.1),
+                               fake, None, fake, need - 1, None) == -3
+    assert lib.segpaged_decode(dplan.handle, 0, fake, fake, fake, fake, ctypes.c_float(0.1),
+                               fake, None, None, need, None) == -1
+    assert lib.segpaged_plan_stats(plan.handle, 3, ctypes.byref(sp.Stats())) == -5
+
+
+def test_library_exports_every_header_symbol():
+    hdr = open(os.path.join(ROOT, "include", "segpaged.h")).read()
+    names = re.findall(r"SEGPAGED_API\s+[\w\s\*]+?\b(segpaged_\w+)\s*\(", hdr)
+    assert len(names) >= 9
+    lib = sp.library()
+    for nm in names:
+        assert hasattr(lib, nm), nm
+    out = subprocess.run(["nm", "-D", "--defined-only", sp.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r" T (segpaged_\w+)", out))
+    assert set(names) == exported
+    assert lib.segpaged_version() >= 100
