@@ -1,0 +1,352 @@
+"""SegPagedAttention throughput on one MI355X.
+
+One step is one pass of the whole hot path:
+  prefill leg  long-prefill workload: one 131072-token sequence, 64 layers x
+               (64 Q / 8 KV heads, D 128, page 64, 15% global heads, local
+               sink 4 / window 8192); per layer segpaged_build (prefill form,
+               dense K/V -> pages) then segpaged_prefill
+  decode leg   Llama-3.3-70B-shaped decode: 8 sequences x 32768 tokens, 80
+               layers (64 Q / 8 KV heads, 15% global, local sink 4 / window
+               8192, page 64); one segpaged_decode over all 80 layers
+               (split-K partials + combine). The decode-form cache is built
+               once before timing (KV-write time).
+Inputs are seeded N(0,1) bf16, resident in HBM before timing.
+
+Prints one JSON line: value = prefill tokens per second of the whole step;
+decode KV GB/s, rooflines of the prefill and decode kernels (HIP events on the
+launch stream), the oracle's CPU rate on a bounded sample, and the dense-mask
+torch SDPA comparison on the same GPU.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SegPaged prefill tok/s & decode KV GB/s (% of peak) at 32K/128K vs dense-mask"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFS = 2500.0         # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--prefill-layers", type=int, default=64)
+    ap.add_argument("--prefill-n", type=int, default=131072)
+    ap.add_argument("--decode-layers", type=int, default=80)
+    ap.add_argument("--decode-n", type=int, default=32768)
+    ap.add_argument("--decode-reps", type=int, default=20)
+    ap.add_argument("--distinct", type=int, default=8,
+                    help="distinct Q and dense K/V tensors the prefill layers cycle through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(units shard by KV head with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import sparse_attention_segmentpagetable_amd as sp
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------------ prefill setup
+    pspec = W.long_prefill(num_layers=args.prefill_layers, n=args.prefill_n)
+    pplan = sp.Plan(pspec)
+    pz = pplan.sizes
+    pb = pplan.allocate(dev, workspace=False)
+    N, Hq, Hkv, D = args.prefill_n, pspec.num_q_heads, pspec.num_kv_heads, pspec.head_dim
+    nd = min(args.distinct, args.prefill_layers)
+    log(f"prefill: {args.prefill_layers} layers x {N} tokens, pool {2 * pz.pool_bytes / 1e9:.1f} GB,"
+        f" items {pz.prefill_items}")
+    qs = [W.randn_bf16_device((N, Hq, D), pspec.seed, W.TAG_Q, l, dev) for l in range(nd)]
+    ks = [W.randn_bf16_device((N, Hkv, D), pspec.seed, W.TAG_K, l, dev) for l in range(nd)]
+    vs = [W.randn_bf16_device((N, Hkv, D), pspec.seed, W.TAG_V, l, dev) for l in range(nd)]
+    o_pre = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=dev)
+    lse_pre = torch.empty((N, Hq), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    pstats = [pplan.stats(l) for l in range(args.prefill_layers)]
+    prefill_flops = sum(4 * D * pspec.group * s["prefill_pairs"] for s in pstats)
+    build_bytes = sum(2 * 2 * D * 2 * s["retained_tokens"] for s in pstats)  # K+V, read + write
+
+    # ------------------------------------------------------------------ decode setup
+    dspec = W.llama70b_decode(num_layers=args.decode_layers, n=args.decode_n)
+    dplan = sp.Plan(dspec)
+    dz = dplan.sizes
+    db = dplan.allocate(dev)
+    B = dspec.num_seqs
+    log(f"decode: {args.decode_layers} layers x {B} x {args.decode_n}, pool "
+        f"{2 * dz.pool_bytes / 1e9:.1f} GB, items {dz.decode_items}, ws {dz.decode_workspace_bytes / 1e6:.0f} MB")
+    for l in range(args.decode_layers):
+        kd = W.randn_bf16_device((B * args.decode_n, Hkv, D), dspec.seed, W.TAG_K, l, dev)
+        vd = W.randn_bf16_device((B * args.decode_n, Hkv, D), dspec.seed, W.TAG_V, l, dev)
+        sp.build(dplan, l, kd, vd, db["table"], db["k_pool"], db["v_pool"])
+        del kd, vd
+    q_dec = W.randn_bf16_device((args.decode_layers, B, Hq, D), dspec.seed, W.TAG_Q, 0, dev)
+    o_dec = torch.empty_like(q_dec)
+    lse_dec = torch.empty((args.decode_layers, B, Hq), dtype=torch.float32, device=dev)
+    dstats = dplan.stats(-1)
+    decode_bytes = dstats["decode_tokens"] * 2 * D * 2  # K and V, bf16, each visible key once
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    rec = {"build": [], "prefill": [], "decode": []}
+
+    def step(record):
+        for l in range(args.prefill_layers):
+            e0, e1, e2 = ev(), ev(), ev()
+            e0.record(stream)
+            sp.build(pplan, l, ks[l % nd], vs[l % nd], pb["table"], pb["k_pool"], pb["v_pool"])
+            e1.record(stream)
+            sp.prefill(pplan, l, qs[l % nd], pb["table"], pb["k_pool"], pb["v_pool"], scale,
+                       o_pre, lse_pre)
+            e2.record(stream)
+            if record:
+                rec["build"].append((e0, e1))
+                rec["prefill"].append((e1, e2))
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        sp.decode(dplan, -1, q_dec, db["table"], db["k_pool"], db["v_pool"], scale, o_dec,
+                  lse_dec, workspace=db["workspace"])
+        e1.record(stream)
+        if record:
+            rec["decode"].append((e0, e1))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    dur = {k: [a.elapsed_time(b) for a, b in v] for k, v in rec.items()}
+
+    # extra decode-only repetitions for a stable bandwidth figure
+    reps = []
+    for _ in range(args.decode_reps):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        sp.decode(dplan, -1, q_dec, db["table"], db["k_pool"], db["v_pool"], scale, o_dec,
+                  lse_dec, workspace=db["workspace"])
+        e1.record(stream)
+        reps.append((e0, e1))
+    torch.cuda.synchronize()
+    dec_ms = [a.elapsed_time(b) for a, b in reps]
+    dec_med = float(np.median(dec_ms))
+
+    pre_ms_layer = float(np.mean(dur["prefill"]))
+    pre_ms_step = float(np.sum(dur["prefill"])) / args.steps
+    bld_ms_step = float(np.sum(dur["build"])) / args.steps
+    pre_tflops = prefill_flops / (pre_ms_step * 1e-3) / 1e12
+    dec_gbs = decode_bytes / (dec_med * 1e-3) / 1e9
+    value = N / (ms_step * 1e-3)
+    log(f"step {ms_step:.1f} ms: build {bld_ms_step:.1f} ms, prefill {pre_ms_step:.1f} ms "
+        f"({pre_tflops:.0f} TF/s), decode {dec_med:.3f} ms ({dec_gbs:.0f} GB/s)")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 Q/K/V, seeded head classes",
+        "config": {
+            "workload": (f"long-prefill {N} tokens x {args.prefill_layers} layers (64 Q / 8 KV "
+                         f"heads, D 128, page 64, 15% global, local sink 4 window 8192; build + "
+                         f"prefill per layer) + llama70b-shaped decode {B} x {args.decode_n} x "
+                         f"{args.decode_layers} layers (one all-layer decode call)"),
+            "prefill_tokens_per_step": N,
+            "prefill_layers": args.prefill_layers,
+            "decode_batch": B,
+            "decode_context": args.decode_n,
+            "decode_layers": args.decode_layers,
+            "distinct_input_layers": nd,
+        },
+        "prefill": {
+            "tok_per_s_kernels": round(N / ((pre_ms_step + bld_ms_step) * 1e-3), 2),
+            "ms_prefill_per_step": round(pre_ms_step, 3),
+            "ms_build_per_step": round(bld_ms_step, 3),
+            "ms_prefill_per_layer": round(pre_ms_layer, 4),
+            "algorithmic_flops_per_step": prefill_flops,
+            "tflops": round(pre_tflops, 1),
+            "build_gbs": round(build_bytes / (bld_ms_step * 1e-3) / 1e9, 1),
+        },
+        "decode": {
+            "value": round(dec_gbs, 1),
+            "unit": "GB/s",
+            "frac_of_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "ms_median": round(dec_med, 4),
+            "ms_min": round(float(np.min(dec_ms)), 4),
+            "reps": args.decode_reps,
+            "kv_bytes": decode_bytes,
+            "ms_in_steps": [round(x, 4) for x in dur["decode"]],
+        },
+        "roofline": {
+            "kernel": "prefill_kernel",
+            "bound": "mfma",
+            "achieved": round(pre_tflops, 1),
+            "peak": BF16_PEAK_TFS,
+            "unit": "TFLOP/s",
+            "frac": round(pre_tflops / BF16_PEAK_TFS, 4),
+            "traffic": None,
+        },
+        "roofline_decode": {
+            "kernel": "decode_partial_kernel + decode_combine_kernel",
+            "bound": "hbm",
+            "achieved": round(dec_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+
+    if not args.no_dense:
+        try:
+            out["dense_mask"] = dense_mask_baseline(torch, W, pspec, dspec, ks[0], vs[0], qs[0],
+                                                    dev, pre_ms_layer, dec_med, args, log)
+        except Exception as e:  # the comparison path is optional context
+            out["dense_mask"] = {"error": f"{type(e).__name__}: {e}"[:300]}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(torch, W, pspec, qs[0], ks[0], vs[0], args, log)
+    print(json.dumps(out), flush=True)
+
+
+def dense_mask_baseline(torch, W, pspec, dspec, k0, v0, q0, dev, pre_ms_layer, dec_ms, args, log):
+    """The pages' comparison path: dense K/V plus a boolean attention mask through
+    torch SDPA on the same GPU. The G query heads of a KV head share its mask, so
+    they are folded into the query-length axis: SDPA reads each KV head once (no
+    K/V repetition). Timed on a slice and scaled linearly: a dense-mask row costs
+    the same at every position."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    import torch.nn.functional as F
+    res = {}
+    N, Hq, Hkv, D, G = args.prefill_n, pspec.num_q_heads, pspec.num_kv_heads, pspec.head_dim, pspec.group
+    R = 256
+    rows = torch.arange(N - R, N, device=dev)
+    j = torch.arange(N, device=dev)
+    masks = []
+    for h in range(Hkv):
+        kind, s, w = pspec.head_class(0, h)
+        m = j[None, :] <= rows[:, None]
+        if kind == W.LOCAL:
+            m = m & ((j[None, :] < s) | (j[None, :] > rows[:, None] - w))
+        masks.append(m.repeat_interleave(G, dim=0))      # rows (position, head-in-group)
+    mask = torch.stack(masks)[None]                     # [1, Hkv, R*G, N]
+    q = q0[N - R:].reshape(R, Hkv, G, D).permute(1, 0, 2, 3).reshape(1, Hkv, R * G, D).contiguous()
+    k = k0.permute(1, 0, 2)[None].contiguous()          # [1, Hkv, N, D]
+    v = v0.permute(1, 0, 2)[None].contiguous()
+    backend = "EFFICIENT_ATTENTION"
+    with sdpa_kernel([SDPBackend.EFFICIENT_ATTENTION]):
+        for _ in range(2):
+            F.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            F.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+        e1.record()
+        torch.cuda.synchronize()
+    t_slice = e0.elapsed_time(e1) / 3
+    t_layer = t_slice * N / R
+    res["prefill"] = {"backend": f"torch SDPA {backend}, bool mask, GQA group folded into rows",
+                      "rows_timed": R, "ms_slice": round(t_slice, 3),
+                      "ms_per_layer_extrapolated": round(t_layer, 2),
+                      "speedup_vs_dense_mask": round(t_layer / pre_ms_layer, 2)}
+    del q, k, v, mask
+    log(f"dense-mask prefill: {t_layer:.1f} ms/layer (extrapolated) vs {pre_ms_layer:.1f}")
+    # decode: a few layers of the decode workload on dense K/V [B, Hkv, n, D]
+    B, n = dspec.num_seqs, args.decode_n
+    nl = 4
+    kd = [W.randn_bf16_device((B, Hkv, n, D), dspec.seed, 99, l, dev) for l in range(nl)]
+    vd = [W.randn_bf16_device((B, Hkv, n, D), dspec.seed, 98, l, dev) for l in range(nl)]
+    qd = W.randn_bf16_device((B, Hkv, G, D), dspec.seed, 97, 0, dev)
+    jj = torch.arange(n, device=dev)
+    dmasks = []
+    for l in range(nl):
+        mm = []
+        for h in range(Hkv):
+            kind, s, w = dspec.head_class(l, h)
+            m = jj <= n - 1
+            if kind == W.LOCAL:
+                m = m & ((jj < s) | (jj > n - 1 - w))
+            mm.append(m)
+        dmasks.append(torch.stack(mm)[None, :, None, :].expand(B, Hkv, G, n).contiguous())
+    with sdpa_kernel([SDPBackend.EFFICIENT_ATTENTION]):
+        for l in range(nl):
+            F.scaled_dot_product_attention(qd, kd[l], vd[l], attn_mask=dmasks[l])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for l in range(nl):
+            F.scaled_dot_product_attention(qd, kd[l], vd[l], attn_mask=dmasks[l])
+        e1.record()
+        torch.cuda.synchronize()
+    t_all = e0.elapsed_time(e1) / nl * args.decode_layers
+    dense_bytes = 2 * B * Hkv * n * D * 2 * args.decode_layers
+    res["decode"] = {"backend": f"torch SDPA {backend}, bool mask, GQA group folded into rows",
+                     "layers_timed": nl, "ms_all_layers_extrapolated": round(t_all, 3),
+                     "dense_kv_gbs": round(dense_bytes / (t_all * 1e-3) / 1e9, 1),
+                     "speedup_vs_dense_mask": round(t_all / dec_ms, 2)}
+    log(f"dense-mask decode: {t_all:.2f} ms (80 layers, extrapolated) vs {dec_ms:.3f}")
+    return res
+
+
+def cpu_baseline(torch, W, pspec, q0, k0, v0, args, log):
+    """The oracle as it stands (numpy fp64, dense scores + explicit mask), timed on
+    the host cores on a bounded sample: rows of layer 0 at seeded positions, all
+    64 Q heads, against the full 131072-token context."""
+    from oracle import attention as OA
+    N = args.prefill_n
+    kb = k0.view(torch.int16).cpu().numpy().view(np.uint16)
+    vb = v0.view(torch.int16).cpu().numpy().view(np.uint16)
+    rng = np.random.default_rng([pspec.seed, 77])
+    cores = len(os.sched_getaffinity(0))
+    done_rows, spent = 0, 0.0
+    chunk = 2
+    while spent < args.cpu_seconds:
+        pos = np.sort(rng.choice(N, size=chunk, replace=False))
+        qr = q0[torch.as_tensor(pos, device=q0.device)].view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        OA.attention_rows(pspec, 0, 0, pos, qr, kb, vb)
+        spent += time.perf_counter() - t0
+        done_rows += chunk
+    head_rows_per_s = done_rows * pspec.num_q_heads / spent
+    tok_s = head_rows_per_s / (pspec.num_q_heads * args.prefill_layers)
+    log(f"oracle: {done_rows} rows x 64 heads in {spent:.1f} s -> {tok_s:.4f} tok/s")
+    return {"value": round(tok_s, 5), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{done_rows} query rows of layer 0 at seeded positions, all "
+                       f"{pspec.num_q_heads} Q heads, full {N}-token context; scaled to "
+                       f"{args.prefill_layers} layers x {pspec.num_q_heads} heads per token"),
+            "seconds": round(spent, 2)}
+
+
+if __name__ == "__main__":
+    main()
