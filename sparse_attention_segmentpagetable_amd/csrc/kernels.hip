@@ -300,15 +300,20 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// prefill. One workgroup (4 waves) per tile of 128 query rows = the G query
-// heads of one KV head x (128 / G) consecutive positions, so every staged K/V
-// block serves all G heads. Keys stream in blocks of 64 slots through LDS
-// (double-buffered; the LDS tiles have the page layouts, so a P = 64 page is
-// copied verbatim). Per block and wave (32 query rows), v_mfma_f32_32x32x16_bf16:
-//   S^T[32 keys][32 rows] = K . Q^T    (2 tiles cover the 64 keys)
-//   O^T[32 dims][32 rows] += V^T . P^T  (D/32 tiles)
-// Only blocks that some row of the tile can see are visited; blocks every row
-// sees entirely skip the per-element predicate.
+// prefill. One workgroup (4 waves) per tile of 256 query rows = the G query
+// heads of one KV head x (256 / G) consecutive positions, so every K/V block
+// read serves all G heads. Keys stream in blocks of 32 slots straight into LDS
+// (global_load_lds_dwordx4, three buffers, one barrier per block); the LDS tiles
+// have the page layouts. Per 32-key block, each wave (64 query rows = two
+// 32-row tiles) runs v_mfma_f32_32x32x16_bf16:
+//   S^T[32 keys][32 rows] = K . Q^T      (2 row tiles)
+//   O^T[32 dims][32 rows] += V^T . P^T   (D/32 dim tiles x 2 row tiles)
+// so every K or V fragment read from LDS feeds two MFMAs. The scores of block
+// j + 1 are issued before the softmax of block j, in one basic block, so the
+// MFMAs overlap the exponentials. Only blocks some row of the tile can see are
+// visited; blocks every row sees entirely skip the per-element predicate. The
+// running max is raised only when a block's max exceeds it by more than 2^8,
+// which keeps the output exact and skips almost every rescale.
 // ---------------------------------------------------------------------------
 // Up to four runs of consecutive key blocks, kept in named scalars (no
 // dynamically indexed private array).
@@ -334,6 +339,14 @@ struct Runs {
   }
 };
 
+__device__ __forceinline__ void lds_dma16(const uint16_t* gsrc, uint16_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0,
+                                   0);
+}
+// s_waitcnt with only vmcnt constrained (expcnt / lgkmcnt left at their maxima)
+#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((0x0F70) | ((n) & 15) | (((n) >> 4) << 14))
+
 template <int D>
 __global__ __launch_bounds__(256) void prefill_kernel(
     const int32_t* __restrict__ tab, int32_t off_seqs, int32_t off_units, int32_t off_pages,
@@ -341,13 +354,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, float* __restrict__ lse,
     int64_t q_layer_stride, int64_t lse_layer_stride, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vp, int32_t G, int32_t Hq, int32_t P, int32_t log2P, float c) {
-  constexpr int KCH = D / 8;          // 16 B chunks per key row
-  constexpr int KSTEP = D / 16;       // k-steps of QK^T
-  constexpr int MD = D / 32;          // O^T tiles
-  constexpr int KLOAD = KCH * 64 / 256;  // K chunks per thread per block
-  constexpr int VLOAD = 8 * D / 256;     // V chunks per thread per block
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][KCH * 64 * 8];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][8 * D * 8];
+  constexpr int BK = kBlockN;          // keys per block (32)
+  constexpr int KCH = D / 8;           // 16 B chunks per key row
+  constexpr int KSTEP = D / 16;        // k-steps of QK^T
+  constexpr int MD = D / 32;           // O^T dim tiles
+  constexpr int TILE = KCH * BK * 8;   // elements of one K (or V) block tile
+  constexpr int NLD = TILE / 8 / 256;  // LDS-DMA instructions per lane per block, each of K and V
+  __shared__ __attribute__((aligned(16))) uint16_t sK[3][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[3][TILE];
 
   const int32_t it = item_b + (int32_t)blockIdx.x;
   if (it >= item_e) return;
@@ -365,21 +379,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, g = lane >> 5;
-  const int row = 32 * wave + n;
-  const int32_t pq = row / G, j = row % G;
-  const int32_t qpos = r0 + pq;
-  const bool row_ok = pq < r1 - r0;
-  const int64_t orow = (int64_t)qrow0 + (qpos - q0);
-  const int hq = h * G + j;
-
-  bf16x8 qf[KSTEP];
-  {
-    const uint16_t* qp = q + (int64_t)l * q_layer_stride + (orow * Hq + hq) * D + g * 8;
+  int32_t qpos[2];
+  bool row_ok[2];
+  int64_t orow[2];
+  int hq[2];
+  bf16x8 qf[2][KSTEP];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int row = 64 * wave + 32 * nt + n;
+    const int32_t pq = row / G, j = row % G;
+    qpos[nt] = r0 + pq;
+    row_ok[nt] = pq < r1 - r0;
+    orow[nt] = (int64_t)qrow0 + (qpos[nt] - q0);
+    hq[nt] = h * G + j;
+    const uint16_t* qp = q + (int64_t)l * q_layer_stride + (orow[nt] * Hq + hq[nt]) * D + g * 8;
 #pragma unroll
     for (int ks = 0; ks < KSTEP; ++ks) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = ld16(qp + ks * 16);
-      qf[ks] = as_bf16x8(v);
+      if (row_ok[nt]) v = ld16(qp + ks * 16);
+      qf[nt][ks] = as_bf16x8(v);
     }
   }
 
@@ -396,13 +414,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         const int32_t mid = (a + z) >> 1;
         if (rpos[mid] <= rmax) a = mid + 1; else z = mid;
       }
-      if (a > 0) runs.add(s, 0, (a + 63) >> 6);
+      if (a > 0) runs.add(s, 0, (a + BK - 1) / BK);
     } else if (kind == SEGPAGED_LOCAL) {
       const int32_t ahi = min(len, min(sink, rmax + 1) - pos0);
       const int32_t blo = max(0, r0 - win + 1 - pos0);
       const int32_t bhi = min(len, rmax + 1 - pos0);
-      const int32_t A1 = ahi > 0 ? (ahi + 63) >> 6 : 0;
-      const int32_t B0 = blo >> 6, B1 = bhi > blo ? (bhi + 63) >> 6 : B0;
+      const int32_t A1 = ahi > 0 ? (ahi + BK - 1) / BK : 0;
+      const int32_t B0 = blo / BK, B1 = bhi > blo ? (bhi + BK - 1) / BK : B0;
       if (A1 > 0 && B1 > B0 && B0 <= A1) {
         runs.add(s, 0, max(A1, B1));
       } else {
@@ -411,133 +429,149 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       }
     } else {
       const int32_t hi = min(len, rmax + 1 - pos0);
-      if (hi > 0) runs.add(s, 0, (hi + 63) >> 6);
+      if (hi > 0) runs.add(s, 0, (hi + BK - 1) / BK);
     }
   }
   const int32_t nblocks = runs.total;
 
-  f32x16 oacc[MD];
+  // ---- K/V block -> LDS buffer, straight from the pool pages. Keys past the
+  // segment's end read a valid key of the segment instead (finite values that
+  // the predicate masks), so no LDS slot is left stale.
+  auto issue = [&](int32_t blk, int buf) {
+    int s;
+    int32_t kb;
+    runs.at(blk, s, kb);
+    const int32_t len = s ? sl1 : sl0, base = s ? sb1 : 0;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int c0 = 64 * (wave + 4 * i), cidx = c0 + lane;
+      const int dc = cidx / BK, t = cidx % BK;  // K chunk: key t, dims 8dc .. 8dc+7
+      const int32_t off = min(kb * BK + t, len - 1);
+      const int32_t slot = base + off;
+      lds_dma16(kp + pages[slot >> log2P] * PD + ((int64_t)dc * P + (slot & (P - 1))) * 8,
+                &sK[buf][c0 * 8]);
+    }
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int c0 = 64 * (wave + 4 * i), cidx = c0 + lane;
+      const int tc = cidx / D, d = cidx % D;    // V chunk: keys 8tc .. 8tc+7, dim d
+      int32_t off8 = kb * BK + 8 * tc;
+      if (off8 >= len) off8 = (len - 1) & ~7;
+      const int32_t slot = base + off8;
+      lds_dma16(vp + pages[slot >> log2P] * PD + ((int64_t)((slot & (P - 1)) >> 3) * D + d) * 8,
+                &sV[buf][c0 * 8]);
+    }
+  };
+
+  // S^T row rho of the 32-key tile <- key 16(q'/2) + 8gg + 4(q'%2) + e', rho = 8q' + 4gg + e';
+  // then lane (n, g) reg i holds key 16(i/8) + 8g + (i%8): for PV k-step kk it owns the
+  // 8 consecutive keys 16kk + 8g .. +7, one V brick.
+  const int rq = n >> 3, rgg = (n >> 2) & 1, re = n & 3;
+  const int tokA = 16 * (rq >> 1) + 8 * rgg + 4 * (rq & 1) + re;
+  auto qk = [&](int buf, f32x16 (&sc)[2]) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[nt][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSTEP; ++ks) {
+      const bf16x8 a = as_bf16x8(ld16(&sK[buf][((2 * ks + g) * BK + tokA) * 8]));
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[nt][ks], sc[nt], 0, 0, 0);
+    }
+  };
+
+  f32x16 oacc[MD][2];
 #pragma unroll
   for (int md = 0; md < MD; ++md)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[md][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // ---- staging: global -> registers -> LDS
-  u32x4 kreg[KLOAD], vreg[VLOAD];
-  auto stage_load = [&](int s, int32_t kb) {
-    const int32_t len = s ? sl1 : sl0, base = s ? sb1 : 0;
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int i = 0; i < KLOAD; ++i) {
-      const int cidx = tid + 256 * i;
-      const int t = cidx & 63, dc = cidx >> 6;
-      const int32_t off = kb * 64 + t;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (off < len) {
-        const int32_t slot = base + off;
-        v = ld16(kp + pages[slot >> log2P] * PD + ((int64_t)dc * P + (slot & (P - 1))) * 8);
-      }
-      kreg[i] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < VLOAD; ++i) {
-      const int cidx = tid + 256 * i;
-      const int d = cidx % D, tc = cidx / D;
-      const int32_t off = kb * 64 + 8 * tc;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (off < len) {
-        const int32_t slot = base + off;
-        v = ld16(vp + pages[slot >> log2P] * PD + ((int64_t)((slot & (P - 1)) >> 3) * D + d) * 8);
-      }
-      vreg[i] = v;
-    }
-  };
-  auto stage_store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KLOAD; ++i) st16(&sK[buf][(tid + 256 * i) * 8], kreg[i]);
-#pragma unroll
-    for (int i = 0; i < VLOAD; ++i) st16(&sV[buf][(tid + 256 * i) * 8], vreg[i]);
-  };
-
-  // S^T row rho of a 32-key tile <- key 16(q'/2) + 8gg + 4(q'%2) + e', rho = 8q' + 4gg + e'
-  const int rq = n >> 3, rgg = (n >> 2) & 1, re = n & 3;
-  const int tokA = 16 * (rq >> 1) + 8 * rgg + 4 * (rq & 1) + re;
+      for (int i = 0; i < 16; ++i) oacc[md][nt][i] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x16 s_a[2], s_b[2];
 
   if (nblocks > 0) {
+    issue(0, 0);
+    if (nblocks > 1) {
+      issue(1, 1);
+      WAIT_VMCNT(2 * NLD);
+    } else {
+      WAIT_VMCNT(0);
+    }
+    __syncthreads();
+    qk(0, s_a);
+  }
+
+  // one block: s_cur holds the scores of block blk, s_nxt receives block blk + 1's
+  auto step = [&](int32_t blk, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+    const int buf = blk % 3;
+    WAIT_VMCNT(0);      // block blk + 1 has landed (this wave's part)
+    __syncthreads();    // ... for every wave; and every wave is done with block blk - 1
+    if (blk + 2 < nblocks) issue(blk + 2, (blk + 2) % 3);
+
+    // ---- predicate of block blk, when some key is not visible to every row
     int s;
     int32_t kb;
-    runs.at(0, s, kb);
-    stage_load(s, kb);
-    stage_store(0);
-    __syncthreads();
-  }
-  for (int32_t blk = 0; blk < nblocks; ++blk) {
-    const int buf = blk & 1;
-    int s;
-    int32_t cur_kb;
-    runs.at(blk, s, cur_kb);
-    const bool has_next = blk + 1 < nblocks;
-    if (has_next) {
-      int ns;
-      int32_t nkb;
-      runs.at(blk + 1, ns, nkb);
-      stage_load(ns, nkb);
-    }
-
-    // ---- S^T = K . Q^T
-    f32x16 sacc[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[mt][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KSTEP; ++ks) {
-        const bf16x8 a = as_bf16x8(ld16(&sK[buf][((2 * ks + g) * 64 + 32 * mt + tokA) * 8]));
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
-      }
-    }
-    // lane (n, g), reg i of tile mt holds key 32mt + 16(i/8) + 8g + (i%8) of the block
+    runs.at(blk, s, kb);
     const int32_t len = s ? sl1 : sl0, pos0 = s ? sp1 : sp0;
-    const int32_t o0 = cur_kb * 64;
+    const int32_t o0 = kb * BK;
     bool interior = false;
-    if (pos0 >= 0 && o0 + 64 <= len) {
-      const int32_t kp0 = pos0 + o0, kp1 = kp0 + 63;
+    if (pos0 >= 0 && o0 + BK <= len) {
+      const int32_t kp0 = pos0 + o0, kp1 = kp0 + BK - 1;
       interior = kp1 <= r0;
       if (kind == SEGPAGED_LOCAL) interior = interior && (kp1 < sink || kp0 > rmax - win);
     }
     if (!interior) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int i = 0; i < 16; ++i) {
+        const int32_t off = o0 + 16 * (i >> 3) + 8 * g + (i & 7);
+        int32_t kpos = 0x7FFFFFFF;
+        if (off < len) kpos = pos0 >= 0 ? pos0 + off : rpos[off];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int32_t off = o0 + 32 * mt + 16 * (i >> 3) + 8 * g + (i & 7);
-          bool vis = off < len;
-          if (vis) {
-            const int32_t kpos = pos0 >= 0 ? pos0 + off : rpos[off];
-            vis = kpos <= qpos;
-            if (kind == SEGPAGED_LOCAL) vis = vis && (kpos < sink || kpos > qpos - win);
-          }
-          if (!vis) sacc[mt][i] = -INFINITY;
+        for (int nt = 0; nt < 2; ++nt) {
+          bool vis = kpos <= qpos[nt];
+          if (kind == SEGPAGED_LOCAL) vis = vis && (kpos < sink || kpos > qpos[nt] - win);
+          if (!vis) s_cur[nt][i] = -INFINITY;
         }
+      }
     }
-    // ---- online softmax (log2 domain)
-    float mx = -INFINITY;
+
+    // ---- scores of the next block (the last iteration computes an unused tile)
+    qk((blk + 1) % 3, s_nxt);
+
+    // ---- online softmax of block blk in the log2 domain
+    float mc[2];
+    bool need[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int nt = 0; nt < 2; ++nt) {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][i]);
-    mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(m_run, mx * c);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float ps = 0.f;
-    bf16x8 pf[2][2];
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[nt][i]);
+      mx = wave_max_xor(mx, 32);
+      mc[nt] = mx * c;
+      need[nt] = mc[nt] > m_run[nt] + 8.f;
+    }
+    if (__builtin_amdgcn_ballot_w64(need[0] || need[1])) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+      for (int nt = 0; nt < 2; ++nt) {
+        const float alpha = need[nt] ? fast_exp2(m_run[nt] - mc[nt]) : 1.f;
+        if (need[nt]) m_run[nt] = mc[nt];
+        l_run[nt] *= alpha;
+#pragma unroll
+        for (int md = 0; md < MD; ++md) oacc[md][nt] *= alpha;
+      }
+    }
+    bf16x8 pf[2][2];  // [nt][kk]
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
       float p[16];
+      float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        p[i] = fast_exp2(fmaf(sacc[mt][i], c, -m_use));
+        p[i] = fast_exp2(fmaf(s_cur[nt][i], c, -m_use));
         ps += p[i];
       }
 #pragma unroll
@@ -547,45 +581,46 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         w.y = pack_bf16x2(p[8 * kk + 2], p[8 * kk + 3]);
         w.z = pack_bf16x2(p[8 * kk + 4], p[8 * kk + 5]);
         w.w = pack_bf16x2(p[8 * kk + 6], p[8 * kk + 7]);
-        pf[mt][kk] = as_bf16x8(w);
+        pf[nt][kk] = as_bf16x8(w);
       }
+      l_run[nt] += ps;
     }
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
     // ---- O^T += V^T . P^T
 #pragma unroll
-    for (int md = 0; md < MD; ++md) {
-      oacc[md] *= alpha;
+    for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 a = as_bf16x8(ld16(&sV[buf][((2 * kk + g) * D + 32 * md + n) * 8]));
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 a =
-              as_bf16x8(ld16(&sV[buf][((4 * mt + 2 * kk + g) * D + 32 * md + n) * 8]));
-          oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[mt][kk], oacc[md], 0, 0, 0);
-        }
-    }
-    if (has_next) stage_store(buf ^ 1);
-    __syncthreads();
+        for (int nt = 0; nt < 2; ++nt)
+          oacc[md][nt] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[nt][kk], oacc[md][nt], 0, 0, 0);
+      }
+  };
+  for (int32_t blk = 0; blk < nblocks; blk += 2) {
+    step(blk, s_a, s_b);
+    if (blk + 1 < nblocks) step(blk + 1, s_b, s_a);
   }
 
-  // ---- epilogue
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (row_ok) {
+  // ---- epilogue: O^T lane (n, g) reg i of dim tile md -> dim 32md + 8(i/4) + 4g + (i%4)
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const float l_tot = l_run[nt] + __shfl_xor(l_run[nt], 32, 64);
+    if (!row_ok[nt]) continue;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* op = o + (int64_t)l * q_layer_stride + (orow * Hq + hq) * D;
+    uint16_t* op = o + (int64_t)l * q_layer_stride + (orow[nt] * Hq + hq[nt]) * D;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         u32x2 w;
-        w.x = pack_bf16x2(oacc[md][4 * qd + 0] * inv, oacc[md][4 * qd + 1] * inv);
-        w.y = pack_bf16x2(oacc[md][4 * qd + 2] * inv, oacc[md][4 * qd + 3] * inv);
+        w.x = pack_bf16x2(oacc[md][nt][4 * qd + 0] * inv, oacc[md][nt][4 * qd + 1] * inv);
+        w.y = pack_bf16x2(oacc[md][nt][4 * qd + 2] * inv, oacc[md][nt][4 * qd + 3] * inv);
         *reinterpret_cast<u32x2*>(op + 32 * md + 8 * qd + 4 * g) = w;
       }
     if (lse && g == 0)
-      lse[(int64_t)l * lse_layer_stride + orow * Hq + hq] =
-          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+      lse[(int64_t)l * lse_layer_stride + orow[nt] * Hq + hq[nt]] =
+          l_tot > 0.f ? (m_run[nt] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   }
 }
 

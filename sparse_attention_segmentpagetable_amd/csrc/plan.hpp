@@ -25,8 +25,8 @@ enum UnitField {
 // Work lists that follow the table in the device image.
 constexpr int kDecItemInts = 4;   // unit, slot_lo, slot_hi, 0
 constexpr int kPreItemInts = 2;   // unit, first query position of the tile
-constexpr int kPrefillRows = 128; // query rows per prefill tile: G heads x (128 / G) positions
-constexpr int kBlockN = 64;       // keys per prefill block
+constexpr int kPrefillRows = 256; // query rows per prefill tile: G heads x (256 / G) positions
+constexpr int kBlockN = 32;       // keys per prefill block
 constexpr int kMaxGroup = 16;     // Q heads per KV head the decode kernel supports
 
 struct LayerRange {

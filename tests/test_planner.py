@@ -124,7 +124,7 @@ def test_prefill_items_tile_every_row_once(spec):
     plan = sp.Plan(spec)
     _, _, _, pre = _decode_items(plan)
     G = spec.group
-    bq = 128 // G
+    bq = 256 // G
     got = {}
     for u, r0 in pre:
         got.setdefault(int(u), []).append(int(r0))
