@@ -303,7 +303,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 // prefill. One workgroup (4 waves) per tile of 256 query rows = the G query
 // heads of one KV head x (256 / G) consecutive positions, so every K/V block
 // read serves all G heads. Keys stream in blocks of 32 slots straight into LDS
-// (global_load_lds_dwordx4, three buffers, one barrier per block); the LDS tiles
+// (global_load_lds_dwordx4, an 8-buffer ring, one barrier per block); the LDS tiles
 // have the page layouts. Per 32-key block, each wave (64 query rows = two
 // 32-row tiles) runs v_mfma_f32_32x32x16_bf16:
 //   S^T[32 keys][32 rows] = K . Q^T      (2 row tiles)
@@ -311,31 +311,28 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 // so every K or V fragment read from LDS feeds two MFMAs. The scores of block
 // j + 1 are issued before the softmax of block j, in one basic block, so the
 // MFMAs overlap the exponentials. Only blocks some row of the tile can see are
-// visited; blocks every row sees entirely skip the per-element predicate. The
-// running max is raised only when a block's max exceeds it by more than 2^8,
-// which keeps the output exact and skips almost every rescale.
+// visited; blocks every row sees entirely skip the per-element predicate. Each
+// row's reference max is fixed by its first block with a visible key, so the hot
+// loop never rescales O (exp2 of scores up to 2^64 above it stays finite in fp32
+// and bf16, with unchanged relative precision); a tile whose scores outgrow that
+// margin is recomputed on a path that rescales per block.
 // ---------------------------------------------------------------------------
-// Up to four runs of consecutive key blocks, kept in named scalars (no
-// dynamically indexed private array).
-struct Runs {
-  int32_t n = 0;
-  int32_t s0 = 0, a0 = 0, c0 = 0, s1 = 0, a1 = 0, c1 = 0, s2 = 0, a2 = 0, c2 = 0, s3 = 0, a3 = 0;
-  int32_t total = 0;  // blocks over all runs; c_k = blocks before run k + 1
-  __device__ void add(int32_t seg, int32_t kb0, int32_t kb1) {
-    const int32_t cnt = kb1 - kb0;
-    if (n == 0) { s0 = seg; a0 = kb0; c0 = cnt; }
-    else if (n == 1) { s1 = seg; a1 = kb0; c1 = c0 + cnt; }
-    else if (n == 2) { s2 = seg; a2 = kb0; c2 = c1 + cnt; }
-    else { s3 = seg; a3 = kb0; }
-    total += cnt;
-    ++n;
-  }
+// The key blocks a tile visits: per segment at most two runs of consecutive
+// blocks (A: sink / prefix, B: window), in four fixed scalar slots 0A, 0B, 1A,
+// 1B; empty runs have zero length.
+struct TileRuns {
+  int32_t a0, n0, a1, n1, a2, n2, a3, n3;  // first block and block count per slot
+  __device__ __forceinline__ int32_t total() const { return n0 + n1 + n2 + n3; }
   // block k of the sequence -> (segment, block index within the segment)
-  __device__ void at(int32_t k, int& seg, int32_t& kb) const {
-    if (k < c0 || n == 1) { seg = s0; kb = a0 + k; }
-    else if (k < c1 || n == 2) { seg = s1; kb = a1 + k - c0; }
-    else if (k < c2 || n == 3) { seg = s2; kb = a2 + k - c1; }
-    else { seg = s3; kb = a3 + k - c2; }
+  __device__ __forceinline__ void at(int32_t k, int& seg, int32_t& kb) const {
+    if (k < n0) { seg = 0; kb = a0 + k; return; }
+    k -= n0;
+    if (k < n1) { seg = 0; kb = a1 + k; return; }
+    k -= n1;
+    if (k < n2) { seg = 1; kb = a2 + k; return; }
+    k -= n2;
+    seg = 1;
+    kb = a3 + k;
   }
 };
 
@@ -344,8 +341,47 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* gsrc, uint16_t* lds_wa
                                    (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0,
                                    0);
 }
+__device__ __forceinline__ void lds_dma4(const int32_t* gsrc, int32_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0,
+                                   0);
+}
 // s_waitcnt with only vmcnt constrained (expcnt / lgkmcnt left at their maxima)
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((0x0F70) | ((n) & 15) | (((n) >> 4) << 14))
+
+// Runs of one segment for query rows [r0, rmax]: A = blocks [0, an), B = [b0, b0 + bn).
+__device__ __forceinline__ void segment_runs(int kind, int32_t pos0, int32_t len, int32_t sink,
+                                             int32_t win, int32_t r0, int32_t rmax,
+                                             const int32_t* rpos, int32_t& an, int32_t& b0,
+                                             int32_t& bn) {
+  constexpr int BK = kBlockN;
+  an = 0; b0 = 0; bn = 0;
+  if (len <= 0) return;
+  if (pos0 < 0) {  // gathered: keys with position <= rmax form a prefix
+    int32_t a = 0, z = len;
+    while (a < z) {
+      const int32_t mid = (a + z) >> 1;
+      if (rpos[mid] <= rmax) a = mid + 1; else z = mid;
+    }
+    an = (a + BK - 1) / BK;
+  } else if (kind == SEGPAGED_LOCAL) {
+    const int32_t ahi = min(len, min(sink, rmax + 1) - pos0);
+    const int32_t blo = max(0, r0 - win + 1 - pos0);
+    const int32_t bhi = min(len, rmax + 1 - pos0);
+    const int32_t A1 = ahi > 0 ? (ahi + BK - 1) / BK : 0;
+    const int32_t B0 = blo / BK, B1 = bhi > blo ? (bhi + BK - 1) / BK : B0;
+    if (A1 > 0 && B1 > B0 && B0 <= A1) {
+      an = max(A1, B1);
+    } else {
+      an = A1;
+      b0 = B0;
+      bn = B1 - B0;
+    }
+  } else {
+    const int32_t hi = min(len, rmax + 1 - pos0);
+    an = hi > 0 ? (hi + BK - 1) / BK : 0;
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void prefill_kernel(
@@ -360,8 +396,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   constexpr int MD = D / 32;           // O^T dim tiles
   constexpr int TILE = KCH * BK * 8;   // elements of one K (or V) block tile
   constexpr int NLD = TILE / 8 / 256;  // LDS-DMA instructions per lane per block, each of K and V
-  __shared__ __attribute__((aligned(16))) uint16_t sK[3][TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[3][TILE];
+  constexpr int NBUF = 8;              // LDS ring: NBUF - 2 blocks in flight ahead of block j + 1
+  constexpr int PER_BLOCK = 2 * NLD;   // vmcnt increments per block
+  __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][TILE];
+  __shared__ __attribute__((aligned(16))) int32_t sPos[NBUF][64];
+  __shared__ int32_t sOverflow;
 
   const int32_t it = item_b + (int32_t)blockIdx.x;
   if (it >= item_e) return;
@@ -376,9 +416,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   const int32_t BQ = kPrefillRows / G;
   const int32_t r1 = min(N, r0 + BQ), rmax = r1 - 1;
   const int64_t PD = (int64_t)P * D;
+  const bool gathered = ur[U_S0POS] < 0;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, g = lane >> 5;
+  if (tid == 0) sOverflow = 0;
   int32_t qpos[2];
   bool row_ok[2];
   int64_t orow[2];
@@ -392,95 +434,26 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     row_ok[nt] = pq < r1 - r0;
     orow[nt] = (int64_t)qrow0 + (qpos[nt] - q0);
     hq[nt] = h * G + j;
-    const uint16_t* qp = q + (int64_t)l * q_layer_stride + (orow[nt] * Hq + hq[nt]) * D + g * 8;
+    // rows past the tile read row q0 of the sequence (valid memory) and are never stored
+    const int64_t qrow = row_ok[nt] ? orow[nt] : (int64_t)qrow0;
+    const uint16_t* qp = q + (int64_t)l * q_layer_stride + (qrow * Hq + hq[nt]) * D + g * 8;
 #pragma unroll
-    for (int ks = 0; ks < KSTEP; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok[nt]) v = ld16(qp + ks * 16);
-      qf[nt][ks] = as_bf16x8(v);
-    }
+    for (int ks = 0; ks < KSTEP; ++ks) qf[nt][ks] = as_bf16x8(ld16(qp + ks * 16));
   }
 
   // ---- block runs this tile visits (uniform across the workgroup)
   const int32_t sp0 = ur[U_S0POS], sl0 = ur[U_S0LEN];
   const int32_t sp1 = ur[U_S1POS], sl1 = ur[U_S1LEN];
   const int32_t sb1 = ((sl0 + P - 1) >> log2P) << log2P;  // slot base of segment 1
-  Runs runs;
-  for (int s = 0; s < nseg; ++s) {
-    const int32_t pos0 = s ? sp1 : sp0, len = s ? sl1 : sl0;
-    if (pos0 < 0) {  // gathered: keys with position <= rmax form a prefix
-      int32_t a = 0, z = len;
-      while (a < z) {
-        const int32_t mid = (a + z) >> 1;
-        if (rpos[mid] <= rmax) a = mid + 1; else z = mid;
-      }
-      if (a > 0) runs.add(s, 0, (a + BK - 1) / BK);
-    } else if (kind == SEGPAGED_LOCAL) {
-      const int32_t ahi = min(len, min(sink, rmax + 1) - pos0);
-      const int32_t blo = max(0, r0 - win + 1 - pos0);
-      const int32_t bhi = min(len, rmax + 1 - pos0);
-      const int32_t A1 = ahi > 0 ? (ahi + BK - 1) / BK : 0;
-      const int32_t B0 = blo / BK, B1 = bhi > blo ? (bhi + BK - 1) / BK : B0;
-      if (A1 > 0 && B1 > B0 && B0 <= A1) {
-        runs.add(s, 0, max(A1, B1));
-      } else {
-        if (A1 > 0) runs.add(s, 0, A1);
-        if (B1 > B0) runs.add(s, B0, B1);
-      }
-    } else {
-      const int32_t hi = min(len, rmax + 1 - pos0);
-      if (hi > 0) runs.add(s, 0, (hi + BK - 1) / BK);
-    }
+  TileRuns runs;
+  {
+    int32_t an, b0, bn;
+    segment_runs(kind, sp0, nseg > 0 ? sl0 : 0, sink, win, r0, rmax, rpos, an, b0, bn);
+    runs.a0 = 0; runs.n0 = an; runs.a1 = b0; runs.n1 = bn;
+    segment_runs(kind, sp1, nseg > 1 ? sl1 : 0, sink, win, r0, rmax, rpos, an, b0, bn);
+    runs.a2 = 0; runs.n2 = an; runs.a3 = b0; runs.n3 = bn;
   }
-  const int32_t nblocks = runs.total;
-
-  // ---- K/V block -> LDS buffer, straight from the pool pages. Keys past the
-  // segment's end read a valid key of the segment instead (finite values that
-  // the predicate masks), so no LDS slot is left stale.
-  auto issue = [&](int32_t blk, int buf) {
-    int s;
-    int32_t kb;
-    runs.at(blk, s, kb);
-    const int32_t len = s ? sl1 : sl0, base = s ? sb1 : 0;
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int c0 = 64 * (wave + 4 * i), cidx = c0 + lane;
-      const int dc = cidx / BK, t = cidx % BK;  // K chunk: key t, dims 8dc .. 8dc+7
-      const int32_t off = min(kb * BK + t, len - 1);
-      const int32_t slot = base + off;
-      lds_dma16(kp + pages[slot >> log2P] * PD + ((int64_t)dc * P + (slot & (P - 1))) * 8,
-                &sK[buf][c0 * 8]);
-    }
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int c0 = 64 * (wave + 4 * i), cidx = c0 + lane;
-      const int tc = cidx / D, d = cidx % D;    // V chunk: keys 8tc .. 8tc+7, dim d
-      int32_t off8 = kb * BK + 8 * tc;
-      if (off8 >= len) off8 = (len - 1) & ~7;
-      const int32_t slot = base + off8;
-      lds_dma16(vp + pages[slot >> log2P] * PD + ((int64_t)((slot & (P - 1)) >> 3) * D + d) * 8,
-                &sV[buf][c0 * 8]);
-    }
-  };
-
-  // S^T row rho of the 32-key tile <- key 16(q'/2) + 8gg + 4(q'%2) + e', rho = 8q' + 4gg + e';
-  // then lane (n, g) reg i holds key 16(i/8) + 8g + (i%8): for PV k-step kk it owns the
-  // 8 consecutive keys 16kk + 8g .. +7, one V brick.
-  const int rq = n >> 3, rgg = (n >> 2) & 1, re = n & 3;
-  const int tokA = 16 * (rq >> 1) + 8 * rgg + 4 * (rq & 1) + re;
-  auto qk = [&](int buf, f32x16 (&sc)[2]) {
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sc[nt][i] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KSTEP; ++ks) {
-      const bf16x8 a = as_bf16x8(ld16(&sK[buf][((2 * ks + g) * BK + tokA) * 8]));
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[nt][ks], sc[nt], 0, 0, 0);
-    }
-  };
+  const int32_t nblocks = runs.total();
 
   f32x16 oacc[MD][2];
 #pragma unroll
@@ -490,117 +463,206 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[md][nt][i] = 0.f;
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  f32x16 s_a[2], s_b[2];
 
-  if (nblocks > 0) {
-    issue(0, 0);
-    if (nblocks > 1) {
-      issue(1, 1);
-      WAIT_VMCNT(2 * NLD);
-    } else {
-      WAIT_VMCNT(0);
-    }
-    __syncthreads();
-    qk(0, s_a);
-  }
+  // K/V block blk -> LDS buffer, straight from the pool pages. Keys past the
+  // segment's end read a valid key of the segment instead (finite values that
+  // the predicate masks), so no LDS slot is left stale.
+#define SEGPAGED_ISSUE(BLK)                                                                   \
+  do {                                                                                        \
+    int s_;                                                                                   \
+    int32_t kb_;                                                                              \
+    runs.at((BLK), s_, kb_);                                                                  \
+    const int buf_ = (BLK) % NBUF;                                                            \
+    const int32_t len_ = s_ ? sl1 : sl0, base_ = s_ ? sb1 : 0;                                \
+    _Pragma("unroll") for (int i = 0; i < NLD; ++i) {                                         \
+      const int c0 = 64 * (wave + 4 * i), cidx = c0 + lane;                                   \
+      const int dc = cidx / BK, t = cidx % BK;                                                \
+      const int32_t slot = base_ + min(kb_ * BK + t, len_ - 1);                               \
+      lds_dma16(kp + pages[slot >> log2P] * PD + ((int64_t)dc * P + (slot & (P - 1))) * 8,    \
+                &sK[buf_][c0 * 8]);                                                           \
+    }                                                                                         \
+    _Pragma("unroll") for (int i = 0; i < NLD; ++i) {                                         \
+      const int c0 = 64 * (wave + 4 * i), cidx = c0 + lane;                                   \
+      const int tc = cidx / D, d = cidx % D;                                                  \
+      int32_t off8 = kb_ * BK + 8 * tc;                                                       \
+      if (off8 >= len_) off8 = (len_ - 1) & ~7;                                               \
+      const int32_t slot = base_ + off8;                                                      \
+      lds_dma16(vp + pages[slot >> log2P] * PD +                                              \
+                    ((int64_t)((slot & (P - 1)) >> 3) * D + d) * 8,                           \
+                &sV[buf_][c0 * 8]);                                                           \
+    }                                                                                         \
+    if (gathered && wave == 0)                                                                \
+      lds_dma4(rpos + min(kb_ * BK + lane, len_ - 1), &sPos[buf_][0]);                        \
+  } while (0)
+
+  // S^T row rho of the 32-key tile <- key 16(q'/2) + 8gg + 4(q'%2) + e', rho = 8q' + 4gg + e';
+  // then lane (n, g) reg i holds key 16(i/8) + 8g + (i%8): for PV k-step kk it owns the
+  // 8 consecutive keys 16kk + 8g .. +7, one V brick.
+  const int rq = n >> 3, rgg = (n >> 2) & 1, re = n & 3;
+  const int tokA = 16 * (rq >> 1) + 8 * rgg + 4 * (rq & 1) + re;
+
+  f32x16 s_a[2], s_b[2];
+  // fill the ring: blocks 0 .. NBUF - 2 in flight, then block 0's scores
+#define SEGPAGED_PROLOGUE()                                                                   \
+  do {                                                                                        \
+    const int32_t pre = min(nblocks, NBUF - 1);                                               \
+    for (int32_t k = 0; k < pre; ++k) SEGPAGED_ISSUE(k);                                      \
+    if (pre >= NBUF - 1) WAIT_VMCNT((NBUF - 2) * PER_BLOCK); else WAIT_VMCNT(0);              \
+    __syncthreads();                                                                          \
+    const f32x16 zero = {};                                                                   \
+    _Pragma("unroll") for (int ks = 0; ks < KSTEP; ++ks) {                                    \
+      const bf16x8 a = as_bf16x8(ld16(&sK[0][((2 * ks + g) * BK + tokA) * 8]));               \
+      _Pragma("unroll") for (int nt = 0; nt < 2; ++nt)                                        \
+        s_a[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[nt][ks], ks ? s_a[nt] : zero, \
+                                                          0, 0, 0);                           \
+    }                                                                                         \
+  } while (0)
 
   // one block: s_cur holds the scores of block blk, s_nxt receives block blk + 1's
-  auto step = [&](int32_t blk, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
-    const int buf = blk % 3;
-    WAIT_VMCNT(0);      // block blk + 1 has landed (this wave's part)
-    __syncthreads();    // ... for every wave; and every wave is done with block blk - 1
-    if (blk + 2 < nblocks) issue(blk + 2, (blk + 2) % 3);
+#define SEGPAGED_STEP(BLK, S_CUR, S_NXT, SAFE)                                                    \
+  do {                                                                                        \
+    const int32_t blk_ = (BLK);                                                               \
+    const int buf_ = blk_ % NBUF, nbuf_ = (blk_ + 1) % NBUF;                                  \
+    /* block blk + 1 has landed for this wave; after the barrier for every wave, and every */ \
+    /* wave is done with block blk - 1, whose buffer the next issue refills */                \
+    if (blk_ + NBUF - 1 <= nblocks) WAIT_VMCNT((NBUF - 3) * PER_BLOCK); else WAIT_VMCNT(0);   \
+    __syncthreads();                                                                          \
+    if (blk_ + NBUF - 1 < nblocks) SEGPAGED_ISSUE(blk_ + NBUF - 1);                           \
+    /* predicate of block blk, when some key is not visible to every row */                   \
+    int s_;                                                                                   \
+    int32_t kb_;                                                                              \
+    runs.at(blk_, s_, kb_);                                                                   \
+    const int32_t len_ = s_ ? sl1 : sl0, pos0_ = s_ ? sp1 : sp0;                              \
+    const int32_t o0_ = kb_ * BK;                                                             \
+    bool interior_ = false;                                                                   \
+    if (pos0_ >= 0 && o0_ + BK <= len_) {                                                     \
+      const int32_t kp0 = pos0_ + o0_, kp1 = kp0 + BK - 1;                                    \
+      interior_ = kp1 <= r0;                                                                  \
+      if (kind == SEGPAGED_LOCAL) interior_ = interior_ && (kp1 < sink || kp0 > rmax - win);  \
+    }                                                                                         \
+    if (!interior_) {                                                                         \
+      /* branch-free: a key past the segment gets position INT_MAX (never visible) */         \
+      const bool local_ = kind == SEGPAGED_LOCAL;                                             \
+      _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                        \
+        const int tk = 16 * (i >> 3) + 8 * g + (i & 7);                                       \
+        const int32_t off = o0_ + tk;                                                         \
+        const int32_t gpos = sPos[buf_][tk];                                                  \
+        int32_t kpos = pos0_ >= 0 ? pos0_ + off : gpos;                                       \
+        kpos = off < len_ ? kpos : 0x7FFFFFFF;                                                \
+        _Pragma("unroll") for (int nt = 0; nt < 2; ++nt) {                                    \
+          const bool vis = (kpos <= qpos[nt]) &                                               \
+                           (!local_ | (kpos < sink) | (kpos > qpos[nt] - win));               \
+          S_CUR[nt][i] = vis ? S_CUR[nt][i] : -INFINITY;                                      \
+        }                                                                                     \
+      }                                                                                       \
+    }                                                                                         \
+    /* scores of the next block (the last step computes an unused tile); K fragments are */   \
+    /* read one k-step ahead */                                                               \
+    {                                                                                         \
+      bf16x8 kcur = as_bf16x8(ld16(&sK[nbuf_][(g * BK + tokA) * 8]));                         \
+      const f32x16 zero = {};                                                                 \
+      _Pragma("unroll") for (int ks = 0; ks < KSTEP; ++ks) {                                  \
+        bf16x8 knext = kcur;                                                                  \
+        if (ks + 1 < KSTEP)                                                                   \
+          knext = as_bf16x8(ld16(&sK[nbuf_][((2 * (ks + 1) + g) * BK + tokA) * 8]));          \
+        _Pragma("unroll") for (int nt = 0; nt < 2; ++nt)                                      \
+          S_NXT[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[nt][ks],               \
+                                                              ks ? S_NXT[nt] : zero, 0, 0, 0);\
+        kcur = knext;                                                                         \
+      }                                                                                       \
+    }                                                                                         \
+    /* online softmax of block blk in the log2 domain */                                      \
+    float mc_[2];                                                                             \
+    bool need_[2];                                                                            \
+    _Pragma("unroll") for (int nt = 0; nt < 2; ++nt) {                                        \
+      float mx = -INFINITY;                                                                   \
+      _Pragma("unroll") for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S_CUR[nt][i]);            \
+      mx = wave_max_xor(mx, 32);                                                              \
+      mc_[nt] = mx * c;                                                                       \
+      need_[nt] = mc_[nt] > m_run[nt] + (SAFE ? 8.f : 64.f);                                  \
+    }                                                                                         \
+    if (!SAFE) {                                                                              \
+      /* a row's reference max is fixed by its first block with a visible key (O = l = 0 */   \
+      /* until then); a later excess beyond 2^64 sends the tile to the rescaling path */      \
+      _Pragma("unroll") for (int nt = 0; nt < 2; ++nt) {                                      \
+        if (m_run[nt] == -INFINITY) { m_run[nt] = mc_[nt]; need_[nt] = false; }               \
+      }                                                                                       \
+      if (__builtin_amdgcn_ballot_w64(need_[0] || need_[1])) sOverflow = 1;                   \
+    } else if (__builtin_amdgcn_ballot_w64(need_[0] || need_[1])) {                           \
+      _Pragma("unroll") for (int nt = 0; nt < 2; ++nt) {                                      \
+        const float alpha = need_[nt] ? fast_exp2(m_run[nt] - mc_[nt]) : 1.f;                 \
+        if (need_[nt]) m_run[nt] = mc_[nt];                                                   \
+        l_run[nt] *= alpha;                                                                   \
+        _Pragma("unroll") for (int md = 0; md < MD; ++md) oacc[md][nt] *= alpha;              \
+      }                                                                                       \
+    }                                                                                         \
+    bf16x8 pf_[2][2];                                                                         \
+    _Pragma("unroll") for (int nt = 0; nt < 2; ++nt) {                                        \
+      const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];                           \
+      float p[16];                                                                            \
+      float ps = 0.f;                                                                         \
+      _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                        \
+        p[i] = fast_exp2(fmaf(S_CUR[nt][i], c, -m_use));                                      \
+        ps += p[i];                                                                           \
+      }                                                                                       \
+      _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                      \
+        u32x4 w;                                                                              \
+        w.x = pack_bf16x2(p[8 * kk + 0], p[8 * kk + 1]);                                      \
+        w.y = pack_bf16x2(p[8 * kk + 2], p[8 * kk + 3]);                                      \
+        w.z = pack_bf16x2(p[8 * kk + 4], p[8 * kk + 5]);                                      \
+        w.w = pack_bf16x2(p[8 * kk + 6], p[8 * kk + 7]);                                      \
+        pf_[nt][kk] = as_bf16x8(w);                                                           \
+      }                                                                                       \
+      l_run[nt] += ps;                                                                        \
+    }                                                                                         \
+    /* O^T += V^T . P^T, V fragments read one MFMA pair ahead */                              \
+    {                                                                                         \
+      bf16x8 vcur = as_bf16x8(ld16(&sV[buf_][(g * D + n) * 8]));                              \
+      _Pragma("unroll") for (int f = 0; f < 2 * MD; ++f) {                                    \
+        const int md = f >> 1, kk = f & 1;                                                    \
+        bf16x8 vnext = vcur;                                                                  \
+        if (f + 1 < 2 * MD) {                                                                 \
+          const int md2 = (f + 1) >> 1, kk2 = (f + 1) & 1;                                    \
+          vnext = as_bf16x8(ld16(&sV[buf_][((2 * kk2 + g) * D + 32 * md2 + n) * 8]));         \
+        }                                                                                     \
+        _Pragma("unroll") for (int nt = 0; nt < 2; ++nt)                                      \
+          oacc[md][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur, pf_[nt][kk],           \
+                                                                 oacc[md][nt], 0, 0, 0);      \
+        vcur = vnext;                                                                         \
+      }                                                                                       \
+    }                                                                                         \
+  } while (0)
 
-    // ---- predicate of block blk, when some key is not visible to every row
-    int s;
-    int32_t kb;
-    runs.at(blk, s, kb);
-    const int32_t len = s ? sl1 : sl0, pos0 = s ? sp1 : sp0;
-    const int32_t o0 = kb * BK;
-    bool interior = false;
-    if (pos0 >= 0 && o0 + BK <= len) {
-      const int32_t kp0 = pos0 + o0, kp1 = kp0 + BK - 1;
-      interior = kp1 <= r0;
-      if (kind == SEGPAGED_LOCAL) interior = interior && (kp1 < sink || kp0 > rmax - win);
+  if (nblocks > 0) {
+    SEGPAGED_PROLOGUE();
+    for (int32_t blk = 0; blk < nblocks; blk += 2) {
+      SEGPAGED_STEP(blk, s_a, s_b, false);
+      if (blk + 1 < nblocks) SEGPAGED_STEP(blk + 1, s_b, s_a, false);
     }
-    if (!interior) {
+    __syncthreads();
+    if (sOverflow) {  // uniform: recompute the tile with per-block rescaling
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int32_t off = o0 + 16 * (i >> 3) + 8 * g + (i & 7);
-        int32_t kpos = 0x7FFFFFFF;
-        if (off < len) kpos = pos0 >= 0 ? pos0 + off : rpos[off];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          bool vis = kpos <= qpos[nt];
-          if (kind == SEGPAGED_LOCAL) vis = vis && (kpos < sink || kpos > qpos[nt] - win);
-          if (!vis) s_cur[nt][i] = -INFINITY;
-        }
-      }
-    }
-
-    // ---- scores of the next block (the last iteration computes an unused tile)
-    qk((blk + 1) % 3, s_nxt);
-
-    // ---- online softmax of block blk in the log2 domain
-    float mc[2];
-    bool need[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[nt][i]);
-      mx = wave_max_xor(mx, 32);
-      mc[nt] = mx * c;
-      need[nt] = mc[nt] > m_run[nt] + 8.f;
-    }
-    if (__builtin_amdgcn_ballot_w64(need[0] || need[1])) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float alpha = need[nt] ? fast_exp2(m_run[nt] - mc[nt]) : 1.f;
-        if (need[nt]) m_run[nt] = mc[nt];
-        l_run[nt] *= alpha;
-#pragma unroll
-        for (int md = 0; md < MD; ++md) oacc[md][nt] *= alpha;
-      }
-    }
-    bf16x8 pf[2][2];  // [nt][kk]
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
-      float p[16];
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = fast_exp2(fmaf(s_cur[nt][i], c, -m_use));
-        ps += p[i];
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        u32x4 w;
-        w.x = pack_bf16x2(p[8 * kk + 0], p[8 * kk + 1]);
-        w.y = pack_bf16x2(p[8 * kk + 2], p[8 * kk + 3]);
-        w.z = pack_bf16x2(p[8 * kk + 4], p[8 * kk + 5]);
-        w.w = pack_bf16x2(p[8 * kk + 6], p[8 * kk + 7]);
-        pf[nt][kk] = as_bf16x8(w);
-      }
-      l_run[nt] += ps;
-    }
-    // ---- O^T += V^T . P^T
-#pragma unroll
-    for (int md = 0; md < MD; ++md)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = as_bf16x8(ld16(&sV[buf][((2 * kk + g) * D + 32 * md + n) * 8]));
+      for (int md = 0; md < MD; ++md)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
-          oacc[md][nt] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[nt][kk], oacc[md][nt], 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[md][nt][i] = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        m_run[nt] = -INFINITY;
+        l_run[nt] = 0.f;
       }
-  };
-  for (int32_t blk = 0; blk < nblocks; blk += 2) {
-    step(blk, s_a, s_b);
-    if (blk + 1 < nblocks) step(blk + 1, s_b, s_a);
+      SEGPAGED_PROLOGUE();
+      for (int32_t blk = 0; blk < nblocks; ++blk) {
+        SEGPAGED_STEP(blk, s_a, s_b, true);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) s_a[nt] = s_b[nt];
+      }
+    }
   }
+#undef SEGPAGED_STEP
+#undef SEGPAGED_PROLOGUE
+#undef SEGPAGED_ISSUE
 
   // ---- epilogue: O^T lane (n, g) reg i of dim tile md -> dim 32md + 8(i/4) + 4g + (i%4)
 #pragma unroll

@@ -317,3 +317,25 @@ def test_empty_and_degenerate_rows():
     parity(o[[0, 2]], ref, "degenerate decode")
     lse_parity(lse[[0, 2]], ref_lse, "degenerate decode")
     assert np.all(o[1] == 0) and np.all(np.isneginf(lse[1]))
+
+
+@pytest.mark.parametrize("slope", [0.05, 2.0])
+def test_prefill_growing_scores(slope):
+    """Scores that rise along the sequence. A gentle slope keeps the hot loop's
+    fixed reference max (p up to ~2^30); a steep one exceeds its 2^64 margin
+    and sends the tiles to the per-block rescaling path. Both must match."""
+    n, D = 300, 64
+    spec = W.Spec(name="growth", num_layers=1, num_q_heads=8, num_kv_heads=1, head_dim=D,
+                  page_size=16, seq_len=[n], first_query_pos=[0], kind=[W.GLOBAL], sink=[0],
+                  window=[1], seed=31)
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((n, 8, D)).astype(np.float32) * 0.1
+    k = rng.standard_normal((n, 1, D)).astype(np.float32) * 0.1
+    v = rng.standard_normal((n, 1, D)).astype(np.float32)
+    q[:, :, 0] = 16.0
+    k[:, 0, 0] = slope * np.arange(n) / 2.0
+    qb, kb, vb = (W.f32_to_bf16_bits(x) for x in (q, k, v))
+    ob, lse = _run_kv(spec, "prefill", kb, vb, qb, scale=0.125)
+    ref, ref_lse = OA.attention(spec, 0, qb, kb, vb, scale=0.125)
+    parity(OA.bf16_bits_to_f64(ob), ref, f"growing scores slope {slope}")
+    assert np.max(np.abs(lse - ref_lse) / np.maximum(1.0, np.abs(ref_lse))) <= 1e-5
