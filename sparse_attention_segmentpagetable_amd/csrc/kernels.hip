@@ -45,9 +45,13 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
 __device__ __forceinline__ void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  const f32x2 f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -300,22 +304,21 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// prefill. One workgroup (4 waves) per tile of 256 query rows = the G query
-// heads of one KV head x (256 / G) consecutive positions, so every K/V block
-// read serves all G heads. Keys stream in blocks of 32 slots straight into LDS
-// (global_load_lds_dwordx4, an 8-buffer ring, one barrier per block); the LDS tiles
-// have the page layouts. Per 32-key block, each wave (64 query rows = two
-// 32-row tiles) runs v_mfma_f32_32x32x16_bf16:
-//   S^T[32 keys][32 rows] = K . Q^T      (2 row tiles)
-//   O^T[32 dims][32 rows] += V^T . P^T   (D/32 dim tiles x 2 row tiles)
-// so every K or V fragment read from LDS feeds two MFMAs. The scores of block
-// j + 1 are issued before the softmax of block j, in one basic block, so the
-// MFMAs overlap the exponentials. Only blocks some row of the tile can see are
-// visited; blocks every row sees entirely skip the per-element predicate. Each
-// row's reference max is fixed by its first block with a visible key, so the hot
-// loop never rescales O (exp2 of scores up to 2^64 above it stays finite in fp32
-// and bf16, with unchanged relative precision); a tile whose scores outgrow that
-// margin is recomputed on a path that rescales per block.
+// prefill. One workgroup (8 waves, two per SIMD) per tile of 256 query rows =
+// the G query heads of one KV head x (256 / G) consecutive positions, so every
+// K/V block read serves all G heads. Keys stream in blocks of 32 slots straight
+// into LDS (global_load_lds_dwordx4, an 8-buffer ring, one barrier per block);
+// the LDS tiles have the page layouts. Per block, each wave (32 query rows)
+// runs v_mfma_f32_32x32x16_bf16:
+//   S^T[32 keys][32 rows] = K . Q^T
+//   O^T[32 dims][32 rows] += V^T . P^T   (D/32 dim tiles)
+// While one wave of a SIMD does its softmax the other's MFMAs run. Only blocks
+// some row of the tile can see are visited; blocks every row sees entirely skip
+// the per-element predicate. Each row's reference max is fixed by its first
+// block with a visible key, so the hot loop never rescales O (exp2 of scores up
+// to 2^64 above it stays finite in fp32 and bf16, with unchanged relative
+// precision); a tile whose scores outgrow that margin is recomputed on a path
+// that rescales per block.
 // ---------------------------------------------------------------------------
 // The key blocks a tile visits: per segment at most two runs of consecutive
 // blocks (A: sink / prefix, B: window), in four fixed scalar slots 0A, 0B, 1A,
@@ -384,7 +387,7 @@ __device__ __forceinline__ void segment_runs(int kind, int32_t pos0, int32_t len
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void prefill_kernel(
+__global__ __launch_bounds__(512) void prefill_kernel(
     const int32_t* __restrict__ tab, int32_t off_seqs, int32_t off_units, int32_t off_pages,
     int32_t off_retr, int32_t off_pre, int32_t item_b, int32_t item_e,
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, float* __restrict__ lse,
@@ -394,10 +397,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   constexpr int KCH = D / 8;           // 16 B chunks per key row
   constexpr int KSTEP = D / 16;        // k-steps of QK^T
   constexpr int MD = D / 32;           // O^T dim tiles
+  constexpr int NT = 512;              // threads per workgroup
   constexpr int TILE = KCH * BK * 8;   // elements of one K (or V) block tile
-  constexpr int NLD = TILE / 8 / 256;  // LDS-DMA instructions per lane per block, each of K and V
+  constexpr int CH = TILE / 8;         // 16 B chunks per tile
+  constexpr int NLD = (CH + NT - 1) / NT;  // LDS-DMA instructions per lane per tile
   constexpr int NBUF = 8;              // LDS ring: NBUF - 2 blocks in flight ahead of block j + 1
-  constexpr int PER_BLOCK = 2 * NLD;   // vmcnt increments per block
+  constexpr int PER_BLOCK = 2 * NLD;   // vmcnt increments per block and lane
+  static_assert(CH % 64 == 0, "tile must be whole waves of 16 B chunks");
   __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][TILE];
   __shared__ __attribute__((aligned(16))) int32_t sPos[NBUF][64];
@@ -421,24 +427,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, g = lane >> 5;
   if (tid == 0) sOverflow = 0;
-  int32_t qpos[2];
-  bool row_ok[2];
-  int64_t orow[2];
-  int hq[2];
-  bf16x8 qf[2][KSTEP];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int row = 64 * wave + 32 * nt + n;
-    const int32_t pq = row / G, j = row % G;
-    qpos[nt] = r0 + pq;
-    row_ok[nt] = pq < r1 - r0;
-    orow[nt] = (int64_t)qrow0 + (qpos[nt] - q0);
-    hq[nt] = h * G + j;
+  // this wave's 32 query rows: lane column n is row 32 * wave + n
+  const int row = 32 * wave + n;
+  const int32_t pq = row / G, jh = row % G;
+  const int32_t qpos = r0 + pq;
+  const bool row_ok = pq < r1 - r0;
+  const int64_t orow = (int64_t)qrow0 + (qpos - q0);
+  const int hq = h * G + jh;
+  bf16x8 qf[KSTEP];
+  {
     // rows past the tile read row q0 of the sequence (valid memory) and are never stored
-    const int64_t qrow = row_ok[nt] ? orow[nt] : (int64_t)qrow0;
-    const uint16_t* qp = q + (int64_t)l * q_layer_stride + (qrow * Hq + hq[nt]) * D + g * 8;
+    const int64_t qrow = row_ok ? orow : (int64_t)qrow0;
+    const uint16_t* qp = q + (int64_t)l * q_layer_stride + (qrow * Hq + hq) * D + g * 8;
 #pragma unroll
-    for (int ks = 0; ks < KSTEP; ++ks) qf[nt][ks] = as_bf16x8(ld16(qp + ks * 16));
+    for (int ks = 0; ks < KSTEP; ++ks) qf[ks] = as_bf16x8(ld16(qp + ks * 16));
   }
 
   // ---- block runs this tile visits (uniform across the workgroup)
@@ -455,14 +457,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   }
   const int32_t nblocks = runs.total();
 
-  f32x16 oacc[MD][2];
+  f32x16 oacc[MD];
 #pragma unroll
   for (int md = 0; md < MD; ++md)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[md][nt][i] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    for (int i = 0; i < 16; ++i) oacc[md][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
 
   // K/V block blk -> LDS buffer, straight from the pool pages. Keys past the
   // segment's end read a valid key of the segment instead (finite values that
@@ -475,21 +475,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     const int buf_ = (BLK) % NBUF;                                                            \
     const int32_t len_ = s_ ? sl1 : sl0, base_ = s_ ? sb1 : 0;                                \
     _Pragma("unroll") for (int i = 0; i < NLD; ++i) {                                         \
-      const int c0 = 64 * (wave + 4 * i), cidx = c0 + lane;                                   \
-      const int dc = cidx / BK, t = cidx % BK;                                                \
-      const int32_t slot = base_ + min(kb_ * BK + t, len_ - 1);                               \
-      lds_dma16(kp + pages[slot >> log2P] * PD + ((int64_t)dc * P + (slot & (P - 1))) * 8,    \
-                &sK[buf_][c0 * 8]);                                                           \
+      const int c0 = 64 * (wave + 8 * i), cidx = c0 + lane;                                   \
+      if (c0 < CH) {                                                                          \
+        const int dc = cidx / BK, t = cidx % BK;                                              \
+        const int32_t slot = base_ + min(kb_ * BK + t, len_ - 1);                             \
+        lds_dma16(kp + pages[slot >> log2P] * PD + ((int64_t)dc * P + (slot & (P - 1))) * 8,  \
+                  &sK[buf_][c0 * 8]);                                                         \
+      }                                                                                       \
     }                                                                                         \
     _Pragma("unroll") for (int i = 0; i < NLD; ++i) {                                         \
-      const int c0 = 64 * (wave + 4 * i), cidx = c0 + lane;                                   \
-      const int tc = cidx / D, d = cidx % D;                                                  \
-      int32_t off8 = kb_ * BK + 8 * tc;                                                       \
-      if (off8 >= len_) off8 = (len_ - 1) & ~7;                                               \
-      const int32_t slot = base_ + off8;                                                      \
-      lds_dma16(vp + pages[slot >> log2P] * PD +                                              \
-                    ((int64_t)((slot & (P - 1)) >> 3) * D + d) * 8,                           \
-                &sV[buf_][c0 * 8]);                                                           \
+      const int c0 = 64 * (wave + 8 * i), cidx = c0 + lane;                                   \
+      if (c0 < CH) {                                                                          \
+        const int tc = cidx / D, d = cidx % D;                                                \
+        int32_t off8 = kb_ * BK + 8 * tc;                                                     \
+        if (off8 >= len_) off8 = (len_ - 1) & ~7;                                             \
+        const int32_t slot = base_ + off8;                                                    \
+        lds_dma16(vp + pages[slot >> log2P] * PD +                                            \
+                      ((int64_t)((slot & (P - 1)) >> 3) * D + d) * 8,                         \
+                  &sV[buf_][c0 * 8]);                                                         \
+      }                                                                                       \
     }                                                                                         \
     if (gathered && wave == 0)                                                                \
       lds_dma4(rpos + min(kb_ * BK + lane, len_ - 1), &sPos[buf_][0]);                        \
@@ -501,34 +505,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   const int rq = n >> 3, rgg = (n >> 2) & 1, re = n & 3;
   const int tokA = 16 * (rq >> 1) + 8 * rgg + 4 * (rq & 1) + re;
 
-  f32x16 s_a[2], s_b[2];
-  // fill the ring: blocks 0 .. NBUF - 2 in flight, then block 0's scores
-#define SEGPAGED_PROLOGUE()                                                                   \
-  do {                                                                                        \
-    const int32_t pre = min(nblocks, NBUF - 1);                                               \
-    for (int32_t k = 0; k < pre; ++k) SEGPAGED_ISSUE(k);                                      \
-    if (pre >= NBUF - 1) WAIT_VMCNT((NBUF - 2) * PER_BLOCK); else WAIT_VMCNT(0);              \
-    __syncthreads();                                                                          \
-    const f32x16 zero = {};                                                                   \
-    _Pragma("unroll") for (int ks = 0; ks < KSTEP; ++ks) {                                    \
-      const bf16x8 a = as_bf16x8(ld16(&sK[0][((2 * ks + g) * BK + tokA) * 8]));               \
-      _Pragma("unroll") for (int nt = 0; nt < 2; ++nt)                                        \
-        s_a[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[nt][ks], ks ? s_a[nt] : zero, \
-                                                          0, 0, 0);                           \
-    }                                                                                         \
-  } while (0)
-
-  // one block: s_cur holds the scores of block blk, s_nxt receives block blk + 1's
-#define SEGPAGED_STEP(BLK, S_CUR, S_NXT, SAFE)                                                    \
+  // one block: scores, predicate, softmax, O^T += V^T . P^T
+#define SEGPAGED_STEP(BLK, SAFE)                                                              \
   do {                                                                                        \
     const int32_t blk_ = (BLK);                                                               \
-    const int buf_ = blk_ % NBUF, nbuf_ = (blk_ + 1) % NBUF;                                  \
-    /* block blk + 1 has landed for this wave; after the barrier for every wave, and every */ \
+    const int buf_ = blk_ % NBUF;                                                             \
+    /* block blk has landed for this wave; after the barrier for every wave, and every */     \
     /* wave is done with block blk - 1, whose buffer the next issue refills */                \
-    if (blk_ + NBUF - 1 <= nblocks) WAIT_VMCNT((NBUF - 3) * PER_BLOCK); else WAIT_VMCNT(0);   \
+    if (blk_ + NBUF - 2 < nblocks) WAIT_VMCNT((NBUF - 2) * PER_BLOCK); else WAIT_VMCNT(0);    \
     __syncthreads();                                                                          \
     if (blk_ + NBUF - 1 < nblocks) SEGPAGED_ISSUE(blk_ + NBUF - 1);                           \
-    /* predicate of block blk, when some key is not visible to every row */                   \
+    f32x16 sc;                                                                                \
+    {                                                                                         \
+      const f32x16 zero = {};                                                                 \
+      _Pragma("unroll") for (int ks = 0; ks < KSTEP; ++ks) {                                  \
+        const bf16x8 a = as_bf16x8(ld16(&sK[buf_][((2 * ks + g) * BK + tokA) * 8]));          \
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks ? sc : zero, 0, 0, 0);     \
+      }                                                                                       \
+    }                                                                                         \
+    /* predicate, when some key of the block is not visible to every row of the tile */       \
     int s_;                                                                                   \
     int32_t kb_;                                                                              \
     runs.at(blk_, s_, kb_);                                                                   \
@@ -549,60 +544,34 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         const int32_t gpos = sPos[buf_][tk];                                                  \
         int32_t kpos = pos0_ >= 0 ? pos0_ + off : gpos;                                       \
         kpos = off < len_ ? kpos : 0x7FFFFFFF;                                                \
-        _Pragma("unroll") for (int nt = 0; nt < 2; ++nt) {                                    \
-          const bool vis = (kpos <= qpos[nt]) &                                               \
-                           (!local_ | (kpos < sink) | (kpos > qpos[nt] - win));               \
-          S_CUR[nt][i] = vis ? S_CUR[nt][i] : -INFINITY;                                      \
-        }                                                                                     \
+        const bool vis = (kpos <= qpos) & (!local_ | (kpos < sink) | (kpos > qpos - win));    \
+        sc[i] = vis ? sc[i] : -INFINITY;                                                      \
       }                                                                                       \
     }                                                                                         \
-    /* scores of the next block (the last step computes an unused tile); K fragments are */   \
-    /* read one k-step ahead */                                                               \
-    {                                                                                         \
-      bf16x8 kcur = as_bf16x8(ld16(&sK[nbuf_][(g * BK + tokA) * 8]));                         \
-      const f32x16 zero = {};                                                                 \
-      _Pragma("unroll") for (int ks = 0; ks < KSTEP; ++ks) {                                  \
-        bf16x8 knext = kcur;                                                                  \
-        if (ks + 1 < KSTEP)                                                                   \
-          knext = as_bf16x8(ld16(&sK[nbuf_][((2 * (ks + 1) + g) * BK + tokA) * 8]));          \
-        _Pragma("unroll") for (int nt = 0; nt < 2; ++nt)                                      \
-          S_NXT[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[nt][ks],               \
-                                                              ks ? S_NXT[nt] : zero, 0, 0, 0);\
-        kcur = knext;                                                                         \
-      }                                                                                       \
-    }                                                                                         \
-    /* online softmax of block blk in the log2 domain */                                      \
-    float mc_[2];                                                                             \
-    bool need_[2];                                                                            \
-    _Pragma("unroll") for (int nt = 0; nt < 2; ++nt) {                                        \
-      float mx = -INFINITY;                                                                   \
-      _Pragma("unroll") for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S_CUR[nt][i]);            \
-      mx = wave_max_xor(mx, 32);                                                              \
-      mc_[nt] = mx * c;                                                                       \
-      need_[nt] = mc_[nt] > m_run[nt] + (SAFE ? 8.f : 64.f);                                  \
-    }                                                                                         \
+    /* online softmax in the log2 domain */                                                   \
+    float mx = -INFINITY;                                                                     \
+    _Pragma("unroll") for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[i]);                     \
+    mx = wave_max_xor(mx, 32);                                                                \
+    const float mc_ = mx * c;                                                                 \
+    bool need_ = mc_ > m_run + (SAFE ? 8.f : 64.f);                                           \
     if (!SAFE) {                                                                              \
-      /* a row's reference max is fixed by its first block with a visible key (O = l = 0 */   \
-      /* until then); a later excess beyond 2^64 sends the tile to the rescaling path */      \
-      _Pragma("unroll") for (int nt = 0; nt < 2; ++nt) {                                      \
-        if (m_run[nt] == -INFINITY) { m_run[nt] = mc_[nt]; need_[nt] = false; }               \
-      }                                                                                       \
-      if (__builtin_amdgcn_ballot_w64(need_[0] || need_[1])) sOverflow = 1;                   \
-    } else if (__builtin_amdgcn_ballot_w64(need_[0] || need_[1])) {                           \
-      _Pragma("unroll") for (int nt = 0; nt < 2; ++nt) {                                      \
-        const float alpha = need_[nt] ? fast_exp2(m_run[nt] - mc_[nt]) : 1.f;                 \
-        if (need_[nt]) m_run[nt] = mc_[nt];                                                   \
-        l_run[nt] *= alpha;                                                                   \
-        _Pragma("unroll") for (int md = 0; md < MD; ++md) oacc[md][nt] *= alpha;              \
-      }                                                                                       \
+      /* the reference max is fixed by the row's first block with a visible key (O and l */   \
+      /* are still zero); a later excess beyond 2^64 sends the tile to the rescaling path */  \
+      if (m_run == -INFINITY) { m_run = mc_; need_ = false; }                                 \
+      if (__builtin_amdgcn_ballot_w64(need_)) sOverflow = 1;                                  \
+    } else if (__builtin_amdgcn_ballot_w64(need_)) {                                          \
+      const float alpha = need_ ? fast_exp2(m_run - mc_) : 1.f;                               \
+      if (need_) m_run = mc_;                                                                 \
+      l_run *= alpha;                                                                         \
+      _Pragma("unroll") for (int md = 0; md < MD; ++md) oacc[md] *= alpha;                    \
     }                                                                                         \
-    bf16x8 pf_[2][2];                                                                         \
-    _Pragma("unroll") for (int nt = 0; nt < 2; ++nt) {                                        \
-      const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];                           \
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;                                     \
+    bf16x8 pf_[2];                                                                            \
+    {                                                                                         \
       float p[16];                                                                            \
       float ps = 0.f;                                                                         \
       _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                        \
-        p[i] = fast_exp2(fmaf(S_CUR[nt][i], c, -m_use));                                      \
+        p[i] = fast_exp2(fmaf(sc[i], c, -m_use));                                             \
         ps += p[i];                                                                           \
       }                                                                                       \
       _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                      \
@@ -611,53 +580,37 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         w.y = pack_bf16x2(p[8 * kk + 2], p[8 * kk + 3]);                                      \
         w.z = pack_bf16x2(p[8 * kk + 4], p[8 * kk + 5]);                                      \
         w.w = pack_bf16x2(p[8 * kk + 6], p[8 * kk + 7]);                                      \
-        pf_[nt][kk] = as_bf16x8(w);                                                           \
+        pf_[kk] = as_bf16x8(w);                                                               \
       }                                                                                       \
-      l_run[nt] += ps;                                                                        \
+      l_run += ps;                                                                            \
     }                                                                                         \
-    /* O^T += V^T . P^T, V fragments read one MFMA pair ahead */                              \
-    {                                                                                         \
-      bf16x8 vcur = as_bf16x8(ld16(&sV[buf_][(g * D + n) * 8]));                              \
-      _Pragma("unroll") for (int f = 0; f < 2 * MD; ++f) {                                    \
-        const int md = f >> 1, kk = f & 1;                                                    \
-        bf16x8 vnext = vcur;                                                                  \
-        if (f + 1 < 2 * MD) {                                                                 \
-          const int md2 = (f + 1) >> 1, kk2 = (f + 1) & 1;                                    \
-          vnext = as_bf16x8(ld16(&sV[buf_][((2 * kk2 + g) * D + 32 * md2 + n) * 8]));         \
-        }                                                                                     \
-        _Pragma("unroll") for (int nt = 0; nt < 2; ++nt)                                      \
-          oacc[md][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur, pf_[nt][kk],           \
-                                                                 oacc[md][nt], 0, 0, 0);      \
-        vcur = vnext;                                                                         \
+    _Pragma("unroll") for (int md = 0; md < MD; ++md)                                         \
+      _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                      \
+        const bf16x8 a = as_bf16x8(ld16(&sV[buf_][((2 * kk + g) * D + 32 * md + n) * 8]));    \
+        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf_[kk], oacc[md], 0, 0, 0);     \
       }                                                                                       \
-    }                                                                                         \
+  } while (0)
+
+  // fill the ring: blocks 0 .. NBUF - 2 in flight
+#define SEGPAGED_PROLOGUE()                                                                   \
+  do {                                                                                        \
+    const int32_t pre = min(nblocks, NBUF - 1);                                               \
+    for (int32_t k = 0; k < pre; ++k) SEGPAGED_ISSUE(k);                                      \
   } while (0)
 
   if (nblocks > 0) {
     SEGPAGED_PROLOGUE();
-    for (int32_t blk = 0; blk < nblocks; blk += 2) {
-      SEGPAGED_STEP(blk, s_a, s_b, false);
-      if (blk + 1 < nblocks) SEGPAGED_STEP(blk + 1, s_b, s_a, false);
-    }
+    for (int32_t blk = 0; blk < nblocks; ++blk) SEGPAGED_STEP(blk, false);
     __syncthreads();
     if (sOverflow) {  // uniform: recompute the tile with per-block rescaling
 #pragma unroll
       for (int md = 0; md < MD; ++md)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[md][nt][i] = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        m_run[nt] = -INFINITY;
-        l_run[nt] = 0.f;
-      }
+        for (int i = 0; i < 16; ++i) oacc[md][i] = 0.f;
+      m_run = -INFINITY;
+      l_run = 0.f;
       SEGPAGED_PROLOGUE();
-      for (int32_t blk = 0; blk < nblocks; ++blk) {
-        SEGPAGED_STEP(blk, s_a, s_b, true);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) s_a[nt] = s_b[nt];
-      }
+      for (int32_t blk = 0; blk < nblocks; ++blk) SEGPAGED_STEP(blk, true);
     }
   }
 #undef SEGPAGED_STEP
@@ -665,24 +618,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #undef SEGPAGED_ISSUE
 
   // ---- epilogue: O^T lane (n, g) reg i of dim tile md -> dim 32md + 8(i/4) + 4g + (i%4)
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const float l_tot = l_run[nt] + __shfl_xor(l_run[nt], 32, 64);
-    if (!row_ok[nt]) continue;
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* op = o + (int64_t)l * q_layer_stride + (orow[nt] * Hq + hq[nt]) * D;
+    uint16_t* op = o + (int64_t)l * q_layer_stride + (orow * Hq + hq) * D;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         u32x2 w;
-        w.x = pack_bf16x2(oacc[md][nt][4 * qd + 0] * inv, oacc[md][nt][4 * qd + 1] * inv);
-        w.y = pack_bf16x2(oacc[md][nt][4 * qd + 2] * inv, oacc[md][nt][4 * qd + 3] * inv);
+        w.x = pack_bf16x2(oacc[md][4 * qd + 0] * inv, oacc[md][4 * qd + 1] * inv);
+        w.y = pack_bf16x2(oacc[md][4 * qd + 2] * inv, oacc[md][4 * qd + 3] * inv);
         *reinterpret_cast<u32x2*>(op + 32 * md + 8 * qd + 4 * g) = w;
       }
     if (lse && g == 0)
-      lse[(int64_t)l * lse_layer_stride + orow[nt] * Hq + hq[nt]] =
-          l_tot > 0.f ? (m_run[nt] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+      lse[(int64_t)l * lse_layer_stride + orow * Hq + hq] =
+          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -793,7 +744,7 @@ SEGPAGED_API int segpaged_prefill(const segpaged_plan* pl, int32_t layer, const 
   const int64_t qstride = layer < 0 ? pl->q_rows * pl->Hq * pl->D : 0;
   const int64_t lstride = layer < 0 ? pl->q_rows * pl->Hq : 0;
   const float c = scale * kLog2e;
-  const dim3 grid((unsigned)nitems), block(256);
+  const dim3 grid((unsigned)nitems), block(512);
   auto* qq = (const uint16_t*)q;
   auto* oo = (uint16_t*)o;
   auto* kpp = (const uint16_t*)k_pool;
