@@ -339,16 +339,43 @@ struct TileRuns {
   }
 };
 
+// Wave-uniform int32 read through the scalar data cache (a read only); it waits
+// on lgkmcnt, so unlike a vector load it never forces a vmcnt wait that would
+// drain the in-flight LDS-DMA transfers.
+__device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p) {
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+  return v;
+}
+
+// LDS-DMA: each lane's 16 (or 4) bytes at gsrc land at lds_wave_base + lane * 16
+// (or * 4). Issued as inline asm so the compiler's wait-count pass does not see
+// an LDS write it cannot place in the ring and drain every transfer in flight
+// before each LDS read; the kernel waits on vmcnt for exactly the block it
+// needs, then passes a barrier. M0 carries the wave's LDS base (the kernel uses
+// M0 for nothing else).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 __device__ __forceinline__ void lds_dma16(const uint16_t* gsrc, uint16_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
-                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0,
-                                   0);
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(m0v)
+               : "memory");
 }
 __device__ __forceinline__ void lds_dma4(const int32_t* gsrc, int32_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
-                                   (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0,
-                                   0);
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gsrc), "s"(m0v)
+               : "memory");
 }
+// Workgroup barrier without the release/acquire fence of __syncthreads (which
+// would wait for every LDS-DMA in flight); the memory clobber keeps LDS reads
+// below it. Callers first wait on vmcnt for the data the barrier publishes.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // s_waitcnt with only vmcnt constrained (expcnt / lgkmcnt left at their maxima)
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((0x0F70) | ((n) & 15) | (((n) >> 4) << 14))
 
@@ -474,13 +501,20 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     runs.at((BLK), s_, kb_);                                                                  \
     const int buf_ = (BLK) % NBUF;                                                            \
     const int32_t len_ = s_ ? sl1 : sl0, base_ = s_ ? sb1 : 0;                                \
+    /* the block's slots lie in at most two pages (two only when P < BK): their ids are */    \
+    /* wave-uniform scalar loads, so no vector-memory wait drains the DMA queue */            \
+    const int32_t first_ = base_ + kb_ * BK;                                                  \
+    const int32_t pi0_ = first_ >> log2P;                                                     \
+    const int64_t pg0_ = (int64_t)scalar_load_i32(pages + pi0_) * PD;                         \
+    const int64_t pg1_ =                                                                      \
+        (P < BK && kb_ * BK + P < len_) ? (int64_t)scalar_load_i32(pages + pi0_ + 1) * PD : pg0_; \
     _Pragma("unroll") for (int i = 0; i < NLD; ++i) {                                         \
       const int c0 = 64 * (wave + 8 * i), cidx = c0 + lane;                                   \
       if (c0 < CH) {                                                                          \
         const int dc = cidx / BK, t = cidx % BK;                                              \
         const int32_t slot = base_ + min(kb_ * BK + t, len_ - 1);                             \
-        lds_dma16(kp + pages[slot >> log2P] * PD + ((int64_t)dc * P + (slot & (P - 1))) * 8,  \
-                  &sK[buf_][c0 * 8]);                                                         \
+        const int64_t pg = (slot >> log2P) == pi0_ ? pg0_ : pg1_;                             \
+        lds_dma16(kp + pg + ((int64_t)dc * P + (slot & (P - 1))) * 8, &sK[buf_][c0 * 8]);     \
       }                                                                                       \
     }                                                                                         \
     _Pragma("unroll") for (int i = 0; i < NLD; ++i) {                                         \
@@ -490,8 +524,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(
         int32_t off8 = kb_ * BK + 8 * tc;                                                     \
         if (off8 >= len_) off8 = (len_ - 1) & ~7;                                             \
         const int32_t slot = base_ + off8;                                                    \
-        lds_dma16(vp + pages[slot >> log2P] * PD +                                            \
-                      ((int64_t)((slot & (P - 1)) >> 3) * D + d) * 8,                         \
+        const int64_t pg = (slot >> log2P) == pi0_ ? pg0_ : pg1_;                             \
+        lds_dma16(vp + pg + ((int64_t)((slot & (P - 1)) >> 3) * D + d) * 8,                   \
                   &sV[buf_][c0 * 8]);                                                         \
       }                                                                                       \
     }                                                                                         \
@@ -505,24 +539,29 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const int rq = n >> 3, rgg = (n >> 2) & 1, re = n & 3;
   const int tokA = 16 * (rq >> 1) + 8 * rgg + 4 * (rq & 1) + re;
 
-  // one block: scores, predicate, softmax, O^T += V^T . P^T
-#define SEGPAGED_STEP(BLK, SAFE)                                                              \
+  // scores of the block in LDS buffer BUF
+#define SEGPAGED_QK(BUF, SC)                                                                  \
+  do {                                                                                        \
+    const f32x16 zero = {};                                                                   \
+    _Pragma("unroll") for (int ks = 0; ks < KSTEP; ++ks) {                                    \
+      const bf16x8 a = as_bf16x8(ld16(&sK[(BUF)][((2 * ks + g) * BK + tokA) * 8]));           \
+      SC = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks ? SC : zero, 0, 0, 0);       \
+    }                                                                                         \
+  } while (0)
+
+  // one block: sc holds block blk's scores (issued a step earlier); issue block
+  // blk + 1's scores into sn, then predicate, softmax and O^T += V^T . P^T of blk
+#define SEGPAGED_STEP(BLK, sc, sn, SAFE)                                                      \
   do {                                                                                        \
     const int32_t blk_ = (BLK);                                                               \
     const int buf_ = blk_ % NBUF;                                                             \
-    /* block blk has landed for this wave; after the barrier for every wave, and every */     \
-    /* wave is done with block blk - 1, whose buffer the next issue refills */                \
-    if (blk_ + NBUF - 2 < nblocks) WAIT_VMCNT((NBUF - 2) * PER_BLOCK); else WAIT_VMCNT(0);    \
-    __syncthreads();                                                                          \
+    /* block blk + 1 has landed for this wave; after the barrier for every wave, and */       \
+    /* every wave is done with block blk - 1, whose buffer the next issue refills */          \
+    if (blk_ + NBUF - 1 <= nblocks) WAIT_VMCNT((NBUF - 3) * PER_BLOCK); else WAIT_VMCNT(0);   \
+    ring_barrier();                                                                           \
     if (blk_ + NBUF - 1 < nblocks) SEGPAGED_ISSUE(blk_ + NBUF - 1);                           \
-    f32x16 sc;                                                                                \
-    {                                                                                         \
-      const f32x16 zero = {};                                                                 \
-      _Pragma("unroll") for (int ks = 0; ks < KSTEP; ++ks) {                                  \
-        const bf16x8 a = as_bf16x8(ld16(&sK[buf_][((2 * ks + g) * BK + tokA) * 8]));          \
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks ? sc : zero, 0, 0, 0);     \
-      }                                                                                       \
-    }                                                                                         \
+    /* the last step computes an unused tile from a stale buffer */                           \
+    SEGPAGED_QK((blk_ + 1) % NBUF, sn);                                                       \
     /* predicate, when some key of the block is not visible to every row of the tile */       \
     int s_;                                                                                   \
     int32_t kb_;                                                                              \
@@ -591,16 +630,24 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       }                                                                                       \
   } while (0)
 
-  // fill the ring: blocks 0 .. NBUF - 2 in flight
-#define SEGPAGED_PROLOGUE()                                                                   \
+  // fill the ring (blocks 0 .. NBUF - 2 in flight), then block 0's scores
+#define SEGPAGED_PROLOGUE(SC)                                                                 \
   do {                                                                                        \
     const int32_t pre = min(nblocks, NBUF - 1);                                               \
     for (int32_t k = 0; k < pre; ++k) SEGPAGED_ISSUE(k);                                      \
+    if (pre >= NBUF - 1) WAIT_VMCNT((NBUF - 2) * PER_BLOCK); else WAIT_VMCNT(0);              \
+    ring_barrier();                                                                           \
+    SEGPAGED_QK(0, SC);                                                                       \
   } while (0)
 
   if (nblocks > 0) {
-    SEGPAGED_PROLOGUE();
-    for (int32_t blk = 0; blk < nblocks; ++blk) SEGPAGED_STEP(blk, false);
+    f32x16 s_a, s_b;
+    SEGPAGED_PROLOGUE(s_a);
+    for (int32_t blk = 0; blk < nblocks; blk += 2) {
+      SEGPAGED_STEP(blk, s_a, s_b, false);
+      if (blk + 1 < nblocks) SEGPAGED_STEP(blk + 1, s_b, s_a, false);
+    }
+    WAIT_VMCNT(0);
     __syncthreads();
     if (sOverflow) {  // uniform: recompute the tile with per-block rescaling
 #pragma unroll
@@ -609,11 +656,15 @@ __global__ __launch_bounds__(512) void prefill_kernel(
         for (int i = 0; i < 16; ++i) oacc[md][i] = 0.f;
       m_run = -INFINITY;
       l_run = 0.f;
-      SEGPAGED_PROLOGUE();
-      for (int32_t blk = 0; blk < nblocks; ++blk) SEGPAGED_STEP(blk, true);
+      SEGPAGED_PROLOGUE(s_a);
+      for (int32_t blk = 0; blk < nblocks; ++blk) {
+        SEGPAGED_STEP(blk, s_a, s_b, true);
+        s_a = s_b;
+      }
     }
   }
 #undef SEGPAGED_STEP
+#undef SEGPAGED_QK
 #undef SEGPAGED_PROLOGUE
 #undef SEGPAGED_ISSUE
 
