@@ -50,11 +50,77 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (the FETCH/WRITE_SIZE scale reference)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs of this script into the traffic file")
     return ap.parse_args()
+
+
+KERNELS_SRC = os.path.join(ROOT, "sparse_attention_segmentpagetable_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_decode.json")
+COPY_BYTES = 1 << 30
+
+
+def kernels_hash():
+    import hashlib
+    return hashlib.sha256(open(KERNELS_SRC, "rb").read()).hexdigest()[:16]
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """HBM bytes per launch of the prefill and decode kernels from rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch), each scaled by the ratio of
+    the plain copy's known bytes to what the same counter read for it."""
+    import csv
+    import glob
+    import re
+
+    def load(d, counter):
+        per = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                nm = r["Kernel_Name"]
+                m = re.search(r"(\w+_kernel)<(\d+)>", nm)
+                key = m.group(1) if m else ("copy" if "direct_copy" in nm else None)
+                if key:
+                    per.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
+        return per
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    f_scale = COPY_BYTES / (sum(fetch["copy"]) / len(fetch["copy"]))
+    w_scale = COPY_BYTES / (sum(write["copy"]) / len(write["copy"]))
+    out = {"kernels_sha256_16": kernels_hash(), "copy_bytes": COPY_BYTES,
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "per_launch": {}}
+    for k in ("prefill_kernel", "decode_partial_kernel", "decode_combine_kernel", "build_kernel"):
+        if k in fetch and k in write:
+            fb = sum(fetch[k]) / len(fetch[k]) * f_scale
+            wb = sum(write[k]) / len(write[k]) * w_scale
+            out["per_launch"][k] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                                    "bytes": round(fb + wb), "launches": len(fetch[k])}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(out))
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter runs, or None when the
+    kernel source changed since they were taken."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernels_sha256_16") != kernels_hash():
+        return None
+    k = t.get("per_launch", {}).get(kernel)
+    return None if k is None else k["bytes"]
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(units shard by KV head with no exchange; see the design notes).", file=sys.stderr)
@@ -107,6 +173,14 @@ def main():
     dstats = dplan.stats(-1)
     decode_bytes = dstats["decode_tokens"] * 2 * D * 2  # K and V, bf16, each visible key once
     torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
     rec = {"build": [], "prefill": [], "decode": []}
@@ -215,7 +289,8 @@ def main():
             "peak": BF16_PEAK_TFS,
             "unit": "TFLOP/s",
             "frac": round(pre_tflops / BF16_PEAK_TFS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("prefill_kernel"),
+            "traffic_unit": "bytes per launch (one layer)",
         },
         "roofline_decode": {
             "kernel": "decode_partial_kernel + decode_combine_kernel",
@@ -224,7 +299,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("decode_partial_kernel"),
+            "traffic_unit": "bytes per launch (all layers)",
+            "algorithmic_bytes_per_launch": decode_bytes,
         },
     }
 
