@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (the FETCH/WRITE_SIZE scale reference)")
+                    help="also run a plain 1 GiB elementwise pass (the FETCH/WRITE_SIZE scale reference)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of this script into the traffic file")
     return ap.parse_args()
@@ -83,7 +83,7 @@ def summarize_pmc(fetch_dir, write_dir):
                     continue
                 nm = r["Kernel_Name"]
                 m = re.search(r"(\w+_kernel)<(\d+)>", nm)
-                key = m.group(1) if m else ("copy" if "direct_copy" in nm else None)
+                key = m.group(1) if m else ("copy" if "neg_kernel" in nm else None)
                 if key:
                     per.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
         return per
@@ -177,8 +177,8 @@ def main():
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
+        for _ in range(3):  # an elementwise kernel with a distinctive name: reads and writes 1 GiB
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
