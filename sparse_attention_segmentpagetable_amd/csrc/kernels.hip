@@ -151,12 +151,24 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   const int32_t it = item_b + (int32_t)blockIdx.x * 4 + wave;
   if (it >= item_e) return;
   const int32_t* item = tab + off_dec + kDecItemInts * it;
-  const int32_t u = item[0], lo = item[1], hi = item[2];
+  // slots [lo, hi) minus the gap [gap_lo, gap_hi): the zero tail of a sink page
+  // between a local head's sink segment and its window segment
+  const int32_t u = item[0], lo = item[1], hi = item[2], gap_lo = item[3];
   const int32_t* ur = tab + off_units + kUnitInts * u;
   const int32_t b = ur[U_B], l = ur[U_L], h = ur[U_H];
   const int32_t* pages = tab + off_pages + ur[U_PAGEOFF];
   const int n = lane & 15, g = lane >> 4;
   const int64_t PD = (int64_t)P * D;
+  const int32_t lo8 = lo & ~7;
+
+  const int32_t gap_hi = gap_lo > 0 ? ((gap_lo + P - 1) >> log2P) << log2P : 0;
+
+  // a window of the item's page ids, one per lane; each step reads the ids it
+  // needs with readlane into scalar registers, and the window moves on when a
+  // step would leave it
+  const int32_t pg_last = (hi - 1) >> log2P;
+  int32_t pg_first = lo8 >> log2P;
+  int32_t pid_lane = pg_first + lane <= pg_last ? pages[pg_first + lane] : 0;
 
   bf16x8 qf[KS];
   {
@@ -177,43 +189,56 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   const int r = lane & 15;
   const int koff = 8 * (r >> 2) + (r & 3);  // key of S^T row r in tile t: koff + 4t
 
-  for (int32_t s0 = lo & ~7; s0 < hi; s0 += 32) {
-    // K operand: row r of tile t <- key s0 + koff + 4t, dims (4ks + g)*8 .. +7
-    bf16x8 kf[2][KS];
+  // operand loads of the 32-key step at s0: K row r of tile t <- key s0 + koff + 4t,
+  // dims (4ks + g)*8 .. +7; V row (dim) 16dt + r <- keys s0 + 8g .. +7 (one brick)
+  u32x4 kbuf[2][2][KS], vbuf[2][DT];
+  auto load_step = [&](int32_t s0, u32x4 (&kr)[2][KS], u32x4 (&vr)[DT]) {
+    const int32_t p0 = s0 >> log2P;
+    const int32_t p2 = min((s0 + 31) >> log2P, pg_last);
+    if (p2 - pg_first >= 64) {  // uniform: move the page-id window
+      pg_first = p0;
+      pid_lane = pg_first + lane <= pg_last ? pages[pg_first + lane] : 0;
+    }
+    const int32_t pidA = __builtin_amdgcn_readlane(pid_lane, p0 - pg_first);
+    const int32_t pidB = __builtin_amdgcn_readlane(pid_lane, p2 - pg_first);
+    const int32_t pidC = __builtin_amdgcn_readlane(pid_lane, min((s0 + 16) >> log2P, pg_last) - pg_first);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int32_t key = s0 + koff + 4 * t;
       const bool ok = key < hi;
-      const int32_t pid = ok ? pages[key >> log2P] : 0;
+      const int32_t pk = key >> log2P;
+      const int32_t pid = pk == p0 ? pidA : (pk == ((s0 + 31) >> log2P) ? pidB : pidC);
       const uint16_t* base = kp + pid * PD + (int64_t)(key & (P - 1)) * 8 + (int64_t)g * P * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         u32x4 v = {0u, 0u, 0u, 0u};
         if (ok) v = ld16(base + (int64_t)ks * 4 * P * 8);
-        kf[t][ks] = as_bf16x8(v);
+        kr[t][ks] = v;
       }
     }
-    // V operand: row (dim) 16dt + r, keys s0 + 8g .. +7 (one brick)
-    bf16x8 vf[DT];
     {
       const int32_t key = s0 + 8 * g;
       const bool ok = key < hi;
-      const int32_t pid = ok ? pages[key >> log2P] : 0;
+      const int32_t pk = key >> log2P;
+      const int32_t pid = pk == p0 ? pidA : (pk == ((s0 + 31) >> log2P) ? pidB : pidC);
       const uint16_t* base = vp + pid * PD + ((int64_t)((key & (P - 1)) >> 3) * D + r) * 8;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         u32x4 v = {0u, 0u, 0u, 0u};
         if (ok) v = ld16(base + dt * 16 * 8);
-        vf[dt] = as_bf16x8(v);
+        vr[dt] = v;
       }
     }
+  };
+
+  auto compute_step = [&](int32_t s0, const u32x4 (&kr)[2][KS], const u32x4 (&vr)[DT]) {
     f32x4 st[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][ks], qf[ks], st[t], 0, 0, 0);
+        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[t][ks]), qf[ks], st[t], 0, 0, 0);
     }
     // lane (n, g) reg i of tile t holds key s0 + 8g + 4t + i
     float mx = -INFINITY;
@@ -222,7 +247,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int32_t key = s0 + 8 * g + 4 * t + i;
-        if (key < lo || key >= hi) st[t][i] = -INFINITY;
+        if (key < lo || key >= hi || (key >= gap_lo && key < gap_hi)) st[t][i] = -INFINITY;
         mx = fmaxf(mx, st[t][i]);
       }
     mx = wave_max_xor(mx, 16);
@@ -249,9 +274,31 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       acc[dt] *= alpha;
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[dt]), pf, acc[dt], 0, 0, 0);
     }
+  };
+
+  // steps of 32 slots from lo8; a step lying entirely in the gap is skipped
+  auto next_step = [&](int32_t s) {
+    s += 32;
+    while (s >= gap_lo && s + 32 <= gap_hi) s += 32;
+    return s;
+  };
+  // two-deep register pipeline: the next step's operands are in flight while a step computes
+  int32_t s0 = lo8;
+  load_step(s0, kbuf[0], vbuf[0]);
+  for (;;) {
+    const int32_t s1 = next_step(s0);
+    if (s1 < hi) load_step(s1, kbuf[1], vbuf[1]);
+    compute_step(s0, kbuf[0], vbuf[0]);
+    if (s1 >= hi) break;
+    const int32_t s2 = next_step(s1);
+    if (s2 < hi) load_step(s2, kbuf[0], vbuf[0]);
+    compute_step(s1, kbuf[1], vbuf[1]);
+    if (s2 >= hi) break;
+    s0 = s2;
   }
+
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
   if (n < G) {

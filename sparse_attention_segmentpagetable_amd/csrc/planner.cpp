@@ -255,9 +255,9 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
     for (int k = 0; k < nr; ++k) dec_tokens_all += rr[k].hi - rr[k].lo;
   }
   int64_t split = s.decode_split_tokens;
-  if (split == 0) {
-    split = 1024;
-    while (split > 64 && dec_tokens_all / split < 8192) split /= 2;
+  if (split == 0) {  // long items amortise each item's set-up; keep enough of them
+    split = 4096;
+    while (split > 64 && dec_tokens_all / split < 4096) split /= 2;
   }
   pl->split = (int32_t)split;
 
@@ -349,8 +349,21 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
         du[0] = (int32_t)(dec_items.size() / kDecItemInts);
         SlotRange rr[4];
         const int nr = decode_ranges(kind, s.sink[c], s.window[c], n, &segs[2 * u], nseg[u], P, rr);
-        for (int k = 0; k < nr; ++k) {
-          st.decode_tokens += rr[k].hi - rr[k].lo;
+        for (int k = 0; k < nr; ++k) st.decode_tokens += rr[k].hi - rr[k].lo;
+        int k0 = 0;
+        if (nr == 2 && rr[1].lo == ceil_div(rr[0].hi, P) * P && rr[0].hi < rr[1].lo &&
+            rr[0].hi - rr[0].lo <= split) {
+          // a short first range (a sink) and a range starting on the next page: one
+          // item covers both, the zero tail of the first range's last page is a gap
+          const int64_t hi0 = std::min(rr[1].lo + split, rr[1].hi);
+          dec_items.push_back((int32_t)u);
+          dec_items.push_back((int32_t)rr[0].lo);
+          dec_items.push_back((int32_t)hi0);
+          dec_items.push_back((int32_t)rr[0].hi);
+          rr[1].lo = hi0;
+          k0 = 1;
+        }
+        for (int k = k0; k < nr; ++k) {
           for (int64_t lo = rr[k].lo; lo < rr[k].hi; lo += split) {
             dec_items.push_back((int32_t)u);
             dec_items.push_back((int32_t)lo);

@@ -207,7 +207,7 @@ def test_prefill_all_layers_in_one_call():
 def test_split_count_invariance():
     spec = W.llama70b_decode(num_layers=1, seqs=2, n=5000, window=700)
     outs = []
-    for split in (64, 256, 4096):
+    for split in (64, 256, 2048):
         _, _, _, o, lse = _run_layer(spec, 0, "decode", split=split)
         outs.append((o, lse))
     for o, lse in outs[1:]:
@@ -339,3 +339,16 @@ def test_prefill_growing_scores(slope):
     ref, ref_lse = OA.attention(spec, 0, qb, kb, vb, scale=0.125)
     parity(OA.bf16_bits_to_f64(ob), ref, f"growing scores slope {slope}")
     assert np.max(np.abs(lse - ref_lse) / np.maximum(1.0, np.abs(ref_lse))) <= 1e-5
+
+
+def test_decode_long_items_small_pages():
+    """Items spanning more than 64 pages (P = 16, 4096-key items): the kernel's
+    per-lane page-id window has to move along the item."""
+    spec = W.Spec(name="longitems", num_layers=1, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                  page_size=16, seq_len=[5000, 2600], first_query_pos=[0, 0],
+                  kind=[W.GLOBAL, W.LOCAL], sink=[0, 5], window=[1, 2500], seed=41)
+    dspec = W.decode_form(spec)
+    _, _, (qb, kb, vb), o, lse = _run_layer(dspec, 0, "decode", split=4096)
+    ref, ref_lse = OA.attention(dspec, 0, qb, kb, vb)
+    parity(o, ref, "decode long items P=16")
+    lse_parity(lse, ref_lse, "decode long items P=16")

@@ -109,11 +109,12 @@ def test_decode_items_cover_visible_keys_once(spec, split):
                 pos_of_slot[slot_base + k] = int(p)
             slot_base += OL.ceil_div(len(OL.segment_positions(seg)), P) * P
         for it in range(ib, ie):
-            uu, lo, hi, _ = items[it]
+            uu, lo, hi, gap = items[it]
             assert uu == u and hi > lo
-            if split:
-                assert hi - lo <= split
-            seen += [pos_of_slot[x] for x in range(lo, hi)]
+            gap_hi = OL.ceil_div(gap, P) * P if gap else 0
+            if split:  # at most `split` keys, plus a sink of at most `split` before a gap
+                assert hi - lo - (gap_hi - gap) <= 2 * split
+            seen += [pos_of_slot[x] for x in range(lo, hi) if not gap <= x < gap_hi]
         want = [] if n == 0 else list(np.nonzero(
             OA.visibility_mask(kind, s, w, r, np.array([n - 1]), n)[0])[0])
         assert sorted(seen) == want and len(seen) == len(set(seen))
@@ -139,8 +140,9 @@ def test_split_and_workspace_sizes():
     plan = sp.Plan(spec, decode_split_tokens=64)
     z = plan.sizes
     assert z.decode_workspace_bytes == z.decode_items * spec.group * (spec.head_dim + 4) * 4
-    # global unit: 513 keys -> 9 items of <= 64; local: sink 4 (1 item) + window 64 (1 item)
-    assert z.decode_items == 9 + 3 * 2
+    # global unit: 513 keys -> 9 items of <= 64; local: sink 4 + window 64 in one item
+    # (the sink page's zero tail is a gap inside it)
+    assert z.decode_items == 9 + 3 * 1
 
 
 def _rc(spec_kwargs, **plan_kwargs):
@@ -175,6 +177,7 @@ def test_validation_errors():
     assert _rc({"free_list": np.arange(12, dtype=np.int32) + 10, "capacity_pages": 20}) == -1
     assert _rc({"free_list": np.arange(12, dtype=np.int32) + 8, "capacity_pages": 20}) == 0
     assert _rc({}, decode_split_tokens=100) == -1
+    assert _rc({}, decode_split_tokens=64 * 64) == 0
 
 
 def test_call_validation_without_gpu():
