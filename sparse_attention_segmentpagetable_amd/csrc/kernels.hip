@@ -418,6 +418,28 @@ __device__ __forceinline__ void lds_dma4(const int32_t* gsrc, int32_t* lds_wave_
                : "v"(gsrc), "s"(m0v)
                : "memory");
 }
+// The same transfer with the LDS destination as a wave-uniform byte address,
+// and a variant whose source is a wave-uniform 64-bit base in SGPRs plus a
+// per-lane 32-bit byte offset (no per-lane address arithmetic).
+__device__ __forceinline__ void lds_dma16_a(const uint16_t* gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(lds_base)
+               : "memory");
+}
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory");
+}
+// Empty asm that takes a value in registers: the value is computed before this
+// point, so the compiler cannot sink its computation below a later barrier.
+template <typename T>
+__device__ __forceinline__ void pin_sgpr(T& x) {
+  asm volatile("" : "+s"(x));
+}
+__device__ __forceinline__ void pin_vgpr(const f32x16& x) { asm volatile("" ::"v"(x)); }
 // Workgroup barrier without the release/acquire fence of __syncthreads (which
 // would wait for every LDS-DMA in flight); the memory clobber keeps LDS reads
 // below it. Callers first wait on vmcnt for the data the barrier publishes.
@@ -425,6 +447,60 @@ __device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "m
 
 // s_waitcnt with only vmcnt constrained (expcnt / lgkmcnt left at their maxima)
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((0x0F70) | ((n) & 15) | (((n) >> 4) << 14))
+// s_waitcnt vmcnt(n) lgkmcnt(0): also every LDS read and scalar load issued so far
+#define WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt((0x0070) | ((n) & 15) | (((n) >> 4) << 14))
+
+// acc + the two bf16 halves of w (v_dot2_f32_bf16 against (1, 1))
+__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
+// Nonempty block runs of a tile in visiting order: first block within its
+// segment, block count, segment.
+struct RunList {
+  int32_t k0 = 0, k1 = 0, k2 = 0, k3 = 0, n0 = 0, n1 = 0, n2 = 0, n3 = 0;
+  int32_t s0 = 0, s1 = 0, s2 = 0, s3 = 0, nr = 0;
+};
+__device__ __forceinline__ int32_t sel4(int32_t r, int32_t a, int32_t b, int32_t c, int32_t d) {
+  return r == 0 ? a : r == 1 ? b : r == 2 ? c : d;
+}
+__device__ __forceinline__ void run_push(RunList& rl, int32_t kb, int32_t cnt, int32_t seg) {
+  if (cnt <= 0) return;
+  rl.k0 = rl.nr == 0 ? kb : rl.k0;
+  rl.k1 = rl.nr == 1 ? kb : rl.k1;
+  rl.k2 = rl.nr == 2 ? kb : rl.k2;
+  rl.k3 = rl.nr == 3 ? kb : rl.k3;
+  rl.n0 = rl.nr == 0 ? cnt : rl.n0;
+  rl.n1 = rl.nr == 1 ? cnt : rl.n1;
+  rl.n2 = rl.nr == 2 ? cnt : rl.n2;
+  rl.n3 = rl.nr == 3 ? cnt : rl.n3;
+  rl.s0 = rl.nr == 0 ? seg : rl.s0;
+  rl.s1 = rl.nr == 1 ? seg : rl.s1;
+  rl.s2 = rl.nr == 2 ? seg : rl.s2;
+  rl.s3 = rl.nr == 3 ? seg : rl.s3;
+  ++rl.nr;
+}
+// A position in the run list: run index, block within the segment, blocks left
+// in the run (this one included), segment.
+struct Cursor {
+  int32_t run, kb, left, seg;
+};
+__device__ __forceinline__ Cursor cursor_start(const RunList& rl) {
+  return Cursor{0, rl.k0, rl.n0, rl.s0};
+}
+// next block; past the last block the cursor stays on it
+__device__ __forceinline__ void cursor_next(Cursor& cu, const RunList& rl) {
+  if (__builtin_expect(cu.left > 1, 1)) {
+    ++cu.kb;
+    --cu.left;
+  } else if (cu.run + 1 < rl.nr) {
+    ++cu.run;
+    cu.kb = sel4(cu.run, rl.k0, rl.k1, rl.k2, rl.k3);
+    cu.left = sel4(cu.run, rl.n0, rl.n1, rl.n2, rl.n3);
+    cu.seg = sel4(cu.run, rl.s0, rl.s1, rl.s2, rl.s3);
+  }
+}
 
 // Runs of one segment for query rows [r0, rmax]: A = blocks [0, an), B = [b0, b0 + bn).
 __device__ __forceinline__ void segment_runs(int kind, int32_t pos0, int32_t len, int32_t sink,
@@ -460,7 +536,7 @@ __device__ __forceinline__ void segment_runs(int kind, int32_t pos0, int32_t len
   }
 }
 
-template <int D>
+template <int D, bool SMALLP>
 __global__ __launch_bounds__(512) void prefill_kernel(
     const int32_t* __restrict__ tab, int32_t off_seqs, int32_t off_units, int32_t off_pages,
     int32_t off_retr, int32_t off_pre, int32_t item_b, int32_t item_e,
@@ -474,10 +550,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   constexpr int NT = 512;              // threads per workgroup
   constexpr int TILE = KCH * BK * 8;   // elements of one K (or V) block tile
   constexpr int CH = TILE / 8;         // 16 B chunks per tile
-  constexpr int NLD = (CH + NT - 1) / NT;  // LDS-DMA instructions per lane per tile
-  constexpr int NBUF = 8;              // LDS ring: NBUF - 2 blocks in flight ahead of block j + 1
-  constexpr int PER_BLOCK = 2 * NLD;   // vmcnt increments per block and lane
-  static_assert(CH % 64 == 0, "tile must be whole waves of 16 B chunks");
+  constexpr int NBUF = 8;              // LDS ring of K/V block tiles
+  constexpr int PER_BLOCK = 2;         // LDS-DMA instructions per block and lane (K and V)
+  // a wave's own blocks still in flight when a phase ends (see the phase loop)
+  constexpr int INFLIGHT = (NBUF - 4) * PER_BLOCK;
+  static_assert(CH % 64 == 0 && CH <= NT, "one 16 B chunk per lane and tile, whole waves");
+  static_assert(KSTEP == 2 * MD && KSTEP % 4 == 0, "QK and PV steps pair up in the MFMA phase");
   __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][TILE];
   __shared__ __attribute__((aligned(16))) int32_t sPos[NBUF][64];
@@ -497,8 +575,13 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const int32_t r1 = min(N, r0 + BQ), rmax = r1 - 1;
   const int64_t PD = (int64_t)P * D;
   const bool gathered = ur[U_S0POS] < 0;
+  const bool local = kind == SEGPAGED_LOCAL;
+  // page table through the constant address space: compiler-tracked scalar loads
+  typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+  const cint_ptr cpages = (cint_ptr)pages;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, g = lane >> 5;
   if (tid == 0) sOverflow = 0;
   // this wave's 32 query rows: lane column n is row 32 * wave + n
@@ -536,44 +619,60 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   for (int md = 0; md < MD; ++md)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[md][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f, neg_m = 0.f;
 
-  // K/V block blk -> LDS buffer, straight from the pool pages. Keys past the
-  // segment's end read a valid key of the segment instead (finite values that
-  // the predicate masks), so no LDS slot is left stale.
+  // Lane chunk of a block tile: K chunk (head-dim group cidx / BK, key cidx % BK),
+  // V chunk cidx (key group cidx / D, head dim cidx % D); both land at LDS chunk
+  // cidx. With P >= BK a block lies inside one page, so its source is the page's
+  // block base (scalar) plus a per-lane byte offset fixed for the whole tile.
+  const int cidx = 64 * wave + lane;
+  const bool dma_wave = 64 * wave < CH;
+  const uint32_t k_off = (uint32_t)((((cidx / BK) << log2P) + (cidx % BK)) * 16);
+  const uint32_t v_off = (uint32_t)(cidx * 16);
+  const uint32_t lds_k = lds_addr(&sK[0][0]) + 64 * 16 * wave;  // this wave's chunks
+  const uint32_t lds_v = lds_addr(&sV[0][0]) + 64 * 16 * wave;
+
+  // K/V block BLK -> LDS buffer BLK % NBUF (general form: any page size). Indexes
+  // past the last block re-read the last block (the ring's wait counts stay
+  // uniform; nothing reads those buffers). With P < BK a block spans two pages
+  // and slots past the segment's end re-read its last key.
 #define SEGPAGED_ISSUE(BLK)                                                                   \
   do {                                                                                        \
     int s_;                                                                                   \
     int32_t kb_;                                                                              \
-    runs.at((BLK), s_, kb_);                                                                  \
+    runs.at(min((BLK), nblocks - 1), s_, kb_);                                                \
     const int buf_ = (BLK) % NBUF;                                                            \
     const int32_t len_ = s_ ? sl1 : sl0, base_ = s_ ? sb1 : 0;                                \
-    /* the block's slots lie in at most two pages (two only when P < BK): their ids are */    \
-    /* wave-uniform scalar loads, so no vector-memory wait drains the DMA queue */            \
     const int32_t first_ = base_ + kb_ * BK;                                                  \
     const int32_t pi0_ = first_ >> log2P;                                                     \
     const int64_t pg0_ = (int64_t)scalar_load_i32(pages + pi0_) * PD;                         \
-    const int64_t pg1_ =                                                                      \
-        (P < BK && kb_ * BK + P < len_) ? (int64_t)scalar_load_i32(pages + pi0_ + 1) * PD : pg0_; \
-    _Pragma("unroll") for (int i = 0; i < NLD; ++i) {                                         \
-      const int c0 = 64 * (wave + 8 * i), cidx = c0 + lane;                                   \
-      if (c0 < CH) {                                                                          \
-        const int dc = cidx / BK, t = cidx % BK;                                              \
-        const int32_t slot = base_ + min(kb_ * BK + t, len_ - 1);                             \
-        const int64_t pg = (slot >> log2P) == pi0_ ? pg0_ : pg1_;                             \
-        lds_dma16(kp + pg + ((int64_t)dc * P + (slot & (P - 1))) * 8, &sK[buf_][c0 * 8]);     \
+    if (!SMALLP) {                                                                            \
+      const int32_t in_ = first_ & (P - 1);                                                   \
+      if (dma_wave) {                                                                         \
+        lds_dma16_s(kp + pg0_ + in_ * 8, k_off, lds_k + buf_ * (TILE * 2));                   \
+        lds_dma16_s(vp + pg0_ + (in_ >> 3) * (D * 8), v_off, lds_v + buf_ * (TILE * 2));      \
       }                                                                                       \
-    }                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < NLD; ++i) {                                         \
-      const int c0 = 64 * (wave + 8 * i), cidx = c0 + lane;                                   \
-      if (c0 < CH) {                                                                          \
-        const int tc = cidx / D, d = cidx % D;                                                \
-        int32_t off8 = kb_ * BK + 8 * tc;                                                     \
-        if (off8 >= len_) off8 = (len_ - 1) & ~7;                                             \
-        const int32_t slot = base_ + off8;                                                    \
-        const int64_t pg = (slot >> log2P) == pi0_ ? pg0_ : pg1_;                             \
-        lds_dma16(vp + pg + ((int64_t)((slot & (P - 1)) >> 3) * D + d) * 8,                   \
-                  &sV[buf_][c0 * 8]);                                                         \
+    } else {                                                                                  \
+      const int64_t pg1_ = kb_ * BK + P < len_                                                \
+                               ? (int64_t)scalar_load_i32(pages + pi0_ + 1) * PD              \
+                               : pg0_;                                                        \
+      if (dma_wave) {                                                                         \
+        {                                                                                     \
+          const int dc = cidx / BK, t = cidx % BK;                                            \
+          const int32_t slot = base_ + min(kb_ * BK + t, len_ - 1);                           \
+          const int64_t pg = (slot >> log2P) == pi0_ ? pg0_ : pg1_;                           \
+          lds_dma16_a(kp + pg + ((int64_t)dc * P + (slot & (P - 1))) * 8,                     \
+                      lds_k + buf_ * (TILE * 2));                                             \
+        }                                                                                     \
+        {                                                                                     \
+          const int tc = cidx / D, d = cidx % D;                                              \
+          int32_t off8 = kb_ * BK + 8 * tc;                                                   \
+          if (off8 >= len_) off8 = (len_ - 1) & ~7;                                           \
+          const int32_t slot = base_ + off8;                                                  \
+          const int64_t pg = (slot >> log2P) == pi0_ ? pg0_ : pg1_;                           \
+          lds_dma16_a(vp + pg + ((int64_t)((slot & (P - 1)) >> 3) * D + d) * 8,               \
+                      lds_v + buf_ * (TILE * 2));                                             \
+        }                                                                                     \
       }                                                                                       \
     }                                                                                         \
     if (gathered && wave == 0)                                                                \
@@ -586,133 +685,331 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const int rq = n >> 3, rgg = (n >> 2) & 1, re = n & 3;
   const int tokA = 16 * (rq >> 1) + 8 * rgg + 4 * (rq & 1) + re;
 
-  // scores of the block in LDS buffer BUF
-#define SEGPAGED_QK(BUF, SC)                                                                  \
+  // MFMA operands of a block, read from LDS into registers
+#define SEGPAGED_LOAD_K(BUF, KF)                                                              \
+  _Pragma("unroll") for (int ks = 0; ks < KSTEP; ++ks)                                        \
+      KF[ks] = as_bf16x8(ld16(&sK[(BUF)][((2 * ks + g) * BK + tokA) * 8]))
+#define SEGPAGED_LOAD_V(BUF, VF)                                                              \
+  _Pragma("unroll") for (int md = 0; md < MD; ++md)                                           \
+      _Pragma("unroll") for (int kk = 0; kk < 2; ++kk)                                        \
+          VF[2 * md + kk] = as_bf16x8(ld16(&sV[(BUF)][((2 * kk + g) * D + 32 * md + n) * 8]))
+  // S^T = K . Q^T of one block
+#define SEGPAGED_QK(KF, SC)                                                                   \
   do {                                                                                        \
-    const f32x16 zero = {};                                                                   \
-    _Pragma("unroll") for (int ks = 0; ks < KSTEP; ++ks) {                                    \
-      const bf16x8 a = as_bf16x8(ld16(&sK[(BUF)][((2 * ks + g) * BK + tokA) * 8]));           \
-      SC = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks ? SC : zero, 0, 0, 0);       \
+    const f32x16 zero_ = {};                                                                  \
+    SC = __builtin_amdgcn_mfma_f32_32x32x16_bf16(KF[0], qf[0], zero_, 0, 0, 0);               \
+    _Pragma("unroll") for (int ks = 1; ks < KSTEP; ++ks)                                      \
+        SC = __builtin_amdgcn_mfma_f32_32x32x16_bf16(KF[ks], qf[ks], SC, 0, 0, 0);            \
+  } while (0)
+  // O^T += V^T . P^T of one block
+#define SEGPAGED_PV(VF, PF)                                                                   \
+  _Pragma("unroll") for (int md = 0; md < MD; ++md)                                           \
+      _Pragma("unroll") for (int kk = 0; kk < 2; ++kk)                                        \
+          oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(VF[2 * md + kk], PF[kk], oacc[md], 0, 0, 0)
+  // k-step KS of QK^T (the dependent chain) paired with PV step KS (independent)
+#define SEGPAGED_QK_PV_STEP(KS, KF, SC, VF, PF)                                               \
+  do {                                                                                        \
+    const f32x16 zero_ = {};                                                                  \
+    SC = __builtin_amdgcn_mfma_f32_32x32x16_bf16(KF[KS], qf[KS], (KS) ? SC : zero_, 0, 0, 0); \
+    oacc[(KS) >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(VF[KS], PF[(KS) & 1],           \
+                                                              oacc[(KS) >> 1], 0, 0, 0);      \
+  } while (0)
+
+  // Predicate of a block's scores from its mask parameters: first key position
+  // POS (non-gathered), keys left in the segment REM, LDS buffer BUF (gathered
+  // positions). Lane (n, g) reg i holds key tk = 16(i/8) + 8g + (i%8) of the block;
+  // a key past the segment's end is never visible.
+#define SEGPAGED_MASK(GATH, POS, REM, BUF, SC)                                                \
+  do {                                                                                        \
+    if (!(GATH)) {                                                                            \
+      /* key e = tk - 8g of the lane's two 8-key groups is at position kb0 + e */             \
+      const int32_t kb0 = (POS) + 8 * g;                                                      \
+      const int32_t hi = min(qpos - kb0, (REM) - 8 * g - 1); /* e <= hi */                    \
+      const int32_t sk = sink - kb0;          /* e < sk: sink key */                          \
+      const int32_t wl = qpos - win - kb0;    /* e > wl: inside the window */                 \
+      if (local) {                                                                            \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                      \
+          const int e = 16 * (i >> 3) + (i & 7);                                              \
+          SC[i] = (e <= hi) & ((e < sk) | (e > wl)) ? SC[i] : -INFINITY;                      \
+        }                                                                                     \
+      } else {                                                                                \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                      \
+          const int e = 16 * (i >> 3) + (i & 7);                                              \
+          SC[i] = e <= hi ? SC[i] : -INFINITY;                                                \
+        }                                                                                     \
+      }                                                                                       \
+    } else {                                                                                  \
+      _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                        \
+        const int tk = 16 * (i >> 3) + 8 * g + (i & 7);                                       \
+        const int32_t gp_ = sPos[(BUF)][tk];                                                  \
+        const int32_t kpos = tk < (REM) ? gp_ : 0x7FFFFFFF;                                   \
+        SC[i] = kpos <= qpos ? SC[i] : -INFINITY;                                             \
+      }                                                                                       \
     }                                                                                         \
   } while (0)
 
-  // one block: sc holds block blk's scores (issued a step earlier); issue block
-  // blk + 1's scores into sn, then predicate, softmax and O^T += V^T . P^T of blk
-#define SEGPAGED_STEP(BLK, sc, sn, SAFE)                                                      \
+  // mask parameters of block BLK (general form, for the prologue and the safe path)
+#define SEGPAGED_MASK_BLOCK(BLK, SC)                                                          \
   do {                                                                                        \
-    const int32_t blk_ = (BLK);                                                               \
-    const int buf_ = blk_ % NBUF;                                                             \
-    /* block blk + 1 has landed for this wave; after the barrier for every wave, and */       \
-    /* every wave is done with block blk - 1, whose buffer the next issue refills */          \
-    if (blk_ + NBUF - 1 <= nblocks) WAIT_VMCNT((NBUF - 3) * PER_BLOCK); else WAIT_VMCNT(0);   \
-    ring_barrier();                                                                           \
-    if (blk_ + NBUF - 1 < nblocks) SEGPAGED_ISSUE(blk_ + NBUF - 1);                           \
-    /* the last step computes an unused tile from a stale buffer */                           \
-    SEGPAGED_QK((blk_ + 1) % NBUF, sn);                                                       \
-    /* predicate, when some key of the block is not visible to every row of the tile */       \
     int s_;                                                                                   \
     int32_t kb_;                                                                              \
-    runs.at(blk_, s_, kb_);                                                                   \
-    const int32_t len_ = s_ ? sl1 : sl0, pos0_ = s_ ? sp1 : sp0;                              \
-    const int32_t o0_ = kb_ * BK;                                                             \
-    bool interior_ = false;                                                                   \
-    if (pos0_ >= 0 && o0_ + BK <= len_) {                                                     \
-      const int32_t kp0 = pos0_ + o0_, kp1 = kp0 + BK - 1;                                    \
-      interior_ = kp1 <= r0;                                                                  \
-      if (kind == SEGPAGED_LOCAL) interior_ = interior_ && (kp1 < sink || kp0 > rmax - win);  \
+    runs.at((BLK), s_, kb_);                                                                  \
+    const int32_t pos0_ = s_ ? sp1 : sp0;                                                     \
+    const int32_t rem_ = (s_ ? sl1 : sl0) - kb_ * BK;                                         \
+    const int32_t pos_ = pos0_ + kb_ * BK;                                                    \
+    if (!block_interior(pos0_ < 0, pos_, rem_)) SEGPAGED_MASK(pos0_ < 0, pos_, rem_, (BLK) % NBUF, SC); \
+  } while (0)
+
+  // every row of the tile sees every key of a (non-gathered) block
+  auto block_interior = [&](bool gath, int32_t pos, int32_t rem) -> bool {
+    const int32_t last = pos + BK - 1;
+    bool in = !gath & (rem >= BK) & (last <= r0);
+    if (local) in = in & ((last < sink) | (pos > rmax - win));
+    return in;
+  };
+
+  // exp2 of the scaled scores against the reference, packed to bf16 for PV
+#define SEGPAGED_EXP(SC, PF)                                                                  \
+  do {                                                                                        \
+    float p_[16];                                                                             \
+    _Pragma("unroll") for (int i = 0; i < 16; ++i) p_[i] = fast_exp2(fmaf(SC[i], c, neg_m));  \
+    _Pragma("unroll") for (int i = 0; i < 16; ++i) l_run += p_[i];                            \
+    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                        \
+      u32x4 w_;                                                                               \
+      w_.x = pack_bf16x2(p_[8 * kk + 0], p_[8 * kk + 1]);                                     \
+      w_.y = pack_bf16x2(p_[8 * kk + 2], p_[8 * kk + 3]);                                     \
+      w_.z = pack_bf16x2(p_[8 * kk + 4], p_[8 * kk + 5]);                                     \
+      w_.w = pack_bf16x2(p_[8 * kk + 6], p_[8 * kk + 7]);                                     \
+      PF[kk] = as_bf16x8(w_);                                                                 \
     }                                                                                         \
-    if (!interior_) {                                                                         \
-      /* branch-free: a key past the segment gets position INT_MAX (never visible) */         \
-      const bool local_ = kind == SEGPAGED_LOCAL;                                             \
-      _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                        \
-        const int tk = 16 * (i >> 3) + 8 * g + (i & 7);                                       \
-        const int32_t off = o0_ + tk;                                                         \
-        const int32_t gpos = sPos[buf_][tk];                                                  \
-        int32_t kpos = pos0_ >= 0 ? pos0_ + off : gpos;                                       \
-        kpos = off < len_ ? kpos : 0x7FFFFFFF;                                                \
-        const bool vis = (kpos <= qpos) & (!local_ | (kpos < sink) | (kpos > qpos - win));    \
-        sc[i] = vis ? sc[i] : -INFINITY;                                                      \
-      }                                                                                       \
+  } while (0)
+
+  // Reference of rows that have none yet (scaled log2 units): the max of the
+  // first block with a visible key; afterwards no max is taken. Scores far above
+  // the reference show up as a row sum above 2^64 at the end of the tile.
+#define SEGPAGED_REFERENCE(SC)                                                                \
+  do {                                                                                        \
+    if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY)) {                                    \
+      float mx_ = SC[0];                                                                      \
+      _Pragma("unroll") for (int i = 1; i < 16; ++i) mx_ = fmaxf(mx_, SC[i]);                 \
+      mx_ = wave_max_xor(mx_, 32);                                                            \
+      if (m_run == -INFINITY) m_run = mx_ * c;                                                \
+      neg_m = m_run == -INFINITY ? 0.f : -m_run;                                              \
     }                                                                                         \
-    /* online softmax in the log2 domain */                                                   \
-    float mx = -INFINITY;                                                                     \
-    _Pragma("unroll") for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[i]);                     \
-    mx = wave_max_xor(mx, 32);                                                                \
-    const float mc_ = mx * c;                                                                 \
-    bool need_ = mc_ > m_run + (SAFE ? 8.f : 64.f);                                           \
-    if (!SAFE) {                                                                              \
-      /* the reference max is fixed by the row's first block with a visible key (O and l */   \
-      /* are still zero); a later excess beyond 2^64 sends the tile to the rescaling path */  \
-      if (m_run == -INFINITY) { m_run = mc_; need_ = false; }                                 \
-      if (__builtin_amdgcn_ballot_w64(need_)) sOverflow = 1;                                  \
-    } else if (__builtin_amdgcn_ballot_w64(need_)) {                                          \
+  } while (0)
+
+  // softmax with per-block rescaling (tiles that overflowed)
+#define SEGPAGED_SOFTMAX_SAFE(BLK, SC, PF)                                                    \
+  do {                                                                                        \
+    SEGPAGED_MASK_BLOCK(BLK, SC);                                                             \
+    float mx_ = SC[0];                                                                        \
+    _Pragma("unroll") for (int i = 1; i < 16; ++i) mx_ = fmaxf(mx_, SC[i]);                   \
+    mx_ = wave_max_xor(mx_, 32);                                                              \
+    const float mc_ = mx_ * c;                                                                \
+    const bool need_ = mc_ > m_run + 8.f;                                                     \
+    if (__builtin_amdgcn_ballot_w64(need_)) {                                                 \
       const float alpha = need_ ? fast_exp2(m_run - mc_) : 1.f;                               \
       if (need_) m_run = mc_;                                                                 \
       l_run *= alpha;                                                                         \
       _Pragma("unroll") for (int md = 0; md < MD; ++md) oacc[md] *= alpha;                    \
+      neg_m = m_run == -INFINITY ? 0.f : -m_run;                                              \
     }                                                                                         \
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;                                     \
-    bf16x8 pf_[2];                                                                            \
-    {                                                                                         \
-      float p[16];                                                                            \
-      float ps = 0.f;                                                                         \
-      _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                        \
-        p[i] = fast_exp2(fmaf(sc[i], c, -m_use));                                             \
-        ps += p[i];                                                                           \
-      }                                                                                       \
-      _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                      \
-        u32x4 w;                                                                              \
-        w.x = pack_bf16x2(p[8 * kk + 0], p[8 * kk + 1]);                                      \
-        w.y = pack_bf16x2(p[8 * kk + 2], p[8 * kk + 3]);                                      \
-        w.z = pack_bf16x2(p[8 * kk + 4], p[8 * kk + 5]);                                      \
-        w.w = pack_bf16x2(p[8 * kk + 6], p[8 * kk + 7]);                                      \
-        pf_[kk] = as_bf16x8(w);                                                               \
-      }                                                                                       \
-      l_run += ps;                                                                            \
-    }                                                                                         \
-    _Pragma("unroll") for (int md = 0; md < MD; ++md)                                         \
-      _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                      \
-        const bf16x8 a = as_bf16x8(ld16(&sV[buf_][((2 * kk + g) * D + 32 * md + n) * 8]));    \
-        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf_[kk], oacc[md], 0, 0, 0);     \
-      }                                                                                       \
+    SEGPAGED_EXP(SC, PF);                                                                     \
   } while (0)
 
-  // fill the ring (blocks 0 .. NBUF - 2 in flight), then block 0's scores
-#define SEGPAGED_PROLOGUE(SC)                                                                 \
+  // End of a phase: this wave's share of the block the next phase may read has
+  // landed; after the barrier, every wave's share has.
+#define SEGPAGED_PHASE_END()                                                                  \
   do {                                                                                        \
-    const int32_t pre = min(nblocks, NBUF - 1);                                               \
-    for (int32_t k = 0; k < pre; ++k) SEGPAGED_ISSUE(k);                                      \
-    if (pre >= NBUF - 1) WAIT_VMCNT((NBUF - 2) * PER_BLOCK); else WAIT_VMCNT(0);              \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    WAIT_VMCNT(INFLIGHT);                                                                     \
     ring_barrier();                                                                           \
-    SEGPAGED_QK(0, SC);                                                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
   } while (0)
 
   if (nblocks > 0) {
-    f32x16 s_a, s_b;
-    SEGPAGED_PROLOGUE(s_a);
-    for (int32_t blk = 0; blk < nblocks; blk += 2) {
-      SEGPAGED_STEP(blk, s_a, s_b, false);
-      if (blk + 1 < nblocks) SEGPAGED_STEP(blk + 1, s_b, s_a, false);
+    bf16x8 kf[KSTEP], vf[2 * MD], pf[2];
+    f32x16 s;
+
+    // Compacted list of the nonempty runs; two cursors walk it: the issue cursor
+    // (block to fetch next) and the mask cursor (block whose scores the next
+    // softmax phase predicates).
+    RunList rl;
+    run_push(rl, runs.a0, runs.n0, 0);
+    run_push(rl, runs.a1, runs.n1, 0);
+    run_push(rl, runs.a2, runs.n2, 1);
+    run_push(rl, runs.a3, runs.n3, 1);
+    auto cursor_slot = [&](const Cursor& cu) { return (cu.seg ? sb1 : 0) + cu.kb * BK; };
+
+    // ---- prologue: blocks 0 .. NBUF - 2 in flight; blocks 0 and 1 landed; block
+    // 0's scores and probabilities; operands of the first MFMA phase
+    for (int32_t k = 0; k < NBUF - 1; ++k) SEGPAGED_ISSUE(k);
+    // issue cursor: block NBUF - 1 with its page bases; page id of block NBUF prefetched
+    Cursor ic = cursor_start(rl);
+    for (int32_t k = 0; k < NBUF - 1; ++k) cursor_next(ic, rl);
+    const uint16_t* i_kb = kp;
+    const uint16_t* i_vb = vp;
+    int32_t i_pid = 0, i_rk = 0, i_rlen = 1;
+    // sources of the cursor's block (page id PID): page bases, and for gathered
+    // segments the block's first retrieval entry and the segment length
+#define SEGPAGED_BLOCK_BASES(CU, PID)                                                         \
+  do {                                                                                        \
+    const int32_t in_ = cursor_slot(CU) & (P - 1);                                            \
+    const int64_t pg_ = (int64_t)(PID) * PD;                                                  \
+    i_kb = kp + pg_ + in_ * 8;                                                                \
+    i_vb = vp + pg_ + (in_ >> 3) * (D * 8);                                                   \
+    i_rk = (CU).kb * BK;                                                                      \
+    i_rlen = (CU).seg ? sl1 : sl0;                                                            \
+  } while (0)
+    if (!SMALLP) {
+      SEGPAGED_BLOCK_BASES(ic, cpages[cursor_slot(ic) >> log2P]);
+      cursor_next(ic, rl);
+      i_pid = cpages[cursor_slot(ic) >> log2P];
     }
-    WAIT_VMCNT(0);
+    // mask cursor: block 1 after the prologue's softmax of block 0
+    Cursor mc = cursor_start(rl);
+    WAIT_VM_LGKM0((NBUF - 3) * PER_BLOCK);
+    ring_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    SEGPAGED_LOAD_K(0, kf);
+    SEGPAGED_QK(kf, s);
+    {
+      const int32_t pos0_ = mc.seg ? sp1 : sp0;
+      const int32_t rem_ = (mc.seg ? sl1 : sl0) - mc.kb * BK;
+      const int32_t pos_ = pos0_ + mc.kb * BK;
+      if (!block_interior(pos0_ < 0, pos_, rem_)) SEGPAGED_MASK(pos0_ < 0, pos_, rem_, 0, s);
+    }
+    SEGPAGED_REFERENCE(s);
+    SEGPAGED_EXP(s, pf);
+    cursor_next(mc, rl);
+    SEGPAGED_LOAD_K(1, kf);
+    SEGPAGED_LOAD_V(0, vf);
+
+    // Ping-pong: phases alternate between the two waves of each SIMD (w and
+    // w + 4): while one runs its MFMA phase the other runs its softmax phase.
+    //   MFMA phase j:    S = K(j+1) . Q^T;  O^T += V(j)^T . P(j)^T; in the MFMAs'
+    //                    shadow, issue block j + NBUF - 1 and advance both cursors
+    //   softmax phase j: P(j+1) from S; operands of K(j+2) and V(j+1)
+    // Waves 4-7 run one phase behind waves 0-3 (an idle first phase); waves 0-3
+    // idle in the last. After phase t every wave has block t/2 + 2 (so at most
+    // NBUF - 4 blocks of its own in flight).
+    const bool late = wave >= 4;
+    if (late) SEGPAGED_PHASE_END();
+    for (int32_t j = 0; j < nblocks; ++j) {
+      // ---- MFMA phase (its operands were read before the barrier; waiting for
+      // them here keeps the scalar loads below from being waited on mid-phase)
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      // the KSTEP QK/PV step pairs in four groups, scalar work between them
+#pragma unroll
+      for (int ks = 0; ks < KSTEP / 4; ++ks) SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
+      __builtin_amdgcn_sched_barrier(0);
+      const int32_t ibuf = (j + NBUF - 1) % NBUF;
+      if (!SMALLP) {
+        if (dma_wave) {
+          lds_dma16_s(i_kb, k_off, lds_k + ibuf * (TILE * 2));
+          lds_dma16_s(i_vb, v_off, lds_v + ibuf * (TILE * 2));
+        }
+        if (gathered && wave == 0) lds_dma4(rpos + min(i_rk + lane, i_rlen - 1), &sPos[ibuf][0]);
+      } else {
+        SEGPAGED_ISSUE(j + NBUF - 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = KSTEP / 4; ks < KSTEP / 2; ++ks) SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
+      __builtin_amdgcn_sched_barrier(0);
+      if (!SMALLP) {
+        SEGPAGED_BLOCK_BASES(ic, i_pid);
+        pin_sgpr(i_kb);
+        pin_sgpr(i_vb);
+        pin_sgpr(i_rk);
+        pin_sgpr(i_rlen);
+        cursor_next(ic, rl);
+        i_pid = cpages[cursor_slot(ic) >> log2P];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = KSTEP / 2; ks < 3 * KSTEP / 4; ++ks) SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
+      __builtin_amdgcn_sched_barrier(0);
+      // mask parameters of block j + 1 (the mask cursor's), then advance it; the
+      // empty asm keeps them computed here, in the MFMAs' shadow
+      const int32_t m_pos0 = mc.seg ? sp1 : sp0;
+      int32_t m_rem = (mc.seg ? sl1 : sl0) - mc.kb * BK;
+      int32_t m_pos = m_pos0 + mc.kb * BK;
+      int32_t m_flags = (m_pos0 < 0 ? 1 : 0) | (block_interior(m_pos0 < 0, m_pos, m_rem) ? 2 : 0);
+      pin_sgpr(m_rem);
+      pin_sgpr(m_pos);
+      pin_sgpr(m_flags);
+      cursor_next(mc, rl);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 3 * KSTEP / 4; ks < KSTEP; ++ks) SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
+      // every MFMA of the phase is issued before the barrier
+      pin_vgpr(s);
+#pragma unroll
+      for (int md = 0; md < MD; ++md) pin_vgpr(oacc[md]);
+      __builtin_amdgcn_s_setprio(0);
+      SEGPAGED_PHASE_END();
+      // ---- softmax phase: operand reads first, their latency under the exps
+      SEGPAGED_LOAD_K((j + 2) % NBUF, kf);
+      SEGPAGED_LOAD_V((j + 1) % NBUF, vf);
+      if (j + 1 < nblocks) {
+        if (!(m_flags & 2)) SEGPAGED_MASK(m_flags & 1, m_pos, m_rem, (j + 1) % NBUF, s);
+        SEGPAGED_REFERENCE(s);
+        SEGPAGED_EXP(s, pf);
+      }
+      SEGPAGED_PHASE_END();
+    }
+    if (!late) SEGPAGED_PHASE_END();
+    WAIT_VM_LGKM0(0);
+    {
+      // a row sum above 2^64 means scores outgrew the reference: redo with rescaling
+      const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+      if (__builtin_amdgcn_ballot_w64(!(l_tot <= 0x1p64f))) sOverflow = 1;
+    }
     __syncthreads();
-    if (sOverflow) {  // uniform: recompute the tile with per-block rescaling
+    if (sOverflow) {  // uniform
 #pragma unroll
       for (int md = 0; md < MD; ++md)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[md][i] = 0.f;
       m_run = -INFINITY;
       l_run = 0.f;
-      SEGPAGED_PROLOGUE(s_a);
-      for (int32_t blk = 0; blk < nblocks; ++blk) {
-        SEGPAGED_STEP(blk, s_a, s_b, true);
-        s_a = s_b;
+      neg_m = 0.f;
+      // one barrier per block, every wave in the same order
+      for (int32_t k = 0; k < NBUF - 1; ++k) SEGPAGED_ISSUE(k);
+      WAIT_VM_LGKM0((NBUF - 3) * PER_BLOCK);
+      ring_barrier();
+      SEGPAGED_LOAD_K(0, kf);
+      SEGPAGED_QK(kf, s);
+      for (int32_t j = 0; j < nblocks; ++j) {
+        f32x16 sn;
+        SEGPAGED_LOAD_K((j + 1) % NBUF, kf);
+        SEGPAGED_LOAD_V(j % NBUF, vf);
+        SEGPAGED_QK(kf, sn);
+        SEGPAGED_SOFTMAX_SAFE(j, s, pf);
+        SEGPAGED_PV(vf, pf);
+        s = sn;
+        // block j + 2 landed and block j's buffer free before it is refilled
+        WAIT_VM_LGKM0((NBUF - 4) * PER_BLOCK);
+        ring_barrier();
+        SEGPAGED_ISSUE(j + NBUF - 1);
       }
+      WAIT_VM_LGKM0(0);
     }
   }
-#undef SEGPAGED_STEP
+#undef SEGPAGED_PHASE_END
+#undef SEGPAGED_BLOCK_BASES
+#undef SEGPAGED_SOFTMAX_SAFE
+#undef SEGPAGED_REFERENCE
+#undef SEGPAGED_EXP
+#undef SEGPAGED_MASK_BLOCK
+#undef SEGPAGED_MASK
+#undef SEGPAGED_QK_PV_STEP
+#undef SEGPAGED_PV
 #undef SEGPAGED_QK
-#undef SEGPAGED_PROLOGUE
+#undef SEGPAGED_LOAD_V
+#undef SEGPAGED_LOAD_K
 #undef SEGPAGED_ISSUE
 
   // ---- epilogue: O^T lane (n, g) reg i of dim tile md -> dim 32md + 8(i/4) + 4g + (i%4)
@@ -847,16 +1144,19 @@ SEGPAGED_API int segpaged_prefill(const segpaged_plan* pl, int32_t layer, const 
   auto* oo = (uint16_t*)o;
   auto* kpp = (const uint16_t*)k_pool;
   auto* vpp = (const uint16_t*)v_pool;
-  if (pl->D == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, grid, block, 0, st, d_table, (int32_t)pl->off_seqs,
-                       (int32_t)pl->off_units, (int32_t)pl->off_pages, (int32_t)pl->off_retr,
-                       (int32_t)pl->off_pre, (int32_t)sp.pre_b, (int32_t)sp.pre_e, qq, oo, lse,
-                       qstride, lstride, kpp, vpp, pl->G, pl->Hq, pl->P, pl->log2P, c);
-  else
-    hipLaunchKernelGGL(prefill_kernel<64>, grid, block, 0, st, d_table, (int32_t)pl->off_seqs,
-                       (int32_t)pl->off_units, (int32_t)pl->off_pages, (int32_t)pl->off_retr,
-                       (int32_t)pl->off_pre, (int32_t)sp.pre_b, (int32_t)sp.pre_e, qq, oo, lse,
-                       qstride, lstride, kpp, vpp, pl->G, pl->Hq, pl->P, pl->log2P, c);
+#define SEGPAGED_LAUNCH_PREFILL(DD, SP)                                                         \
+  hipLaunchKernelGGL((prefill_kernel<DD, SP>), grid, block, 0, st, d_table,                     \
+                     (int32_t)pl->off_seqs, (int32_t)pl->off_units, (int32_t)pl->off_pages,     \
+                     (int32_t)pl->off_retr, (int32_t)pl->off_pre, (int32_t)sp.pre_b,            \
+                     (int32_t)sp.pre_e, qq, oo, lse, qstride, lstride, kpp, vpp, pl->G, pl->Hq,  \
+                     pl->P, pl->log2P, c)
+  const bool small_pages = pl->P < kBlockN;  // a 32-key block spans two pages
+  if (pl->D == 128) {
+    if (small_pages) SEGPAGED_LAUNCH_PREFILL(128, true); else SEGPAGED_LAUNCH_PREFILL(128, false);
+  } else {
+    if (small_pages) SEGPAGED_LAUNCH_PREFILL(64, true); else SEGPAGED_LAUNCH_PREFILL(64, false);
+  }
+#undef SEGPAGED_LAUNCH_PREFILL
   return check_launch();
 }
 
