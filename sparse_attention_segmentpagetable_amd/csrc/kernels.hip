@@ -435,9 +435,15 @@ __device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, ui
 }
 // Empty asm that takes a value in registers: the value is computed before this
 // point, so the compiler cannot sink its computation below a later barrier.
-template <typename T>
-__device__ __forceinline__ void pin_sgpr(T& x) {
+__device__ __forceinline__ void pin_sgpr(int32_t& x) {
+  x = __builtin_amdgcn_readfirstlane(x);  // uniform by construction
   asm volatile("" : "+s"(x));
+}
+__device__ __forceinline__ void pin_sgpr(const uint16_t*& p) {
+  uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+  uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)p >> 32));
+  asm volatile("" : "+s"(lo), "+s"(hi));
+  p = (const uint16_t*)(((uintptr_t)hi << 32) | lo);
 }
 __device__ __forceinline__ void pin_vgpr(const f32x16& x) { asm volatile("" ::"v"(x)); }
 // Workgroup barrier without the release/acquire fence of __syncthreads (which
@@ -462,9 +468,6 @@ struct RunList {
   int32_t k0 = 0, k1 = 0, k2 = 0, k3 = 0, n0 = 0, n1 = 0, n2 = 0, n3 = 0;
   int32_t s0 = 0, s1 = 0, s2 = 0, s3 = 0, nr = 0;
 };
-__device__ __forceinline__ int32_t sel4(int32_t r, int32_t a, int32_t b, int32_t c, int32_t d) {
-  return r == 0 ? a : r == 1 ? b : r == 2 ? c : d;
-}
 __device__ __forceinline__ void run_push(RunList& rl, int32_t kb, int32_t cnt, int32_t seg) {
   if (cnt <= 0) return;
   rl.k0 = rl.nr == 0 ? kb : rl.k0;
@@ -481,25 +484,32 @@ __device__ __forceinline__ void run_push(RunList& rl, int32_t kb, int32_t cnt, i
   rl.s3 = rl.nr == 3 ? seg : rl.s3;
   ++rl.nr;
 }
-// A position in the run list: run index, block within the segment, blocks left
-// in the run (this one included), segment.
+// A position in the run list: block within the segment, blocks left in the run
+// (this one included), segment, and the runs still ahead as a queue (a run with
+// count 0 is empty). Advancing shifts the queue: no indexing, so everything
+// stays in scalar registers.
 struct Cursor {
-  int32_t run, kb, left, seg;
+  int32_t kb, left, seg;
+  int32_t k1, n1, s1, k2, n2, s2, k3, n3, s3;
 };
 __device__ __forceinline__ Cursor cursor_start(const RunList& rl) {
-  return Cursor{0, rl.k0, rl.n0, rl.s0};
+  return Cursor{rl.k0, rl.n0, rl.s0, rl.k1, rl.n1, rl.s1,
+                rl.k2, rl.n2, rl.s2, rl.k3, rl.n3, rl.s3};
 }
-// next block; past the last block the cursor stays on it
-__device__ __forceinline__ void cursor_next(Cursor& cu, const RunList& rl) {
-  if (__builtin_expect(cu.left > 1, 1)) {
-    ++cu.kb;
-    --cu.left;
-  } else if (cu.run + 1 < rl.nr) {
-    ++cu.run;
-    cu.kb = sel4(cu.run, rl.k0, rl.k1, rl.k2, rl.k3);
-    cu.left = sel4(cu.run, rl.n0, rl.n1, rl.n2, rl.n3);
-    cu.seg = sel4(cu.run, rl.s0, rl.s1, rl.s2, rl.s3);
-  }
+// next block; past the last block the cursor stays on it (branch free)
+__device__ __forceinline__ void cursor_next(Cursor& cu) {
+  const bool more = cu.left > 1;
+  const bool sw = !more & (cu.n1 > 0);
+  cu.kb = more ? cu.kb + 1 : sw ? cu.k1 : cu.kb;
+  cu.left = more ? cu.left - 1 : sw ? cu.n1 : cu.left;
+  cu.seg = sw ? cu.s1 : cu.seg;
+  cu.k1 = sw ? cu.k2 : cu.k1;
+  cu.n1 = sw ? cu.n2 : cu.n1;
+  cu.s1 = sw ? cu.s2 : cu.s1;
+  cu.k2 = sw ? cu.k3 : cu.k2;
+  cu.n2 = sw ? cu.n3 : cu.n2;
+  cu.s2 = sw ? cu.s3 : cu.s2;
+  cu.n3 = sw ? 0 : cu.n3;
 }
 
 // Runs of one segment for query rows [r0, rmax]: A = blocks [0, an), B = [b0, b0 + bn).
@@ -574,6 +584,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const int32_t BQ = kPrefillRows / G;
   const int32_t r1 = min(N, r0 + BQ), rmax = r1 - 1;
   const int64_t PD = (int64_t)P * D;
+  const int32_t log2PD = log2P + __builtin_ctz(D);  // page elements P * D, a power of two
   const bool gathered = ur[U_S0POS] < 0;
   const bool local = kind == SEGPAGED_LOCAL;
   // page table through the constant address space: compiler-tracked scalar loads
@@ -846,7 +857,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     for (int32_t k = 0; k < NBUF - 1; ++k) SEGPAGED_ISSUE(k);
     // issue cursor: block NBUF - 1 with its page bases; page id of block NBUF prefetched
     Cursor ic = cursor_start(rl);
-    for (int32_t k = 0; k < NBUF - 1; ++k) cursor_next(ic, rl);
+    for (int32_t k = 0; k < NBUF - 1; ++k) cursor_next(ic);
     const uint16_t* i_kb = kp;
     const uint16_t* i_vb = vp;
     int32_t i_pid = 0, i_rk = 0, i_rlen = 1;
@@ -855,7 +866,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
 #define SEGPAGED_BLOCK_BASES(CU, PID)                                                         \
   do {                                                                                        \
     const int32_t in_ = cursor_slot(CU) & (P - 1);                                            \
-    const int64_t pg_ = (int64_t)(PID) * PD;                                                  \
+    const int64_t pg_ = (int64_t)(PID) << log2PD;                                             \
     i_kb = kp + pg_ + in_ * 8;                                                                \
     i_vb = vp + pg_ + (in_ >> 3) * (D * 8);                                                   \
     i_rk = (CU).kb * BK;                                                                      \
@@ -863,7 +874,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   } while (0)
     if (!SMALLP) {
       SEGPAGED_BLOCK_BASES(ic, cpages[cursor_slot(ic) >> log2P]);
-      cursor_next(ic, rl);
+      cursor_next(ic);
       i_pid = cpages[cursor_slot(ic) >> log2P];
     }
     // mask cursor: block 1 after the prologue's softmax of block 0
@@ -880,8 +891,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       if (!block_interior(pos0_ < 0, pos_, rem_)) SEGPAGED_MASK(pos0_ < 0, pos_, rem_, 0, s);
     }
     SEGPAGED_REFERENCE(s);
+    // rows without a reference yet (no visible key so far) keep the check per block
+    bool need_ref = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
     SEGPAGED_EXP(s, pf);
-    cursor_next(mc, rl);
+    cursor_next(mc);
     SEGPAGED_LOAD_K(1, kf);
     SEGPAGED_LOAD_V(0, vf);
 
@@ -900,51 +913,48 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       // them here keeps the scalar loads below from being waited on mid-phase)
       __builtin_amdgcn_s_setprio(1);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      // the KSTEP QK/PV step pairs in four groups, scalar work between them
-#pragma unroll
-      for (int ks = 0; ks < KSTEP / 4; ++ks) SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
+      SEGPAGED_QK_PV_STEP(0, kf, s, vf, pf);
       __builtin_amdgcn_sched_barrier(0);
       const int32_t ibuf = (j + NBUF - 1) % NBUF;
+      const int32_t s_rk = i_rk, s_rlen = i_rlen;  // retrieval entries of block j + NBUF - 1
       if (!SMALLP) {
-        if (dma_wave) {
+        if (CH == NT || dma_wave) {
           lds_dma16_s(i_kb, k_off, lds_k + ibuf * (TILE * 2));
           lds_dma16_s(i_vb, v_off, lds_v + ibuf * (TILE * 2));
         }
-        if (gathered && wave == 0) lds_dma4(rpos + min(i_rk + lane, i_rlen - 1), &sPos[ibuf][0]);
       } else {
         SEGPAGED_ISSUE(j + NBUF - 1);
       }
       __builtin_amdgcn_sched_barrier(0);
+      // the other step pairs, with the cursors' scalar work in the MFMAs' shadow
 #pragma unroll
-      for (int ks = KSTEP / 4; ks < KSTEP / 2; ++ks) SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 1; ks < KSTEP; ++ks) SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
       if (!SMALLP) {
         SEGPAGED_BLOCK_BASES(ic, i_pid);
-        pin_sgpr(i_kb);
-        pin_sgpr(i_vb);
-        pin_sgpr(i_rk);
-        pin_sgpr(i_rlen);
-        cursor_next(ic, rl);
+        cursor_next(ic);
         i_pid = cpages[cursor_slot(ic) >> log2P];
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = KSTEP / 2; ks < 3 * KSTEP / 4; ++ks) SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
-      __builtin_amdgcn_sched_barrier(0);
-      // mask parameters of block j + 1 (the mask cursor's), then advance it; the
-      // empty asm keeps them computed here, in the MFMAs' shadow
+      // mask parameters of block j + 1 (the mask cursor's), then advance it
       const int32_t m_pos0 = mc.seg ? sp1 : sp0;
       int32_t m_rem = (mc.seg ? sl1 : sl0) - mc.kb * BK;
       int32_t m_pos = m_pos0 + mc.kb * BK;
       int32_t m_flags = (m_pos0 < 0 ? 1 : 0) | (block_interior(m_pos0 < 0, m_pos, m_rem) ? 2 : 0);
+      cursor_next(mc);
+#pragma unroll
+      for (int i = 0; i < 2 * KSTEP - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x004, 4, 0);  // then up to four SALU
+      }
+      // computed here, not sunk below the barrier; every MFMA issued before it
+      if (!SMALLP) {
+        pin_sgpr(i_kb);
+        pin_sgpr(i_vb);
+        pin_sgpr(i_rk);
+        pin_sgpr(i_rlen);
+      }
       pin_sgpr(m_rem);
       pin_sgpr(m_pos);
       pin_sgpr(m_flags);
-      cursor_next(mc, rl);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = 3 * KSTEP / 4; ks < KSTEP; ++ks) SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
-      // every MFMA of the phase is issued before the barrier
       pin_vgpr(s);
 #pragma unroll
       for (int md = 0; md < MD; ++md) pin_vgpr(oacc[md]);
@@ -953,9 +963,15 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       // ---- softmax phase: operand reads first, their latency under the exps
       SEGPAGED_LOAD_K((j + 2) % NBUF, kf);
       SEGPAGED_LOAD_V((j + 1) % NBUF, vf);
-      if (j + 1 < nblocks) {
-        if (!(m_flags & 2)) SEGPAGED_MASK(m_flags & 1, m_pos, m_rem, (j + 1) % NBUF, s);
-        SEGPAGED_REFERENCE(s);
+      if (!SMALLP && __builtin_expect(gathered, 0) && wave == 0)
+        lds_dma4(rpos + min(s_rk + lane, s_rlen - 1), &sPos[ibuf][0]);
+      if (__builtin_expect(j + 1 < nblocks, 1)) {
+        if (__builtin_expect(!(m_flags & 2), 0))
+          SEGPAGED_MASK(m_flags & 1, m_pos, m_rem, (j + 1) % NBUF, s);
+        if (__builtin_expect(need_ref, 0)) {
+          SEGPAGED_REFERENCE(s);
+          need_ref = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+        }
         SEGPAGED_EXP(s, pf);
       }
       SEGPAGED_PHASE_END();
