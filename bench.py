@@ -82,7 +82,8 @@ def summarize_pmc(fetch_dir, write_dir):
                 if r["Counter_Name"] != counter:
                     continue
                 nm = r["Kernel_Name"]
-                m = re.search(r"(\w+_kernel)<(\d+)>", nm)
+                m = re.search(r"\b(prefill_kernel|decode_partial_kernel|decode_combine_kernel|"
+                              r"build_kernel)<\d+[,>]", nm)
                 key = m.group(1) if m else ("copy" if "neg_kernel" in nm else None)
                 if key:
                     per.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
