@@ -484,34 +484,6 @@ __device__ __forceinline__ void run_push(RunList& rl, int32_t kb, int32_t cnt, i
   rl.s3 = rl.nr == 3 ? seg : rl.s3;
   ++rl.nr;
 }
-// A position in the run list: block within the segment, blocks left in the run
-// (this one included), segment, and the runs still ahead as a queue (a run with
-// count 0 is empty). Advancing shifts the queue: no indexing, so everything
-// stays in scalar registers.
-struct Cursor {
-  int32_t kb, left, seg;
-  int32_t k1, n1, s1, k2, n2, s2, k3, n3, s3;
-};
-__device__ __forceinline__ Cursor cursor_start(const RunList& rl) {
-  return Cursor{rl.k0, rl.n0, rl.s0, rl.k1, rl.n1, rl.s1,
-                rl.k2, rl.n2, rl.s2, rl.k3, rl.n3, rl.s3};
-}
-// next block; past the last block the cursor stays on it (branch free)
-__device__ __forceinline__ void cursor_next(Cursor& cu) {
-  const bool more = cu.left > 1;
-  const bool sw = !more & (cu.n1 > 0);
-  cu.kb = more ? cu.kb + 1 : sw ? cu.k1 : cu.kb;
-  cu.left = more ? cu.left - 1 : sw ? cu.n1 : cu.left;
-  cu.seg = sw ? cu.s1 : cu.seg;
-  cu.k1 = sw ? cu.k2 : cu.k1;
-  cu.n1 = sw ? cu.n2 : cu.n1;
-  cu.s1 = sw ? cu.s2 : cu.s1;
-  cu.k2 = sw ? cu.k3 : cu.k2;
-  cu.n2 = sw ? cu.n3 : cu.n2;
-  cu.s2 = sw ? cu.s3 : cu.s2;
-  cu.n3 = sw ? 0 : cu.n3;
-}
-
 // Runs of one segment for query rows [r0, rmax]: A = blocks [0, an), B = [b0, b0 + bn).
 __device__ __forceinline__ void segment_runs(int kind, int32_t pos0, int32_t len, int32_t sink,
                                              int32_t win, int32_t r0, int32_t rmax,
@@ -565,10 +537,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   // a wave's own blocks still in flight when a phase ends (see the phase loop)
   constexpr int INFLIGHT = (NBUF - 4) * PER_BLOCK;
   static_assert(CH % 64 == 0 && CH <= NT, "one 16 B chunk per lane and tile, whole waves");
+  static_assert(BK == 32, "block index arithmetic below shifts by 5");
   static_assert(KSTEP == 2 * MD && KSTEP % 4 == 0, "QK and PV steps pair up in the MFMA phase");
   __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][TILE];
   __shared__ __attribute__((aligned(16))) int32_t sPos[NBUF][64];
+  __shared__ int32_t sRun[4][4];
   __shared__ int32_t sOverflow;
 
   const int32_t it = item_b + (int32_t)blockIdx.x;
@@ -842,61 +816,135 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     bf16x8 kf[KSTEP], vf[2 * MD], pf[2];
     f32x16 s;
 
-    // Compacted list of the nonempty runs; two cursors walk it: the issue cursor
-    // (block to fetch next) and the mask cursor (block whose scores the next
-    // softmax phase predicates).
+    // Compacted list of the nonempty runs (first block within its segment, block
+    // count, segment), kept in LDS: the cursors below read it only when a run ends.
     RunList rl;
     run_push(rl, runs.a0, runs.n0, 0);
     run_push(rl, runs.a1, runs.n1, 0);
     run_push(rl, runs.a2, runs.n2, 1);
     run_push(rl, runs.a3, runs.n3, 1);
-    auto cursor_slot = [&](const Cursor& cu) { return (cu.seg ? sb1 : 0) + cu.kb * BK; };
+    if (tid == 0) {
+      sRun[0][0] = rl.k0; sRun[0][1] = rl.n0; sRun[0][2] = rl.s0;
+      sRun[1][0] = rl.k1; sRun[1][1] = rl.n1; sRun[1][2] = rl.s1;
+      sRun[2][0] = rl.k2; sRun[2][1] = rl.n2; sRun[2][2] = rl.s2;
+      sRun[3][0] = rl.k3; sRun[3][1] = rl.n3; sRun[3][2] = rl.s3;
+    }
+    const int32_t nr = rl.nr;
+#define SEGPAGED_RUNF(R, F) __builtin_amdgcn_readfirstlane(sRun[(R)][(F)])
+
+    // Issue cursor: block to fetch next. Per block: its slot, blocks left in its
+    // run, its first retrieval entry (kb * BK) and segment length; past the last
+    // block it stays there.
+    int32_t ic_run = 0, ic_left = rl.n0, ic_slot = (rl.s0 ? sb1 : 0) + rl.k0 * BK;
+    int32_t ic_kb32 = rl.k0 * BK, ic_len = rl.s0 ? sl1 : sl0;
+#define SEGPAGED_IC_NEXT()                                                                    \
+  do {                                                                                        \
+    if (__builtin_expect(--ic_left > 0, 1)) {                                                 \
+      ic_slot += BK;                                                                          \
+      ic_kb32 += BK;                                                                          \
+    } else if (ic_run + 1 < nr) {                                                             \
+      ++ic_run;                                                                               \
+      const int32_t kb0_ = SEGPAGED_RUNF(ic_run, 0), seg_ = SEGPAGED_RUNF(ic_run, 2);         \
+      ic_left = SEGPAGED_RUNF(ic_run, 1);                                                     \
+      ic_slot = (seg_ ? sb1 : 0) + kb0_ * BK;                                                 \
+      ic_kb32 = kb0_ * BK;                                                                    \
+      ic_len = seg_ ? sl1 : sl0;                                                              \
+    } else {                                                                                  \
+      ic_left = 1;                                                                            \
+    }                                                                                         \
+  } while (0)
+
+    // Mask cursor: block whose scores the next softmax phase predicates. Its mask
+    // parameters (first key position, keys left in the segment, flags 1: gathered,
+    // 2: every row sees every key) hold for m_span more blocks; they are recomputed
+    // in closed form at run ends and where the block starts or stops being interior.
+    int32_t mk_run = 0, mk_kb = rl.k0, mk_end = rl.k0 + rl.n0, mk_seg = rl.s0;
+    int32_t m_pos = 0, m_rem = 0, m_flags = 0, m_span = 1;
+    auto blocks_lt = [](int32_t x) { return x > 0 ? (x + BK - 1) >> 5 : 0; };  // #{kb >= 0: kb*BK < x}
+#define SEGPAGED_MASK_STATE()                                                                 \
+  do {                                                                                        \
+    const int32_t pos0_ = mk_seg ? sp1 : sp0, len_ = mk_seg ? sl1 : sl0;                      \
+    m_pos = pos0_ + mk_kb * BK;                                                               \
+    m_rem = len_ - mk_kb * BK;                                                                \
+    if (pos0_ < 0) {                                                                          \
+      m_flags = 1;                                                                            \
+      m_span = mk_end - mk_kb;                                                                \
+    } else {                                                                                  \
+      /* interior blocks of the segment: kb in [0, a1) or [u, a) */                           \
+      const int32_t a_ = min(blocks_lt(len_ - BK + 1), blocks_lt(r0 - pos0_ - BK + 2));       \
+      int32_t a1_ = a_, u_ = a_;                                                              \
+      if (local) {                                                                            \
+        a1_ = min(a_, blocks_lt(sink - pos0_ - BK + 1));                                      \
+        u_ = max(a1_, ((rmax - win - pos0_) >> 5) + 1);                                       \
+      }                                                                                       \
+      int32_t nxt_;                                                                           \
+      if (mk_kb < a1_) { m_flags = 2; nxt_ = a1_; }                                           \
+      else if (mk_kb < u_) { m_flags = 0; nxt_ = u_; }                                        \
+      else if (mk_kb < a_) { m_flags = 2; nxt_ = a_; }                                        \
+      else { m_flags = 0; nxt_ = mk_end; }                                                    \
+      m_span = min(nxt_, mk_end) - mk_kb;                                                     \
+    }                                                                                         \
+  } while (0)
+#define SEGPAGED_MC_NEXT()                                                                    \
+  do {                                                                                        \
+    m_pos += BK;                                                                              \
+    m_rem -= BK;                                                                              \
+    ++mk_kb;                                                                                  \
+    if (__builtin_expect(--m_span == 0, 0)) {                                                 \
+      if (mk_kb >= mk_end) {                                                                  \
+        if (mk_run + 1 < nr) {                                                                \
+          ++mk_run;                                                                           \
+          mk_kb = SEGPAGED_RUNF(mk_run, 0);                                                   \
+          mk_end = mk_kb + SEGPAGED_RUNF(mk_run, 1);                                          \
+          mk_seg = SEGPAGED_RUNF(mk_run, 2);                                                  \
+        } else {                                                                              \
+          mk_kb = mk_end - 1; /* past the last block: stay on it */                           \
+        }                                                                                     \
+      }                                                                                       \
+      SEGPAGED_MASK_STATE();                                                                  \
+    }                                                                                         \
+  } while (0)
 
     // ---- prologue: blocks 0 .. NBUF - 2 in flight; blocks 0 and 1 landed; block
     // 0's scores and probabilities; operands of the first MFMA phase
     for (int32_t k = 0; k < NBUF - 1; ++k) SEGPAGED_ISSUE(k);
-    // issue cursor: block NBUF - 1 with its page bases; page id of block NBUF prefetched
-    Cursor ic = cursor_start(rl);
-    for (int32_t k = 0; k < NBUF - 1; ++k) cursor_next(ic);
-    const uint16_t* i_kb = kp;
-    const uint16_t* i_vb = vp;
-    int32_t i_pid = 0, i_rk = 0, i_rlen = 1;
-    // sources of the cursor's block (page id PID): page bases, and for gathered
-    // segments the block's first retrieval entry and the segment length
-#define SEGPAGED_BLOCK_BASES(CU, PID)                                                         \
+    // issue sources of block NBUF - 1 (page base, byte offset within the page,
+    // retrieval entries); the cursor then stays one block ahead, its page id
+    // prefetched a phase before use
+    const char* i_kbase = (const char*)kp;
+    const char* i_vbase = (const char*)vp;
+    int32_t i_in = 0, i_rk = 0, i_rlen = 1, ic_pid = 0;
+    const int log2PDB = log2PD + 1;  // bytes per page, log2
+#define SEGPAGED_BLOCK_SOURCES(PID)                                                           \
   do {                                                                                        \
-    const int32_t in_ = cursor_slot(CU) & (P - 1);                                            \
-    const int64_t pg_ = (int64_t)(PID) << log2PD;                                             \
-    i_kb = kp + pg_ + in_ * 8;                                                                \
-    i_vb = vp + pg_ + (in_ >> 3) * (D * 8);                                                   \
-    i_rk = (CU).kb * BK;                                                                      \
-    i_rlen = (CU).seg ? sl1 : sl0;                                                            \
+    const uint64_t pg_ = (uint64_t)(uint32_t)(PID) << log2PDB;                                \
+    i_kbase = (const char*)kp + pg_;                                                          \
+    i_vbase = (const char*)vp + pg_;                                                          \
+    i_in = ic_slot & (P - 1);                                                                 \
+    i_rk = ic_kb32;                                                                           \
+    i_rlen = ic_len;                                                                          \
   } while (0)
     if (!SMALLP) {
-      SEGPAGED_BLOCK_BASES(ic, cpages[cursor_slot(ic) >> log2P]);
-      cursor_next(ic);
-      i_pid = cpages[cursor_slot(ic) >> log2P];
+      for (int32_t k = 0; k < NBUF - 1; ++k) SEGPAGED_IC_NEXT();
+      SEGPAGED_BLOCK_SOURCES(cpages[ic_slot >> log2P]);
+      SEGPAGED_IC_NEXT();
+      ic_pid = cpages[ic_slot >> log2P];
     }
-    // mask cursor: block 1 after the prologue's softmax of block 0
-    Cursor mc = cursor_start(rl);
+    SEGPAGED_MASK_STATE();
     WAIT_VM_LGKM0((NBUF - 3) * PER_BLOCK);
     ring_barrier();
     __builtin_amdgcn_sched_barrier(0);
     SEGPAGED_LOAD_K(0, kf);
     SEGPAGED_QK(kf, s);
-    {
-      const int32_t pos0_ = mc.seg ? sp1 : sp0;
-      const int32_t rem_ = (mc.seg ? sl1 : sl0) - mc.kb * BK;
-      const int32_t pos_ = pos0_ + mc.kb * BK;
-      if (!block_interior(pos0_ < 0, pos_, rem_)) SEGPAGED_MASK(pos0_ < 0, pos_, rem_, 0, s);
-    }
+    if (!(m_flags & 2)) SEGPAGED_MASK(m_flags & 1, m_pos, m_rem, 0, s);
     SEGPAGED_REFERENCE(s);
     // rows without a reference yet (no visible key so far) keep the check per block
     bool need_ref = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
     SEGPAGED_EXP(s, pf);
-    cursor_next(mc);
+    SEGPAGED_MC_NEXT();
     SEGPAGED_LOAD_K(1, kf);
     SEGPAGED_LOAD_V(0, vf);
+    uint32_t i_lds = lds_k + (NBUF - 1) * (TILE * 2);  // LDS destination of the next issue
 
     // Ping-pong: phases alternate between the two waves of each SIMD (w and
     // w + 4): while one runs its MFMA phase the other runs its softmax phase.
@@ -919,42 +967,34 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       const int32_t s_rk = i_rk, s_rlen = i_rlen;  // retrieval entries of block j + NBUF - 1
       if (!SMALLP) {
         if (CH == NT || dma_wave) {
-          lds_dma16_s(i_kb, k_off, lds_k + ibuf * (TILE * 2));
-          lds_dma16_s(i_vb, v_off, lds_v + ibuf * (TILE * 2));
+          lds_dma16_s(i_kbase, k_off + i_in * 16, i_lds);
+          lds_dma16_s(i_vbase, v_off + (i_in >> 3) * (D * 16), i_lds + (lds_v - lds_k));
         }
+        i_lds = i_lds == lds_k + (NBUF - 1) * (TILE * 2) ? lds_k : i_lds + TILE * 2;
       } else {
         SEGPAGED_ISSUE(j + NBUF - 1);
       }
       __builtin_amdgcn_sched_barrier(0);
       // the other step pairs, with the cursors' scalar work in the MFMAs' shadow
 #pragma unroll
-      for (int ks = 1; ks < KSTEP; ++ks) SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
+      for (int ks = 1; ks < KSTEP / 2; ++ks) SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
+      __builtin_amdgcn_sched_barrier(0);
       if (!SMALLP) {
-        SEGPAGED_BLOCK_BASES(ic, i_pid);
-        cursor_next(ic);
-        i_pid = cpages[cursor_slot(ic) >> log2P];
+        SEGPAGED_BLOCK_SOURCES(ic_pid);
+        SEGPAGED_IC_NEXT();
+        ic_pid = cpages[ic_slot >> log2P];
       }
-      // mask parameters of block j + 1 (the mask cursor's), then advance it
-      const int32_t m_pos0 = mc.seg ? sp1 : sp0;
-      int32_t m_rem = (mc.seg ? sl1 : sl0) - mc.kb * BK;
-      int32_t m_pos = m_pos0 + mc.kb * BK;
-      int32_t m_flags = (m_pos0 < 0 ? 1 : 0) | (block_interior(m_pos0 < 0, m_pos, m_rem) ? 2 : 0);
-      cursor_next(mc);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 2 * KSTEP - 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x004, 4, 0);  // then up to four SALU
-      }
+      for (int ks = KSTEP / 2; ks < 3 * KSTEP / 4; ++ks) SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
+      __builtin_amdgcn_sched_barrier(0);
+      // mask parameters of block j + 1 for the softmax phase, then block j + 2's
+      const int32_t c_pos = m_pos, c_rem = m_rem, c_flags = m_flags;
+      SEGPAGED_MC_NEXT();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 3 * KSTEP / 4; ks < KSTEP; ++ks) SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
       // computed here, not sunk below the barrier; every MFMA issued before it
-      if (!SMALLP) {
-        pin_sgpr(i_kb);
-        pin_sgpr(i_vb);
-        pin_sgpr(i_rk);
-        pin_sgpr(i_rlen);
-      }
-      pin_sgpr(m_rem);
-      pin_sgpr(m_pos);
-      pin_sgpr(m_flags);
       pin_vgpr(s);
 #pragma unroll
       for (int md = 0; md < MD; ++md) pin_vgpr(oacc[md]);
@@ -966,8 +1006,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       if (!SMALLP && __builtin_expect(gathered, 0) && wave == 0)
         lds_dma4(rpos + min(s_rk + lane, s_rlen - 1), &sPos[ibuf][0]);
       if (__builtin_expect(j + 1 < nblocks, 1)) {
-        if (__builtin_expect(!(m_flags & 2), 0))
-          SEGPAGED_MASK(m_flags & 1, m_pos, m_rem, (j + 1) % NBUF, s);
+        if (__builtin_expect(!(c_flags & 2), 0))
+          SEGPAGED_MASK(c_flags & 1, c_pos, c_rem, (j + 1) % NBUF, s);
         if (__builtin_expect(need_ref, 0)) {
           SEGPAGED_REFERENCE(s);
           need_ref = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
@@ -1015,7 +1055,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     }
   }
 #undef SEGPAGED_PHASE_END
-#undef SEGPAGED_BLOCK_BASES
+#undef SEGPAGED_BLOCK_SOURCES
+#undef SEGPAGED_MC_NEXT
+#undef SEGPAGED_MASK_STATE
+#undef SEGPAGED_IC_NEXT
+#undef SEGPAGED_RUNF
 #undef SEGPAGED_SOFTMAX_SAFE
 #undef SEGPAGED_REFERENCE
 #undef SEGPAGED_EXP
