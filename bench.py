@@ -49,6 +49,8 @@ def parse():
                     help="distinct Q and dense K/V tensors the prefill layers cycle through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the mixed-length decode and Mistral-layer figures")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB elementwise pass (the FETCH/WRITE_SIZE scale reference)")
@@ -314,7 +316,106 @@ def main():
             out["dense_mask"] = {"error": f"{type(e).__name__}: {e}"[:300]}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(torch, W, pspec, qs[0], ks[0], vs[0], args, log)
+    if not args.no_extra:
+        del pb, db, qs, ks, vs, o_pre, lse_pre, q_dec, o_dec, lse_dec
+        torch.cuda.empty_cache()
+        out.update(extra_configs(torch, W, sp, dev, stream, log))
     print(json.dumps(out), flush=True)
+
+
+def extra_configs(torch, W, sp, dev, stream, log):
+    """The other configurations of the scope table, timed outside the step (not part
+    of `value`): the mixed-length decode with retrieval heads (32 sequences of 2K-128K
+    tokens, 48 layers, one all-layer call; working set far beyond the caches) and the
+    Mistral-7B-shaped layer (4 x 8K prefill and one decode step; the decode working
+    set of 31 MB is cache-resident, so its GB/s is context, not an HBM figure)."""
+    res = {}
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        pairs = []
+        for _ in range(reps):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in pairs]
+        return float(np.median(ms)), float(np.min(ms))
+
+    # mixed-length decode
+    spec = W.mixed_varlen_decode()
+    plan = sp.Plan(spec)
+    bufs = plan.allocate(dev)
+    L, Hq, Hkv, D = spec.num_layers, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    T = spec.total_tokens
+    for l in range(L):
+        kd = W.randn_bf16_device((T, Hkv, D), spec.seed, W.TAG_K, l, dev)
+        vd = W.randn_bf16_device((T, Hkv, D), spec.seed, W.TAG_V, l, dev)
+        sp.build(plan, l, kd, vd, bufs["table"], bufs["k_pool"], bufs["v_pool"])
+        del kd, vd
+    q = W.randn_bf16_device((L, spec.num_seqs, Hq, D), spec.seed, W.TAG_Q, 0, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((L, spec.num_seqs, Hq), dtype=torch.float32, device=dev)
+    st = plan.stats(-1)
+    kv_bytes = st["decode_tokens"] * 2 * D * 2
+    med, mn = timed(lambda: sp.decode(plan, -1, q, bufs["table"], bufs["k_pool"], bufs["v_pool"],
+                                      1.0 / math.sqrt(D), o, lse, workspace=bufs["workspace"]), 10)
+    gbs = kv_bytes / (med * 1e-3) / 1e9
+    res["decode_mixed"] = {
+        "workload": (f"{spec.num_seqs} sequences of {min(spec.seq_len)}-{max(spec.seq_len)} tokens, "
+                     f"{L} layers x {Hkv} KV heads (12% global, 8% retrieval with 5% index sets, "
+                     f"local sink 4 window 4096), one all-layer decode call"),
+        "value": round(gbs, 1), "unit": "GB/s", "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "ms_median": round(med, 4), "ms_min": round(mn, 4), "kv_bytes": kv_bytes,
+        "decode_items": plan.sizes.decode_items,
+    }
+    log(f"mixed decode: {med:.3f} ms, {gbs:.0f} GB/s")
+    del plan, bufs, q, o, lse
+    torch.cuda.empty_cache()
+
+    # Mistral-7B-shaped layer
+    spec = W.mistral_layer("prefill")
+    plan = sp.Plan(spec)
+    bufs = plan.allocate(dev, workspace=False)
+    Hq, Hkv, D = spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    T = spec.total_tokens
+    k = W.randn_bf16_device((T, Hkv, D), spec.seed, W.TAG_K, 0, dev)
+    v = W.randn_bf16_device((T, Hkv, D), spec.seed, W.TAG_V, 0, dev)
+    q = W.randn_bf16_device((T, Hq, D), spec.seed, W.TAG_Q, 0, dev)
+    o = torch.empty_like(q)
+    sp.build(plan, 0, k, v, bufs["table"], bufs["k_pool"], bufs["v_pool"])
+    flops = 4 * D * spec.group * plan.stats(0)["prefill_pairs"]
+    pmed, pmn = timed(lambda: sp.prefill(plan, 0, q, bufs["table"], bufs["k_pool"], bufs["v_pool"],
+                                         1.0 / math.sqrt(D), o), 20)
+    bmed, _ = timed(lambda: sp.build(plan, 0, k, v, bufs["table"], bufs["k_pool"], bufs["v_pool"]), 20)
+    dspec = W.mistral_layer("decode")
+    dplan = sp.Plan(dspec)
+    db = dplan.allocate(dev)
+    kd = W.randn_bf16_device((dspec.total_tokens, Hkv, D), dspec.seed, W.TAG_K, 0, dev)
+    vd = W.randn_bf16_device((dspec.total_tokens, Hkv, D), dspec.seed, W.TAG_V, 0, dev)
+    sp.build(dplan, 0, kd, vd, db["table"], db["k_pool"], db["v_pool"])
+    qd = W.randn_bf16_device((dspec.num_seqs, Hq, D), dspec.seed, W.TAG_Q, 1, dev)
+    od = torch.empty_like(qd)
+    dmed, dmn = timed(lambda: sp.decode(dplan, 0, qd, db["table"], db["k_pool"], db["v_pool"],
+                                        1.0 / math.sqrt(D), od, workspace=db["workspace"]), 50)
+    dbytes = dplan.stats(0)["decode_tokens"] * 2 * D * 2
+    res["mistral_layer"] = {
+        "workload": "4 x 8192 tokens, 32 Q / 8 KV heads, D 128, page 64, KV head 0 global, 1-7 local (sink 4, window 1024)",
+        "prefill_tflops": round(flops / (pmed * 1e-3) / 1e12, 1),
+        "prefill_frac_of_bf16_peak": round(flops / (pmed * 1e-3) / 1e12 / BF16_PEAK_TFS, 4),
+        "prefill_ms": round(pmed, 4), "prefill_flops": flops,
+        "prefill_tok_per_s_with_build": round(T / ((pmed + bmed) * 1e-3), 1),
+        "build_ms": round(bmed, 4),
+        "decode_ms": round(dmed, 4), "decode_kv_bytes": dbytes,
+        "decode_gbs_cache_resident": round(dbytes / (dmed * 1e-3) / 1e9, 1),
+    }
+    log(f"mistral layer: prefill {pmed:.3f} ms ({flops / (pmed * 1e-3) / 1e12:.0f} TF/s), "
+        f"decode {dmed * 1e3:.1f} us")
+    return res
 
 
 def dense_mask_baseline(torch, W, pspec, dspec, k0, v0, q0, dev, pre_ms_layer, dec_ms, args, log):
