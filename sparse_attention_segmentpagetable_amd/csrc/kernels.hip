@@ -313,40 +313,80 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   }
 }
 
-// One wave per (unit, query head of its group): merge the unit's item partials.
-template <int D>
+// Merge the item partials of each (unit, query head of its group) pair by their
+// log-sum-exp weights. WPP waves work on one pair (WPP = 1: four pairs per
+// workgroup; WPP = 4: one). Inside a wave, groups of D/4 lanes each take one
+// item (a float4 of O per lane), so a wave has 64/(D/4) items and, unrolled,
+// several times that many loads in flight: the partials are L2-resident and the
+// merge is bound by load latency, not bytes.
+template <int D, int WPP>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const int32_t* __restrict__ tab, int32_t off_units, int32_t off_decunits, int32_t unit_b,
     int32_t unit_e, int32_t item_b, const float* __restrict__ ws, int32_t G, int32_t Hq,
     int32_t B, uint16_t* __restrict__ o, float* __restrict__ lse, int32_t all_layers) {
+  constexpr int LPI = D / 4;        // lanes per item
+  constexpr int IPW = 64 / LPI;     // items per wave at a time
+  constexpr int NS = IPW * WPP;     // items per pair at a time
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t idx = (int64_t)blockIdx.x * 4 + wave;
+  const int wp = wave % WPP;        // wave within its pair
+  const int64_t idx = (int64_t)blockIdx.x * (4 / WPP) + wave / WPP;
   const int64_t u = unit_b + idx / G;
   const int j = (int)(idx % G);
-  if (u >= unit_e) return;
+  if (u >= unit_e) return;          // uniform over the waves of a pair
   const int32_t* ur = tab + off_units + kUnitInts * u;
   const int32_t b = ur[U_B], l = ur[U_L], h = ur[U_H];
   const int32_t ib = tab[off_decunits + 2 * u], ie = tab[off_decunits + 2 * u + 1];
   const int64_t row = (all_layers ? (int64_t)l * B * Hq : 0) + (int64_t)b * Hq + h * G + j;
-  constexpr int PER = D / 64;
+  // record of (item it, query column j): D floats of O, then m (log2 units) and l
+  const float* rec0 = ws + ((int64_t)(ib - item_b) * G + j) * kWsStride<D>;
+  const int64_t rstride = (int64_t)G * kWsStride<D>;
+  // the unit's max over its items, one item per lane (every wave of the pair alike)
   float m = -INFINITY;
-  for (int32_t it = ib; it < ie; ++it)
-    m = fmaxf(m, ws[((int64_t)(it - item_b) * G + j) * kWsStride<D> + D]);
-  float accv[PER];
+  for (int32_t t = lane; t < ie - ib; t += 64) m = fmaxf(m, rec0[t * rstride + D]);
 #pragma unroll
-  for (int k = 0; k < PER; ++k) accv[k] = 0.f;
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
-  for (int32_t it = ib; it < ie; ++it) {
-    const float* w = ws + ((int64_t)(it - item_b) * G + j) * kWsStride<D>;
-    const float sc = fast_exp2(w[D] - m);
-    lsum += w[D + 1] * sc;
+  if (m != -INFINITY) {
+    const int slot = wp * IPW + lane / LPI, d0 = 4 * (lane % LPI);
+#pragma unroll 4
+    for (int32_t t = slot; t < ie - ib; t += NS) {
+      const float* w = rec0 + t * rstride;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(w + d0);
+      const float2 ml = *reinterpret_cast<const float2*>(w + D);
+      const float sc = fast_exp2(ml.x - m);
+      lsum += ml.y * sc;
+      acc += v * sc;
+    }
+  }
+  // the wave's item groups
 #pragma unroll
-    for (int k = 0; k < PER; ++k) accv[k] += w[lane + 64 * k] * sc;
+  for (int off = LPI; off < 64; off <<= 1) {
+    lsum += __shfl_xor(lsum, off, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], off, 64);
+  }
+  if constexpr (WPP > 1) {
+    __shared__ f32x4 sAcc[WPP][LPI];
+    __shared__ float sL[WPP];
+    if (lane < LPI) sAcc[wp][lane] = acc;
+    if (lane == 0) sL[wp] = lsum;
+    __syncthreads();
+    if (wp != 0) return;
+    if (lane < LPI)
+#pragma unroll
+      for (int w2 = 1; w2 < WPP; ++w2) acc += sAcc[w2][lane];
+#pragma unroll
+    for (int w2 = 1; w2 < WPP; ++w2) lsum += sL[w2];
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  if (lane < LPI) {
+    uint16_t r4[4];
 #pragma unroll
-  for (int k = 0; k < PER; ++k)
-    o[row * D + lane + 64 * k] = __builtin_bit_cast(uint16_t, (__bf16)(accv[k] * inv));
+    for (int i = 0; i < 4; ++i) r4[i] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i] * inv));
+    *reinterpret_cast<uint2*>(o + row * D + 4 * lane) =
+        make_uint2(r4[0] | ((uint32_t)r4[1] << 16), r4[2] | ((uint32_t)r4[3] << 16));
+  }
   if (lse && lane == 0) lse[row] = lsum > 0.f ? (m + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
 }
 
@@ -1105,15 +1145,17 @@ int check_launch() {
 
 struct Span {
   int64_t unit_b, unit_e, page_b, page_e, retr_b, retr_e, dec_b, dec_e, pre_b, pre_e;
+  int64_t max_unit_items;
 };
 
 Span span_of(const segpaged_plan* pl, int32_t layer) {
   if (layer >= 0) {
     const LayerRange& r = pl->layers[layer];
     return {r.unit_b, r.unit_e, r.page_b, r.page_e, r.retr_b, r.retr_e,
-            r.dec_b, r.dec_e, r.pre_b, r.pre_e};
+            r.dec_b, r.dec_e, r.pre_b, r.pre_e, r.max_unit_items};
   }
-  return {0, pl->num_units, 0, pl->num_pages, 0, pl->num_retr, 0, pl->n_dec, 0, pl->n_pre};
+  return {0, pl->num_units, 0, pl->num_pages, 0, pl->num_retr, 0, pl->n_dec, 0, pl->n_pre,
+          pl->max_unit_items};
 }
 
 int upload(const segpaged_plan* pl, int32_t* d_table, int64_t off, int64_t count,
@@ -1259,19 +1301,24 @@ SEGPAGED_API int segpaged_decode(const segpaged_plan* pl, int32_t layer, const v
     int rc = check_launch();
     if (rc) return rc;
   }
-  const int64_t waves = nunits * pl->G;
-  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  // Four waves per pair when some unit has many items and the pairs alone leave
+  // the chip short of waves (under 64 per CU); otherwise four pairs per workgroup.
+  const int64_t pairs = nunits * pl->G;
+  const int wpp = sp.max_unit_items > 16 && pairs < 64 * 256 ? 4 : 1;
+  const int64_t per_wg = 4 / wpp;
+  const dim3 grid((unsigned)((pairs + per_wg - 1) / per_wg)), block(256);
   auto* oo = (uint16_t*)o;
-  if (pl->D == 128)
-    hipLaunchKernelGGL(decode_combine_kernel<128>, grid, block, 0, st, d_table,
-                       (int32_t)pl->off_units, (int32_t)pl->off_decunits, (int32_t)sp.unit_b,
-                       (int32_t)sp.unit_e, (int32_t)sp.dec_b, ws, pl->G, pl->Hq, pl->B, oo, lse,
-                       (int32_t)(layer < 0));
-  else
-    hipLaunchKernelGGL(decode_combine_kernel<64>, grid, block, 0, st, d_table,
-                       (int32_t)pl->off_units, (int32_t)pl->off_decunits, (int32_t)sp.unit_b,
-                       (int32_t)sp.unit_e, (int32_t)sp.dec_b, ws, pl->G, pl->Hq, pl->B, oo, lse,
-                       (int32_t)(layer < 0));
+#define SEGPAGED_LAUNCH_COMBINE(DD, WW)                                                          \
+  hipLaunchKernelGGL((decode_combine_kernel<DD, WW>), grid, block, 0, st, d_table,               \
+                     (int32_t)pl->off_units, (int32_t)pl->off_decunits, (int32_t)sp.unit_b,     \
+                     (int32_t)sp.unit_e, (int32_t)sp.dec_b, ws, pl->G, pl->Hq, pl->B, oo, lse,  \
+                     (int32_t)(layer < 0))
+  if (pl->D == 128) {
+    if (wpp == 4) SEGPAGED_LAUNCH_COMBINE(128, 4); else SEGPAGED_LAUNCH_COMBINE(128, 1);
+  } else {
+    if (wpp == 4) SEGPAGED_LAUNCH_COMBINE(64, 4); else SEGPAGED_LAUNCH_COMBINE(64, 1);
+  }
+#undef SEGPAGED_LAUNCH_COMBINE
   return check_launch();
 }
 

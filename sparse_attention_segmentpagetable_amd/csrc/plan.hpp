@@ -35,6 +35,7 @@ struct LayerRange {
   int64_t retr_b, retr_e;   // retrieval positions
   int64_t dec_b, dec_e;     // decode items
   int64_t pre_b, pre_e;     // prefill items
+  int64_t max_unit_items;   // most decode items of one unit
 };
 
 }  // namespace segpaged
@@ -46,7 +47,7 @@ struct segpaged_plan {
   int64_t q_rows = 0, kv_rows = 0;
   int64_t off_seqs = 0, off_units = 0, off_pages = 0, off_retr = 0, table_len = 0;
   int64_t off_decunits = 0, off_dec = 0, off_pre = 0, total_ints = 0;
-  int64_t n_dec = 0, n_pre = 0;
+  int64_t n_dec = 0, n_pre = 0, max_unit_items = 0;
   std::vector<int32_t> buf;                  // device image: table ++ work lists
   std::vector<segpaged::LayerRange> layers;  // per-layer slices of buf
   std::vector<segpaged_stats> stats;         // per-layer work counts

@@ -296,6 +296,7 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
     lr.page_b = page_cursor; lr.retr_b = retr_cursor;
     lr.dec_b = (int64_t)dec_items.size() / kDecItemInts;
     lr.pre_b = (int64_t)pre_items.size() / kPreItemInts;
+    lr.max_unit_items = 0;
     struct PreTile { int64_t cost, unit, r0; };
     std::vector<PreTile> tiles;
     for (int64_t b = 0; b < B; ++b)
@@ -372,6 +373,7 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
           }
         }
         du[1] = (int32_t)(dec_items.size() / kDecItemInts);
+        lr.max_unit_items = std::max<int64_t>(lr.max_unit_items, du[1] - du[0]);
 
         // prefill tiles
         for (int64_t r0 = q0; r0 < n; r0 += BQ) {
@@ -393,6 +395,7 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
     st.pages = lr.page_e - lr.page_b;
     st.decode_items = lr.dec_e - lr.dec_b;
     st.prefill_items = lr.pre_e - lr.pre_b;
+    pl->max_unit_items = std::max(pl->max_unit_items, lr.max_unit_items);
   }
   pl->n_dec = (int64_t)dec_items.size() / kDecItemInts;
   pl->n_pre = (int64_t)pre_items.size() / kPreItemInts;
