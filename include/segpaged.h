@@ -148,7 +148,9 @@ SEGPAGED_API int segpaged_plan_sizes(const segpaged_plan* plan, segpaged_sizes* 
  *           for other classes; unused segment fields 0)
  *   pages   page id of each table page (a unit's pages start at page_off)
  *   retr    positions of the RETRIEVAL segments, units in order
- * The ints after table_len are the kernels' work lists (not part of the format).
+ * The ints after table_len are the kernels' work lists and, last, L + 1 lines of
+ * 16 zero ints that prefill calls use as work counters (not part of the format;
+ * segpaged_build uploads the lines of its layer and of all-layer calls).
  * ENOSPACE if n < table_int32s. */
 SEGPAGED_API int segpaged_plan_table_host(const segpaged_plan* plan, int32_t* out, int64_t n);
 
@@ -184,9 +186,13 @@ SEGPAGED_API int segpaged_build(const segpaged_plan* plan, int32_t layer,
  *   scale softmax scale, typically 1/sqrt(D)
  *   workspace/workspace_bytes: prefill_workspace_bytes (may be NULL when 0)
  * d_table, k_pool, v_pool must hold what segpaged_build wrote for this layer.
+ * Workgroups take the tiles heaviest-first from a work counter in d_table's
+ * counter line of this layer (layer = -1: the all-layers line); the call leaves
+ * it at zero again. Calls for the same layer on one d_table must therefore not
+ * overlap; other calls may.
  * A row whose visible set is empty (RETRIEVAL only) gets O = 0, LSE = -inf. */
 SEGPAGED_API int segpaged_prefill(const segpaged_plan* plan, int32_t layer, const void* q,
-                                  const int32_t* d_table, const void* k_pool,
+                                  int32_t* d_table, const void* k_pool,
                                   const void* v_pool, float scale, void* o, float* lse,
                                   void* workspace, int64_t workspace_bytes, void* stream);
 

@@ -16,6 +16,7 @@
 // key (K) or 8 consecutive keys of one head dim (V).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -430,8 +431,14 @@ struct TileRuns {
 // on lgkmcnt, so unlike a vector load it never forces a vmcnt wait that would
 // drain the in-flight LDS-DMA transfers.
 __device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p) {
+  // the address is uniform; readfirstlane states it for the SGPR operand
+  const uint64_t a = (uint64_t)p;
+  const uint64_t sa = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)a);
   int32_t v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=s"(v)
+               : "s"((const int32_t*)sa));
   return v;
 }
 
@@ -561,7 +568,7 @@ __device__ __forceinline__ void segment_runs(int kind, int32_t pos0, int32_t len
 template <int D, bool SMALLP>
 __global__ __launch_bounds__(512) void prefill_kernel(
     const int32_t* __restrict__ tab, int32_t off_seqs, int32_t off_units, int32_t off_pages,
-    int32_t off_retr, int32_t off_pre, int32_t item_b, int32_t item_e,
+    int32_t off_retr, int32_t off_pre, int32_t item_b, int32_t item_e, int32_t* __restrict__ ctr,
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, float* __restrict__ lse,
     int64_t q_layer_stride, int64_t lse_layer_stride, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vp, int32_t G, int32_t Hq, int32_t P, int32_t log2P, float c) {
@@ -584,17 +591,69 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   __shared__ __attribute__((aligned(16))) int32_t sPos[NBUF][64];
   __shared__ int32_t sRun[4][4];
   __shared__ int32_t sOverflow;
+  __shared__ int32_t sItem[2];
 
-  const int32_t it = item_b + (int32_t)blockIdx.x;
-  if (it >= item_e) return;
-  const int32_t u = tab[off_pre + kPreItemInts * it];
-  const int32_t r0 = tab[off_pre + kPreItemInts * it + 1];
-  const int32_t* ur = tab + off_units + kUnitInts * u;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, g = lane >> 5;
+  // this wave's 32 query rows: lane column n is row 32 * wave + n
+  const int row = 32 * wave + n;
+  const int32_t pq = row / G, jh = row % G;
+
+  // O accumulators and row statistics; they outlive a tile, whose O is written
+  // once the next tile's Q and first K/V blocks are in flight
+  f32x16 oacc[MD];
+  float m_run = -INFINITY, l_run = 0.f;
+  bool e_valid = false, e_row_ok = false;
+  int64_t e_obase = 0, e_lidx = 0;
+#define SEGPAGED_EPILOGUE_PREV()                                                              \
+  do {                                                                                        \
+    if (e_valid) {                                                                            \
+      /* O^T lane (n, g) reg i of dim tile md -> dim 32md + 8(i/4) + 4g + (i%4) */            \
+      const float l_tot_ = l_run + __shfl_xor(l_run, 32, 64);                                 \
+      if (e_row_ok) {                                                                         \
+        const float inv_ = l_tot_ > 0.f ? 1.f / l_tot_ : 0.f;                                 \
+        uint16_t* op_ = o + e_obase;                                                          \
+        _Pragma("unroll") for (int md = 0; md < MD; ++md)                                     \
+            _Pragma("unroll") for (int qd = 0; qd < 4; ++qd) {                                \
+          u32x2 w_;                                                                           \
+          w_.x = pack_bf16x2(oacc[md][4 * qd + 0] * inv_, oacc[md][4 * qd + 1] * inv_);       \
+          w_.y = pack_bf16x2(oacc[md][4 * qd + 2] * inv_, oacc[md][4 * qd + 3] * inv_);       \
+          *reinterpret_cast<u32x2*>(op_ + 32 * md + 8 * qd + 4 * g) = w_;                     \
+        }                                                                                     \
+        if (lse && g == 0)                                                                    \
+          lse[e_lidx] = l_tot_ > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot_)) * kLn2         \
+                                     : -INFINITY;                                             \
+      }                                                                                       \
+    }                                                                                         \
+    _Pragma("unroll") for (int md = 0; md < MD; ++md)                                         \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i) oacc[md][i] = 0.f;                     \
+    m_run = -INFINITY;                                                                        \
+    l_run = 0.f;                                                                              \
+  } while (0)
+
+  // Persistent workgroups take items of the heaviest-first list from a counter
+  // (ctr[0]), so faster compute units take more: the next item is fetched while
+  // the current one runs. ctr[1] counts finished workgroups; the last one resets
+  // both for the next launch.
+  if (tid == 0) sItem[0] = atomicAdd(&ctr[0], 1);
+  __syncthreads();
+  for (int32_t round = 0;; ++round) {
+  const int32_t it = item_b + __builtin_amdgcn_readfirstlane(sItem[round & 1]);
+  if (it >= item_e) break;
+  int32_t it_next = 0;  // the item after this one (wave 0, lane 0)
+  // tile metadata through the constant address space: scalar loads (the table
+  // is not written while a kernel runs)
+  typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+  const cint_ptr ctab = (cint_ptr)tab;
+  const int32_t u = ctab[off_pre + kPreItemInts * it];
+  const int32_t r0 = ctab[off_pre + kPreItemInts * it + 1];
+  const cint_ptr ur = ctab + off_units + kUnitInts * u;
   const int32_t kind = ur[U_KIND], b = ur[U_B], l = ur[U_L], h = ur[U_H], N = ur[U_N];
   const int32_t q0 = ur[U_Q0], sink = ur[U_SINK], win = ur[U_WIN], nseg = ur[U_NSEG];
   const int32_t* pages = tab + off_pages + ur[U_PAGEOFF];
   const int32_t* rpos = tab + off_retr + ur[U_RETROFF];
-  const int32_t qrow0 = tab[off_seqs + kSeqInts * b + S_QOFF];
+  const int32_t qrow0 = ctab[off_seqs + kSeqInts * b + S_QOFF];
   const int32_t BQ = kPrefillRows / G;
   const int32_t r1 = min(N, r0 + BQ), rmax = r1 - 1;
   const int64_t PD = (int64_t)P * D;
@@ -602,16 +661,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const bool gathered = ur[U_S0POS] < 0;
   const bool local = kind == SEGPAGED_LOCAL;
   // page table through the constant address space: compiler-tracked scalar loads
-  typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
   const cint_ptr cpages = (cint_ptr)pages;
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 31, g = lane >> 5;
   if (tid == 0) sOverflow = 0;
-  // this wave's 32 query rows: lane column n is row 32 * wave + n
-  const int row = 32 * wave + n;
-  const int32_t pq = row / G, jh = row % G;
   const int32_t qpos = r0 + pq;
   const bool row_ok = pq < r1 - r0;
   const int64_t orow = (int64_t)qrow0 + (qpos - q0);
@@ -639,12 +691,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   }
   const int32_t nblocks = runs.total();
 
-  f32x16 oacc[MD];
-#pragma unroll
-  for (int md = 0; md < MD; ++md)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[md][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f, neg_m = 0.f;
+  float neg_m = 0.f;
 
   // Lane chunk of a block tile: K chunk (head-dim group cidx / BK, key cidx % BK),
   // V chunk cidx (key group cidx / D, head dim cidx % D); both land at LDS chunk
@@ -971,6 +1018,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       ic_pid = cpages[ic_slot >> log2P];
     }
     SEGPAGED_MASK_STATE();
+    // the previous tile's O while this tile's Q and first blocks are in flight
+    SEGPAGED_EPILOGUE_PREV();
+    // the next item; its return is waited for with the blocks below
+    if (tid == 0) it_next = atomicAdd(&ctr[0], 1);
+    // Q and blocks 0 and 1 landed: vector loads complete in issue order and the
+    // O stores can only lower the count
     WAIT_VM_LGKM0((NBUF - 3) * PER_BLOCK);
     ring_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -1093,6 +1146,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       }
       WAIT_VM_LGKM0(0);
     }
+  } else {
+    SEGPAGED_EPILOGUE_PREV();
+    if (tid == 0) it_next = atomicAdd(&ctr[0], 1);
   }
 #undef SEGPAGED_PHASE_END
 #undef SEGPAGED_BLOCK_SOURCES
@@ -1111,24 +1167,19 @@ __global__ __launch_bounds__(512) void prefill_kernel(
 #undef SEGPAGED_LOAD_V
 #undef SEGPAGED_LOAD_K
 #undef SEGPAGED_ISSUE
-
-  // ---- epilogue: O^T lane (n, g) reg i of dim tile md -> dim 32md + 8(i/4) + 4g + (i%4)
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (row_ok) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* op = o + (int64_t)l * q_layer_stride + (orow * Hq + hq) * D;
-#pragma unroll
-    for (int md = 0; md < MD; ++md)
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        u32x2 w;
-        w.x = pack_bf16x2(oacc[md][4 * qd + 0] * inv, oacc[md][4 * qd + 1] * inv);
-        w.y = pack_bf16x2(oacc[md][4 * qd + 2] * inv, oacc[md][4 * qd + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + 32 * md + 8 * qd + 4 * g) = w;
-      }
-    if (lse && g == 0)
-      lse[(int64_t)l * lse_layer_stride + orow * Hq + hq] =
-          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+  if (tid == 0) sItem[(round + 1) & 1] = it_next;
+  // every wave is done with the ring and sOverflow before the next tile's set-up
+  __syncthreads();
+  e_valid = true;
+  e_row_ok = row_ok;
+  e_obase = (int64_t)l * q_layer_stride + (orow * Hq + hq) * D;
+  e_lidx = (int64_t)l * lse_layer_stride + orow * Hq + hq;
+  }  // tile loop
+  SEGPAGED_EPILOGUE_PREV();
+#undef SEGPAGED_EPILOGUE_PREV
+  if (tid == 0 && atomicAdd(&ctr[1], 1) == (int32_t)gridDim.x - 1) {
+    atomicExch(&ctr[0], 0);
+    atomicExch(&ctr[1], 0);
   }
 }
 
@@ -1137,6 +1188,18 @@ __global__ __launch_bounds__(512) void prefill_kernel(
 // ---------------------------------------------------------------------------
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+// Compute units of the current device (cached per device id; 0 on error).
+int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  return n;
+}
 
 int check_launch() {
   const hipError_t e = hipGetLastError();
@@ -1200,6 +1263,9 @@ SEGPAGED_API int segpaged_build(const segpaged_plan* pl, int32_t layer, const vo
     if ((rc = upload(pl, d_table, pl->off_pre + kPreItemInts * sp.pre_b,
                      kPreItemInts * (sp.pre_e - sp.pre_b), st)))
       return rc;
+    // zeroed prefill work counters of this layer and of all-layer calls
+    if ((rc = upload(pl, d_table, pl->off_ctr + kCtrInts * layer, kCtrInts, st))) return rc;
+    if ((rc = upload(pl, d_table, pl->off_ctr + kCtrInts * pl->L, kCtrInts, st))) return rc;
   }
   const int64_t npages = sp.page_e - sp.page_b;
   if (npages == 0) return SEGPAGED_OK;
@@ -1223,7 +1289,7 @@ SEGPAGED_API int segpaged_build(const segpaged_plan* pl, int32_t layer, const vo
 }
 
 SEGPAGED_API int segpaged_prefill(const segpaged_plan* pl, int32_t layer, const void* q,
-                                  const int32_t* d_table, const void* k_pool, const void* v_pool,
+                                  int32_t* d_table, const void* k_pool, const void* v_pool,
                                   float scale, void* o, float* lse, void* workspace,
                                   int64_t workspace_bytes, void* stream) {
   (void)workspace;
@@ -1241,7 +1307,12 @@ SEGPAGED_API int segpaged_prefill(const segpaged_plan* pl, int32_t layer, const 
   const int64_t qstride = layer < 0 ? pl->q_rows * pl->Hq * pl->D : 0;
   const int64_t lstride = layer < 0 ? pl->q_rows * pl->Hq : 0;
   const float c = scale * kLog2e;
-  const dim3 grid((unsigned)nitems), block(512);
+  // persistent workgroups, one per compute unit (a workgroup fills a CU's
+  // registers), each walking its share of the items
+  const int cus = device_cus();
+  if (cus <= 0) return SEGPAGED_EHIP;
+  const dim3 grid((unsigned)std::min<int64_t>(nitems, cus)), block(512);
+  int32_t* ctr = d_table + pl->off_ctr + kCtrInts * (layer < 0 ? pl->L : layer);
   auto* qq = (const uint16_t*)q;
   auto* oo = (uint16_t*)o;
   auto* kpp = (const uint16_t*)k_pool;
@@ -1250,7 +1321,8 @@ SEGPAGED_API int segpaged_prefill(const segpaged_plan* pl, int32_t layer, const 
   hipLaunchKernelGGL((prefill_kernel<DD, SP>), grid, block, 0, st, d_table,                     \
                      (int32_t)pl->off_seqs, (int32_t)pl->off_units, (int32_t)pl->off_pages,     \
                      (int32_t)pl->off_retr, (int32_t)pl->off_pre, (int32_t)sp.pre_b,            \
-                     (int32_t)sp.pre_e, qq, oo, lse, qstride, lstride, kpp, vpp, pl->G, pl->Hq,  \
+                     (int32_t)sp.pre_e, ctr, qq, oo, lse, qstride, lstride, kpp, vpp, pl->G,     \
+                     pl->Hq,                                                                     \
                      pl->P, pl->log2P, c)
   const bool small_pages = pl->P < kBlockN;  // a 32-key block spans two pages
   if (pl->D == 128) {

@@ -28,6 +28,7 @@ constexpr int kPreItemInts = 2;   // unit, first query position of the tile
 constexpr int kPrefillRows = 256; // query rows per prefill tile: G heads x (256 / G) positions
 constexpr int kBlockN = 32;       // keys per prefill block
 constexpr int kMaxGroup = 16;     // Q heads per KV head the decode kernel supports
+constexpr int kCtrInts = 16;      // prefill work counter line per layer (+1 for all layers)
 
 struct LayerRange {
   int64_t unit_b, unit_e;   // units
@@ -46,7 +47,7 @@ struct segpaged_plan {
   int64_t num_units = 0, num_pages = 0, pool_pages = 0, num_retr = 0;
   int64_t q_rows = 0, kv_rows = 0;
   int64_t off_seqs = 0, off_units = 0, off_pages = 0, off_retr = 0, table_len = 0;
-  int64_t off_decunits = 0, off_dec = 0, off_pre = 0, total_ints = 0;
+  int64_t off_decunits = 0, off_dec = 0, off_pre = 0, off_ctr = 0, total_ints = 0;
   int64_t n_dec = 0, n_pre = 0, max_unit_items = 0;
   std::vector<int32_t> buf;                  // device image: table ++ work lists
   std::vector<segpaged::LayerRange> layers;  // per-layer slices of buf

@@ -401,10 +401,12 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
   pl->n_pre = (int64_t)pre_items.size() / kPreItemInts;
   pl->off_dec = pl->off_decunits + 2 * U;
   pl->off_pre = pl->off_dec + (int64_t)dec_items.size();
-  pl->total_ints = pl->off_pre + (int64_t)pre_items.size();
+  pl->off_ctr = pl->off_pre + (int64_t)pre_items.size();
+  pl->total_ints = pl->off_ctr + (int64_t)kCtrInts * (L + 1);
   if (pl->total_ints > kI32Max) { delete pl; return SEGPAGED_EINVAL; }
   t.insert(t.end(), dec_items.begin(), dec_items.end());
   t.insert(t.end(), pre_items.begin(), pre_items.end());
+  t.resize(pl->total_ints, 0);  // prefill work counters, zero between calls
 
   segpaged_stats& tot = pl->total;
   tot = segpaged_stats{};

@@ -86,7 +86,9 @@ def _decode_items(plan):
     U = z.num_units
     du = t[z.table_len:z.table_len + 2 * U].reshape(U, 2)
     items = t[z.table_len + 2 * U:z.table_len + 2 * U + 4 * z.decode_items].reshape(-1, 4)
-    pre = t[z.table_len + 2 * U + 4 * z.decode_items:].reshape(-1, 2)
+    p0 = z.table_len + 2 * U + 4 * z.decode_items
+    pre = t[p0:p0 + 2 * z.prefill_items].reshape(-1, 2)
+    assert np.all(t[p0 + 2 * z.prefill_items:] == 0)  # work counters start at zero
     return t, du, items, pre
 
 
