@@ -232,6 +232,8 @@ def main():
     dec_ms = [a.elapsed_time(b) for a, b in reps]
     dec_med = float(np.median(dec_ms))
 
+    ceil = measure_ceilings(torch, dev, stream, log)
+
     pre_ms_layer = float(np.mean(dur["prefill"]))
     pre_ms_step = float(np.sum(dur["prefill"])) / args.steps
     bld_ms_step = float(np.sum(dur["build"])) / args.steps
@@ -292,6 +294,7 @@ def main():
             "peak": BF16_PEAK_TFS,
             "unit": "TFLOP/s",
             "frac": round(pre_tflops / BF16_PEAK_TFS, 4),
+            "frac_of_measured_ceiling": round(pre_tflops / ceil["mfma_bf16_tflops"], 4),
             "traffic": measured_traffic("prefill_kernel"),
             "traffic_unit": "bytes per launch (one layer)",
         },
@@ -302,12 +305,14 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "frac_of_measured_ceiling": round(dec_gbs / ceil["hbm_read_gbs"], 4),
             "traffic": measured_traffic("decode_partial_kernel"),
             "traffic_unit": "bytes per launch (all layers)",
             "algorithmic_bytes_per_launch": decode_bytes,
         },
     }
 
+    out["measured_ceilings"] = ceil
     if not args.no_dense:
         try:
             out["dense_mask"] = dense_mask_baseline(torch, W, pspec, dspec, ks[0], vs[0], qs[0],
@@ -321,6 +326,58 @@ def main():
         torch.cuda.empty_cache()
         out.update(extra_configs(torch, W, sp, dev, stream, log))
     print(json.dumps(out), flush=True)
+
+
+def measure_ceilings(torch, dev, stream, log):
+    """What the chip sustains on this machine, from the probes of libsegpaged_probe.so:
+    dense bf16 MFMA issue with N(0,1) operands (one and two 8-wave workgroups per
+    CU; the better is kept) and a streaming read of 4 GiB (16 times the 256 MB
+    Infinity Cache; the best of 1-32 workgroups per CU x 4, 8, 16 loads in flight
+    per thread). Operands that change every MFMA hold the clock lower than constant
+    ones (~1.6 vs ~2.0 PFLOP/s here), so the probe rotates them as the attention
+    kernels' operands do. Timed with HIP events, median of 5."""
+    from sparse_attention_segmentpagetable_amd import probe
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    g = torch.Generator(device="cpu").manual_seed(2024)
+    seed = torch.randn(probe.SEED_ELEMS, generator=g).to(torch.bfloat16).to(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def med(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ts]))
+
+    iters = 200
+    best = 0.0
+    for per_cu in (1, 2):
+        wgs = cus * per_cu
+        out = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
+        ms = med(lambda: probe.mfma_bf16(seed, iters, wgs, out))
+        best = max(best, wgs * 8 * iters * 8 * 32768 / (ms * 1e-3) / 1e12)
+    src = torch.ones((4 << 30) // 4, dtype=torch.float32, device=dev)
+    ms = float("inf")
+    for per_cu in (1, 2, 4, 8, 16, 32):
+        for depth in (4, 8, 16):
+            wgs = cus * per_cu
+            out = torch.empty(wgs, dtype=torch.float32, device=dev)
+            ms = min(ms, med(lambda: probe.hbm_read(src, wgs, out, depth=depth)))
+    hbm = src.numel() * 4 / (ms * 1e-3) / 1e9
+    del src
+    torch.cuda.empty_cache()
+    log(f"measured ceilings: bf16 MFMA {best:.0f} TF/s, HBM read {hbm:.0f} GB/s")
+    return {"mfma_bf16_tflops": round(best, 1), "hbm_read_gbs": round(hbm, 1),
+            "mfma_frac_of_peak": round(best / BF16_PEAK_TFS, 4),
+            "hbm_frac_of_peak": round(hbm / HBM_PEAK_GBS, 4),
+            "probes": "include/segpaged_probe.h (bf16 MFMA loop, N(0,1) operands; 4 GiB "
+                      "streaming read)"}
 
 
 def extra_configs(torch, W, sp, dev, stream, log):
@@ -415,7 +472,99 @@ def extra_configs(torch, W, sp, dev, stream, log):
     }
     log(f"mistral layer: prefill {pmed:.3f} ms ({flops / (pmed * 1e-3) / 1e12:.0f} TF/s), "
         f"decode {dmed * 1e3:.1f} us")
+    del plan, bufs, k, v, q, o, dplan, db
+    torch.cuda.empty_cache()
+    res["long_prefill_decode_form_build"] = decode_form_build(torch, W, sp, dev, timed, log)
+    res["decode_context_sweep"] = decode_context_sweep(torch, W, sp, dev, timed, log)
     return res
+
+
+def decode_form_build(torch, W, sp, dev, timed, log):
+    """The long-prefill workload's cache in decode form (what decoding after the
+    prefill keeps: local heads only their sink and last 8192 keys), built per layer
+    from the same dense K/V and reported apart from the prefill-form build."""
+    pspec = W.long_prefill(num_layers=4)
+    dspec = W.decode_form(pspec)
+    plan = sp.Plan(dspec)
+    bufs = plan.allocate(dev, workspace=False)
+    n, Hkv, D = pspec.seq_len[0], pspec.num_kv_heads, pspec.head_dim
+    k = W.randn_bf16_device((n, Hkv, D), pspec.seed, W.TAG_K, 0, dev)
+    v = W.randn_bf16_device((n, Hkv, D), pspec.seed, W.TAG_V, 0, dev)
+    per = []
+    for l in range(4):
+        ms, _ = timed(lambda: sp.build(plan, l, k, v, bufs["table"], bufs["k_pool"],
+                                       bufs["v_pool"]), 10)
+        tok = plan.stats(l)["retained_tokens"]
+        per.append((ms, tok))
+    ms = float(np.mean([p[0] for p in per]))
+    tok = float(np.mean([p[1] for p in per]))
+    gbs = 2 * 2 * D * 2 * tok / (ms * 1e-3) / 1e9
+    log(f"long-prefill decode-form build: {ms:.3f} ms/layer, {2 * D * 2 * tok / 1e6:.0f} MB of "
+        f"K/V kept, {gbs:.0f} GB/s")
+    del plan, bufs, k, v
+    torch.cuda.empty_cache()
+    return {"workload": f"layers 0-3 of the long-prefill workload ({n} tokens) in decode form",
+            "ms_per_layer": round(ms, 4), "kv_bytes_kept_per_layer": int(2 * D * 2 * tok),
+            "gbs_read_plus_write": round(gbs, 1)}
+
+
+def decode_context_sweep(torch, W, sp, dev, timed, log):
+    """Decode speedup over the dense-mask path as the context grows: the
+    Llama-shaped decode (8 sequences, 8 layers, 15% global, local sink 4 window
+    8192) at N = 8K .. 128K; SegPaged one all-layer call, dense-mask torch SDPA
+    with boolean masks per layer on dense K/V, both on the same K/V values."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    import torch.nn.functional as F
+    rows = []
+    for n in (8192, 16384, 32768, 65536, 131072):
+        spec = W.llama70b_decode(num_layers=8, n=n)
+        B, Hq, Hkv, D, G, L = (spec.num_seqs, spec.num_q_heads, spec.num_kv_heads,
+                               spec.head_dim, spec.group, spec.num_layers)
+        plan = sp.Plan(spec)
+        bufs = plan.allocate(dev)
+        k = W.randn_bf16_device((B * n, Hkv, D), spec.seed, W.TAG_K, 0, dev)
+        v = W.randn_bf16_device((B * n, Hkv, D), spec.seed, W.TAG_V, 0, dev)
+        for l in range(L):
+            sp.build(plan, l, k, v, bufs["table"], bufs["k_pool"], bufs["v_pool"])
+        q = W.randn_bf16_device((L, B, Hq, D), spec.seed, W.TAG_Q, 0, dev)
+        o = torch.empty_like(q)
+        scale = 1.0 / math.sqrt(D)
+        seg_ms, _ = timed(lambda: sp.decode(plan, -1, q, bufs["table"], bufs["k_pool"],
+                                            bufs["v_pool"], scale, o, workspace=bufs["workspace"]),
+                          10)
+        kv_bytes = plan.stats(-1)["decode_tokens"] * 2 * D * 2
+        del bufs, plan
+        # dense: [B, Hkv, n, D], the G query heads of a KV head folded into the query axis
+        kd = k.view(B, n, Hkv, D).permute(0, 2, 1, 3).contiguous()
+        vd = v.view(B, n, Hkv, D).permute(0, 2, 1, 3).contiguous()
+        del k, v
+        qd = q[0].view(B, Hkv, G, D).contiguous()
+        jj = torch.arange(n, device=dev)
+        masks = []
+        for l in range(L):
+            mm = []
+            for h in range(Hkv):
+                kind, s_, w_ = spec.head_class(l, h)
+                m = jj <= n - 1
+                if kind == W.LOCAL:
+                    m = m & ((jj < s_) | (jj > n - 1 - w_))
+                mm.append(m)
+            masks.append(torch.stack(mm)[None, :, None, :].expand(B, Hkv, G, n).contiguous())
+        with sdpa_kernel([SDPBackend.EFFICIENT_ATTENTION]):
+            def dense_all():
+                for l in range(L):
+                    F.scaled_dot_product_attention(qd, kd, vd, attn_mask=masks[l])
+            dense_ms, _ = timed(dense_all, 3)
+        del kd, vd, qd, masks, q, o
+        torch.cuda.empty_cache()
+        rows.append({"n": n, "segpaged_ms": round(seg_ms, 4),
+                     "segpaged_kv_gbs": round(kv_bytes / (seg_ms * 1e-3) / 1e9, 1),
+                     "dense_mask_ms": round(dense_ms, 4),
+                     "speedup_vs_dense_mask": round(dense_ms / seg_ms, 2)})
+        log(f"decode sweep N={n}: segpaged {seg_ms:.3f} ms, dense-mask {dense_ms:.3f} ms, "
+            f"x{dense_ms / seg_ms:.1f}")
+    return {"workload": "llama70b-shaped decode, 8 seqs x 8 layers, one all-layer call",
+            "rows": rows}
 
 
 def dense_mask_baseline(torch, W, pspec, dspec, k0, v0, q0, dev, pre_ms_layer, dec_ms, args, log):

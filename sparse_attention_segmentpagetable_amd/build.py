@@ -1,5 +1,6 @@
 """Compile libsegpaged.so in-tree for gfx950 with hipcc (the HIP kernels, the
-C-ABI and the host planner in one shared library)."""
+C-ABI and the host planner in one shared library), and libsegpaged_probe.so
+(the rate probes of include/segpaged_probe.h, used for measurement only)."""
 import os
 import subprocess
 import sys
@@ -8,6 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "lib", "libsegpaged.so")
+PROBE_LIB = os.path.join(PKG, "lib", "libsegpaged_probe.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -17,12 +19,12 @@ HIPCC_FLAGS = [
 ]
 
 
-def build_library(verbose: bool = False) -> str:
+def _compile(sources, out, verbose):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    os.makedirs(os.path.dirname(LIB), exist_ok=True)
-    tmp = LIB + ".tmp"
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp"
     cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           os.path.join(CSRC, "planner.cpp"), os.path.join(CSRC, "kernels.hip"), "-o", tmp]
+           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -31,8 +33,13 @@ def build_library(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
     if verbose and errs:
         print("\n".join(errs), file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build_library(verbose: bool = False) -> str:
+    _compile(["probe.hip"], PROBE_LIB, verbose)
+    return _compile(["planner.cpp", "kernels.hip"], LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -216,3 +216,21 @@ def test_library_exports_every_header_symbol():
     exported = set(re.findall(r" T (segpaged_\w+)", out))
     assert set(names) == exported
     assert lib.segpaged_version() >= 100
+
+
+def test_probe_library_exports_its_header_symbols():
+    from sparse_attention_segmentpagetable_amd import probe
+    hdr = open(os.path.join(ROOT, "include", "segpaged_probe.h")).read()
+    names = re.findall(r"SEGPAGED_API\s+[\w\s\*]+?\b(segpaged_\w+)\s*\(", hdr)
+    assert sorted(names) == ["segpaged_probe_hbm_read", "segpaged_probe_mfma_bf16"]
+    lib = probe.library()
+    out = subprocess.run(["nm", "-D", "--defined-only", probe.PROBE_LIB_PATH],
+                         capture_output=True, text=True).stdout
+    assert set(re.findall(r" T (segpaged_\w+)", out)) == set(names)
+    # argument checks happen before any launch (no GPU needed)
+    fake = ctypes.c_void_p(4096)
+    assert lib.segpaged_probe_mfma_bf16(None, 1, 1, fake, None) == -1
+    assert lib.segpaged_probe_mfma_bf16(fake, 0, 1, fake, None) == -1
+    assert lib.segpaged_probe_hbm_read(fake, 24, 1, 8, fake, None) == -1
+    assert lib.segpaged_probe_hbm_read(fake, 16, 0, 8, fake, None) == -1
+    assert lib.segpaged_probe_hbm_read(fake, 16, 1, 5, fake, None) == -1
