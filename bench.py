@@ -476,7 +476,66 @@ def extra_configs(torch, W, sp, dev, stream, log):
     torch.cuda.empty_cache()
     res["long_prefill_decode_form_build"] = decode_form_build(torch, W, sp, dev, timed, log)
     res["decode_context_sweep"] = decode_context_sweep(torch, W, sp, dev, timed, log)
+    res["decode_loop_append"] = decode_loop_append(torch, W, sp, dev, stream, log)
     return res
+
+
+def decode_loop_append(torch, W, sp, dev, stream, log):
+    """The Llama-shaped decode (8 x 32K x 80 layers) as a decode loop: a cache
+    planned once with room to grow, then per step each sequence gains a token
+    (segpaged_plan_append on the host, segpaged_append writing its K/V for all 80
+    layers) and the all-layer decode runs. Host plan time, device append time and
+    decode time per step; the step is what a serving loop pays per token."""
+    import time as _time
+    steps, cap = 32, 64
+    spec = W.llama70b_decode(num_layers=80, n=32768)
+    B, Hkv, D, L = spec.num_seqs, spec.num_kv_heads, spec.head_dim, spec.num_layers
+    plan = sp.Plan(spec, append_capacity=cap)
+    bufs = plan.allocate(dev)
+    for l in range(L):
+        kd = W.randn_bf16_device((B * 32768, Hkv, D), spec.seed, W.TAG_K, l, dev)
+        vd = W.randn_bf16_device((B * 32768, Hkv, D), spec.seed, W.TAG_V, l, dev)
+        sp.build(plan, l, kd, vd, bufs["table"], bufs["k_pool"], bufs["v_pool"])
+        del kd, vd
+    q = W.randn_bf16_device((L, B, spec.num_q_heads, D), spec.seed, W.TAG_Q, 0, dev)
+    o = torch.empty_like(q)
+    kn = W.randn_bf16_device((L, B, Hkv, D), spec.seed, 77, 0, dev)
+    vn = W.randn_bf16_device((L, B, Hkv, D), spec.seed, 78, 0, dev)
+    scale = 1.0 / math.sqrt(D)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    host_ms, app_ev, dec_ev, kv_bytes = [], [], [], []
+    torch.cuda.synchronize()
+    t0 = _time.perf_counter()
+    for _ in range(steps):
+        h0 = _time.perf_counter()
+        plan.append([1] * B)
+        host_ms.append((_time.perf_counter() - h0) * 1e3)
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record(stream)
+        sp.append(plan, -1, kn, vn, bufs["table"], bufs["k_pool"], bufs["v_pool"])
+        e1.record(stream)
+        sp.decode(plan, -1, q, bufs["table"], bufs["k_pool"], bufs["v_pool"], scale, o,
+                  workspace=bufs["workspace"])
+        e2.record(stream)
+        app_ev.append((e0, e1))
+        dec_ev.append((e1, e2))
+        kv_bytes.append(plan.stats(-1)["decode_tokens"] * 2 * D * 2)
+    torch.cuda.synchronize()
+    wall = (_time.perf_counter() - t0) * 1e3 / steps
+    app_ms = float(np.median([a.elapsed_time(b) for a, b in app_ev]))
+    dec_ms = float(np.median([a.elapsed_time(b) for a, b in dec_ev]))
+    gbs = float(np.median(kv_bytes)) / (dec_ms * 1e-3) / 1e9
+    log(f"decode loop: step {wall:.3f} ms wall (host plan {np.median(host_ms):.3f} ms, "
+        f"append {app_ms:.3f} ms, decode {dec_ms:.3f} ms = {gbs:.0f} GB/s)")
+    del plan, bufs, q, o, kn, vn
+    torch.cuda.empty_cache()
+    return {"workload": "llama70b-shaped decode 8 x 32768 x 80 layers, one token per sequence "
+                        "per step, 32 steps, cache planned once with append capacity 64",
+            "steps": steps, "ms_per_step_wall": round(wall, 4),
+            "host_plan_append_ms": round(float(np.median(host_ms)), 4),
+            "append_kernel_ms": round(app_ms, 4), "decode_ms": round(dec_ms, 4),
+            "decode_kv_gbs": round(gbs, 1),
+            "tokens_per_s": round(B / (wall * 1e-3), 1)}
 
 
 def decode_form_build(torch, W, sp, dev, timed, log):

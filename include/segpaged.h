@@ -85,7 +85,7 @@ typedef struct {
   int64_t capacity_pages;       /* pages of the pool the caller provides; 0 = exactly the pages needed.
                                    Every page id must be < capacity. */
   int32_t decode_split_tokens;  /* keys per decode work item, a multiple of 64; 0 = automatic */
-  int32_t reserved;
+  int32_t append_capacity;      /* tokens each sequence may gain after planning (decode form only); 0 = none */
 } segpaged_spec;
 
 /* Sizes the caller allocates. */
@@ -128,6 +128,12 @@ typedef struct segpaged_plan segpaged_plan;  /* opaque, host heap */
  * per-head varlen work lists of the prefill and decode kernels [RT section 4].
  * Host only: makes no HIP call, so it runs without a GPU. The layout is built
  * once here and reused by every call [RT section 5].
+ * append_capacity > 0 (every sequence in decode form, q0_b = max(N_b - 1, 0))
+ * plans for a decode loop: global heads reserve the pages of N_b +
+ * append_capacity; local heads keep two segments, the sink (ceil(sink/P) pages
+ * reserved) and the window [max(sink, N_b - W), N_b) in a ring of ceil(W/P) + 1
+ * pages; the work-list regions and the decode workspace are sized for the
+ * largest lengths (see segpaged_plan_append).
  * Returns EINVAL for a bad spec, EUNSUPPORTED for an unsupported D/P/group,
  * ENOSPACE when the free list or capacity is too small. *plan is NULL on error. */
 SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan** plan,
@@ -195,6 +201,34 @@ SEGPAGED_API int segpaged_prefill(const segpaged_plan* plan, int32_t layer, cons
                                   int32_t* d_table, const void* k_pool,
                                   const void* v_pool, float scale, void* o, float* lse,
                                   void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Decode-loop growth, host side (the layout is written once, when K/V is
+ * written, and then only extended [RT section 5]): every sequence b gains
+ * n_new[b] >= 0 tokens, N_b += n_new[b], q0_b = N_b - 1. Only for plans made
+ * with append_capacity > 0 (ESTATE otherwise); ENOSPACE if a sequence would pass
+ * its planned length plus append_capacity, EINVAL for a negative count. Updates
+ * the plan's image: sequence rows; unit records (a global head's segment grows
+ * into its reserved pages; a local head keeps its sink and the window positions
+ * [p0, N) in a ring of ceil(W/P) + 1 pages: when the window outgrows the ring,
+ * p0 moves on by P and the id of the page that held the oldest positions moves
+ * to the end of the ring); the work lists; and the append list the next
+ * segpaged_append reads. Sizes (table_int32s, pools, workspace) do not change.
+ * No HIP call. */
+SEGPAGED_API int segpaged_plan_append(segpaged_plan* plan, const int32_t* n_new);
+
+/* Decode-loop growth, device side: write the K/V of the tokens the last
+ * segpaged_plan_append added into their pages; the first call after it also
+ * uploads the changed parts of the image (all layers) into d_table.
+ *   k_new, v_new  device bf16 [T_new][Hkv][D] of this layer, T_new = sum of
+ *                 n_new, rows packed in sequence order ([L][T_new][Hkv][D] when
+ *                 layer = -1); may be NULL when T_new = 0
+ *   d_table, k_pool, v_pool  as built by segpaged_build for this plan
+ * Retrieval heads store nothing (their index set is given). Call it for a layer
+ * before that layer's decode, on the stream the decode uses. ESTATE for a plan
+ * without append capacity or a layer out of range. */
+SEGPAGED_API int segpaged_append(segpaged_plan* plan, int32_t layer, const void* k_new,
+                                 const void* v_new, int32_t* d_table, void* k_pool,
+                                 void* v_pool, void* stream);
 
 /* Split-K decode [RT section 4; KV section 10.2]: the query at position N_b - 1 of
  * each sequence attends to every key it can see. Work items are (unit, key

@@ -132,6 +132,56 @@ __global__ __launch_bounds__(256) void build_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// append: the K/V of tokens added to the sequences since planning go to their
+// slots, the layout fixed when K/V is written [runtime explainer, section 5].
+// One wave per (layer, new row, KV head). A global head's token at position p
+// sits at slot p; a local head's at slot p in the sink, or in the window
+// segment, whose positions [p0, N) the plan keeps in a ring of pages; tokens
+// already outside it, and retrieval heads (a given index set), store nothing.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void append_kernel(
+    const int32_t* __restrict__ tab, int32_t off_units, int32_t off_pages, int32_t off_app,
+    int32_t B, int32_t Hkv, int32_t layer0, int32_t nl, int32_t t_new,
+    const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn, int64_t new_layer_stride,
+    uint16_t* __restrict__ kp, uint16_t* __restrict__ vp, int32_t P, int32_t log2P) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t idx = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t per_layer = (int64_t)t_new * Hkv;
+  if (idx >= per_layer * nl) return;
+  const int32_t li = (int32_t)(idx / per_layer);
+  const int32_t t = (int32_t)((idx % per_layer) / Hkv), h = (int32_t)(idx % Hkv);
+  const int32_t l = layer0 + li;
+  // sequence b owns new rows [app[b], app[b+1]); its first new position is app[B+1+b]
+  const int32_t* app = tab + off_app;
+  int32_t b = 0;
+  while (b + 1 < B && app[b + 1] <= t) ++b;
+  const int32_t p = app[B + 1 + b] + (t - app[b]);
+  const int32_t* ur = tab + off_units + kUnitInts * ((l * B + b) * Hkv + h);
+  int32_t slot = -1;
+  if (ur[U_KIND] == SEGPAGED_GLOBAL) {
+    slot = p;
+  } else if (ur[U_KIND] == SEGPAGED_LOCAL) {
+    if (p < ur[U_SINK]) {
+      slot = p;
+    } else if (p >= ur[U_S1POS]) {
+      slot = (((ur[U_S0LEN] + P - 1) >> log2P) << log2P) + (p - ur[U_S1POS]);
+    }
+  }
+  if (slot < 0) return;
+  const int32_t pid = tab[off_pages + ur[U_PAGEOFF] + (slot >> log2P)];
+  const int32_t ts = slot & (P - 1);
+  const int64_t src = (int64_t)li * new_layer_stride + ((int64_t)t * Hkv + h) * D;
+  uint16_t* kpage = kp + (int64_t)pid * P * D;
+  uint16_t* vpage = vp + (int64_t)pid * P * D;
+  // K page [D/8][P][8]: the token's 16-byte chunks; V page [P/8][D][8]: one
+  // element of each dim's 8-slot brick
+  if (lane < D / 8) st16(kpage + ((int64_t)lane * P + ts) * 8, ld16(kn + src + lane * 8));
+  for (int d = lane; d < D; d += 64)
+    vpage[((int64_t)(ts >> 3) * D + d) * 8 + (ts & 7)] = vn[src + d];
+}
+
+// ---------------------------------------------------------------------------
 // decode, split-K. One wave per work item (unit, slots [lo, hi)), all of which
 // the decode row sees. Per 32-key step, with v_mfma_f32_16x16x32_bf16:
 //   S^T[16 keys][16 cols] = K[keys][D] . Q^T[D][cols]   (cols = the G query heads)
@@ -1285,6 +1335,55 @@ SEGPAGED_API int segpaged_build(const segpaged_plan* pl, int32_t layer, const vo
                        (int32_t)pl->off_units, (int32_t)pl->off_pages, (int32_t)pl->off_retr,
                        (int32_t)sp.unit_b, (int32_t)sp.unit_e, (int32_t)sp.page_b, pl->Hkv, pl->P,
                        pl->log2P, kd, vd, dstride, kpp, vpp);
+  return check_launch();
+}
+
+SEGPAGED_API int segpaged_append(segpaged_plan* pl, int32_t layer, const void* k_new,
+                                 const void* v_new, int32_t* d_table, void* k_pool, void* v_pool,
+                                 void* stream) {
+  if (!pl || !d_table || !k_pool || !v_pool) return SEGPAGED_EINVAL;
+  if (pl->append_cap <= 0) return SEGPAGED_ESTATE;
+  if (layer < -1 || layer >= pl->L) return SEGPAGED_ESTATE;
+  const int64_t B = pl->B, Hkv = pl->Hkv;
+  const int32_t t_new = pl->buf[pl->off_app + B];
+  if (t_new > 0 && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)))
+    return SEGPAGED_EINVAL;
+  if (!aligned4(d_table) || !aligned16(k_pool) || !aligned16(v_pool)) return SEGPAGED_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  int rc;
+  if (pl->app_upload) {  // what the last segpaged_plan_append changed, all layers
+    if ((rc = upload(pl, d_table, pl->off_seqs, kSeqInts * B, st))) return rc;
+    if ((rc = upload(pl, d_table, pl->off_units, kUnitInts * pl->num_units, st))) return rc;
+    for (int32_t l = 0; l < pl->L; ++l) {
+      if (!pl->pages_dirty[l]) continue;
+      const LayerRange& r = pl->layers[l];
+      if ((rc = upload(pl, d_table, pl->off_pages + r.page_b, r.page_e - r.page_b, st))) return rc;
+      pl->pages_dirty[l] = 0;
+    }
+    if ((rc = upload(pl, d_table, pl->off_decunits,
+                     pl->off_pre + kPreItemInts * pl->pre_cap - pl->off_decunits, st)))
+      return rc;
+    if ((rc = upload(pl, d_table, pl->off_app, 2 * B + 1, st))) return rc;
+    pl->app_upload = false;
+  }
+  if (t_new == 0) return SEGPAGED_OK;
+  const int32_t nl = layer < 0 ? pl->L : 1;
+  const int64_t waves = (int64_t)nl * t_new * Hkv;
+  const int64_t lstride = layer < 0 ? (int64_t)t_new * Hkv * pl->D : 0;
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  auto* kn = (const uint16_t*)k_new;
+  auto* vn = (const uint16_t*)v_new;
+  auto* kpp = (uint16_t*)k_pool;
+  auto* vpp = (uint16_t*)v_pool;
+  const int32_t l0 = layer < 0 ? 0 : layer;
+  if (pl->D == 128)
+    hipLaunchKernelGGL(append_kernel<128>, grid, block, 0, st, d_table, (int32_t)pl->off_units,
+                       (int32_t)pl->off_pages, (int32_t)pl->off_app, (int32_t)B, (int32_t)Hkv, l0,
+                       nl, t_new, kn, vn, lstride, kpp, vpp, pl->P, pl->log2P);
+  else
+    hipLaunchKernelGGL(append_kernel<64>, grid, block, 0, st, d_table, (int32_t)pl->off_units,
+                       (int32_t)pl->off_pages, (int32_t)pl->off_app, (int32_t)B, (int32_t)Hkv, l0,
+                       nl, t_new, kn, vn, lstride, kpp, vpp, pl->P, pl->log2P);
   return check_launch();
 }
 

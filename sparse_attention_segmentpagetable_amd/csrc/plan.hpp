@@ -53,4 +53,11 @@ struct segpaged_plan {
   std::vector<segpaged::LayerRange> layers;  // per-layer slices of buf
   std::vector<segpaged_stats> stats;         // per-layer work counts
   segpaged_stats total{};
+  // append mode (spec.append_capacity > 0): sequences grow after planning
+  int64_t append_cap = 0;                    // tokens each sequence may gain
+  std::vector<int64_t> n_max;                // per sequence: length limit
+  int64_t dec_cap = 0, pre_cap = 0;          // work-list capacities (items)
+  int64_t off_app = 0;                       // append list: row offsets [B+1], first positions [B]
+  bool app_upload = false;                   // image changed since the last segpaged_append
+  std::vector<uint8_t> pages_dirty;          // per layer: a page list rotated
 };

@@ -130,6 +130,153 @@ int64_t tile_cost(int kind, int64_t sink, int64_t window, int64_t r0, int64_t r1
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// Sequence rows from lengths and first query positions (dense K/V rows and Q
+// rows are packed in sequence order).
+void write_seq_rows(segpaged_plan* pl, const int32_t* n, const int32_t* q0) {
+  int64_t kvo = 0, qo = 0;
+  for (int64_t b = 0; b < pl->B; ++b) {
+    int32_t* r = &pl->buf[pl->off_seqs + kSeqInts * b];
+    r[S_N] = n[b]; r[S_Q0] = q0[b];
+    r[S_KVOFF] = (int32_t)kvo; r[S_QOFF] = (int32_t)qo;
+    kvo += n[b];
+    qo += n[b] - q0[b];
+  }
+  pl->kv_rows = kvo;
+  pl->q_rows = qo;
+}
+
+// The per-head varlen work lists of the kernels [runtime explainer, section 4],
+// derived from the unit records of the image alone: per layer, the decode items
+// (slot ranges of the keys row N-1 sees, cut into <= split keys) with each unit's
+// item range, and the prefill tiles heaviest-first; plus the per-layer work
+// counts (pages excepted).
+struct WorkLists {
+  std::vector<int32_t> decunits, dec, pre;
+  std::vector<LayerRange> ranges;
+  std::vector<segpaged_stats> stats;
+  int64_t n_dec() const { return (int64_t)dec.size() / kDecItemInts; }
+  int64_t n_pre() const { return (int64_t)pre.size() / kPreItemInts; }
+};
+
+void make_work_lists(const segpaged_plan* pl, WorkLists& wl) {
+  const int32_t* t = pl->buf.data();
+  const int64_t B = pl->B, L = pl->L, Hkv = pl->Hkv, P = pl->P, U = pl->num_units;
+  const int64_t split = pl->split, BQ = kPrefillRows / pl->G;
+  wl.decunits.assign(2 * U, 0);
+  wl.dec.clear();
+  wl.pre.clear();
+  wl.ranges.assign(L, LayerRange{});
+  wl.stats.assign(L, segpaged_stats{});
+  for (int64_t l = 0; l < L; ++l) {
+    LayerRange& lr = wl.ranges[l];
+    segpaged_stats& st = wl.stats[l];
+    lr.dec_b = wl.n_dec();
+    lr.pre_b = wl.n_pre();
+    lr.max_unit_items = 0;
+    struct PreTile { int64_t cost, unit, r0; };
+    std::vector<PreTile> tiles;
+    for (int64_t u = l * B * Hkv; u < (l + 1) * B * Hkv; ++u) {
+      const int32_t* r = t + pl->off_units + kUnitInts * u;
+      const int eff = r[U_KIND];
+      const int64_t n = r[U_N], q0 = r[U_Q0], sink = r[U_SINK], win = r[U_WIN];
+      const int ns = r[U_NSEG];
+      Seg sg[2] = {{0, 0}, {0, 0}};
+      for (int k = 0; k < ns; ++k) sg[k] = {r[U_S0POS + 2 * k], r[U_S0LEN + 2 * k]};
+      const int32_t* rpos = r[U_RETROFF] >= 0 ? t + pl->off_retr + r[U_RETROFF] : nullptr;
+      const int64_t rl = rpos && ns > 0 ? sg[0].len : 0;
+
+      st.units += 1;
+      st.retained_tokens += r[U_KVLEN];
+      st.q_rows += n - q0;
+      if (eff == SEGPAGED_GLOBAL) {
+        st.prefill_pairs += pairs_global(n, q0);
+      } else if (eff == SEGPAGED_LOCAL) {
+        st.prefill_pairs += pairs_local(n, q0, sink, win);
+      } else {
+        st.prefill_pairs += pairs_retrieval(n, q0, rpos, rl);
+      }
+
+      // decode items: visible slot ranges of row n - 1, cut into <= split keys
+      int32_t* du = &wl.decunits[2 * u];
+      du[0] = (int32_t)wl.n_dec();
+      SlotRange rr[4];
+      const int nr = decode_ranges(eff, sink, win, n, sg, ns, P, rr);
+      for (int k = 0; k < nr; ++k) st.decode_tokens += rr[k].hi - rr[k].lo;
+      int k0 = 0;
+      if (nr == 2 && rr[1].lo == ceil_div(rr[0].hi, P) * P && rr[0].hi < rr[1].lo &&
+          rr[0].hi - rr[0].lo <= split) {
+        // a short first range (a sink) and a range starting on the next page: one
+        // item covers both, the zero tail of the first range's last page is a gap
+        const int64_t hi0 = std::min(rr[1].lo + split, rr[1].hi);
+        wl.dec.push_back((int32_t)u);
+        wl.dec.push_back((int32_t)rr[0].lo);
+        wl.dec.push_back((int32_t)hi0);
+        wl.dec.push_back((int32_t)rr[0].hi);
+        rr[1].lo = hi0;
+        k0 = 1;
+      }
+      for (int k = k0; k < nr; ++k) {
+        for (int64_t lo = rr[k].lo; lo < rr[k].hi; lo += split) {
+          wl.dec.push_back((int32_t)u);
+          wl.dec.push_back((int32_t)lo);
+          wl.dec.push_back((int32_t)std::min(lo + split, rr[k].hi));
+          wl.dec.push_back(0);
+        }
+      }
+      du[1] = (int32_t)wl.n_dec();
+      lr.max_unit_items = std::max<int64_t>(lr.max_unit_items, du[1] - du[0]);
+
+      // prefill tiles
+      for (int64_t r0 = q0; r0 < n; r0 += BQ) {
+        const int64_t r1 = std::min(n, r0 + BQ);
+        tiles.push_back({tile_cost(eff, sink, win, r0, r1, sg, ns, rpos), u, r0});
+      }
+    }
+    std::stable_sort(tiles.begin(), tiles.end(),
+                     [](const PreTile& a, const PreTile& b) { return a.cost > b.cost; });
+    for (const PreTile& tl : tiles) {
+      wl.pre.push_back((int32_t)tl.unit);
+      wl.pre.push_back((int32_t)tl.r0);
+    }
+    lr.dec_e = wl.n_dec();
+    lr.pre_e = wl.n_pre();
+    st.decode_items = lr.dec_e - lr.dec_b;
+    st.prefill_items = lr.pre_e - lr.pre_b;
+  }
+}
+
+// Work lists into the image (unused capacity zeroed) and the plan's ranges and counts.
+void store_work_lists(segpaged_plan* pl, const WorkLists& wl) {
+  std::vector<int32_t>& t = pl->buf;
+  std::copy(wl.decunits.begin(), wl.decunits.end(), t.begin() + pl->off_decunits);
+  std::copy(wl.dec.begin(), wl.dec.end(), t.begin() + pl->off_dec);
+  std::fill(t.begin() + pl->off_dec + wl.dec.size(),
+            t.begin() + pl->off_dec + kDecItemInts * pl->dec_cap, 0);
+  std::copy(wl.pre.begin(), wl.pre.end(), t.begin() + pl->off_pre);
+  std::fill(t.begin() + pl->off_pre + wl.pre.size(),
+            t.begin() + pl->off_pre + kPreItemInts * pl->pre_cap, 0);
+  pl->n_dec = wl.n_dec();
+  pl->n_pre = wl.n_pre();
+  pl->max_unit_items = 0;
+  segpaged_stats& tot = pl->total;
+  tot = segpaged_stats{};
+  for (int64_t l = 0; l < pl->L; ++l) {
+    LayerRange& lr = pl->layers[l];
+    lr.dec_b = wl.ranges[l].dec_b; lr.dec_e = wl.ranges[l].dec_e;
+    lr.pre_b = wl.ranges[l].pre_b; lr.pre_e = wl.ranges[l].pre_e;
+    lr.max_unit_items = wl.ranges[l].max_unit_items;
+    pl->max_unit_items = std::max(pl->max_unit_items, lr.max_unit_items);
+    const int64_t pages = pl->stats[l].pages;
+    segpaged_stats& st = pl->stats[l];
+    st = wl.stats[l];
+    st.pages = pages;
+    tot.units += st.units; tot.pages += st.pages; tot.retained_tokens += st.retained_tokens;
+    tot.decode_tokens += st.decode_tokens; tot.prefill_pairs += st.prefill_pairs;
+    tot.q_rows += st.q_rows; tot.decode_items += st.decode_items;
+    tot.prefill_items += st.prefill_items;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -151,6 +298,7 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
   if (!s.seq_len || !s.first_query_pos || !s.kind || !s.sink || !s.window) return SEGPAGED_EINVAL;
   if (s.decode_split_tokens < 0 || s.decode_split_tokens % 64 != 0) return SEGPAGED_EINVAL;
   if (s.capacity_pages < 0 || s.free_list_len < 0) return SEGPAGED_EINVAL;
+  if (s.append_capacity < 0) return SEGPAGED_EINVAL;
 
   const int64_t B = s.num_seqs, L = s.num_layers, Hkv = s.num_kv_heads, P = s.page_size;
   const int64_t U = L * B * Hkv;
@@ -165,6 +313,12 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
     q_rows += n - q0;
   }
   if (kv_rows > kI32Max || q_rows > kI32Max) return SEGPAGED_EINVAL;
+  if (s.append_capacity > 0) {
+    // growth is for the decode loop: every sequence in decode form
+    if (kv_rows + (int64_t)s.append_capacity * B > kI32Max) return SEGPAGED_EINVAL;
+    for (int64_t b = 0; b < B; ++b)
+      if (s.first_query_pos[b] != std::max(s.seq_len[b] - 1, 0)) return SEGPAGED_EINVAL;
+  }
 
   bool any_retr = false;
   for (int64_t i = 0; i < L * Hkv; ++i) {
@@ -202,23 +356,49 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
   pl->log2P = 0;
   while ((1 << pl->log2P) < P) ++pl->log2P;
   pl->num_units = U; pl->q_rows = q_rows; pl->kv_rows = kv_rows;
+  pl->append_cap = s.append_capacity;
+  if (pl->append_cap > 0) {
+    pl->n_max.resize(B);
+    for (int64_t b = 0; b < B; ++b) pl->n_max[b] = (int64_t)s.seq_len[b] + pl->append_cap;
+  }
 
-  // ---- pass 1: segments per unit, page counts, retrieval totals
+  // ---- pass 1: segments per unit, reserved pages, retrieval totals
+  // Append mode keeps room to grow: a global head reserves the pages of its
+  // length limit; a local head always has two segments, the sink (its pages
+  // reserved) and the window, whose pages form a ring of ceil(W/P) + 1.
+  const bool grow = pl->append_cap > 0;
   std::vector<Seg> segs(U * 2);
   std::vector<int> nseg(U);
+  std::vector<int64_t> res_pages(U);
   int64_t num_pages = 0, num_retr = 0;
   for (int64_t l = 0; l < L; ++l)
     for (int64_t b = 0; b < B; ++b)
       for (int64_t h = 0; h < Hkv; ++h) {
         const int64_t u = (l * B + b) * Hkv + h, c = l * Hkv + h;
         const int64_t rl = s.retr_offsets ? s.retr_offsets[u + 1] - s.retr_offsets[u] : 0;
-        nseg[u] = retained(s.kind[c], s.sink[c], s.window[c], s.seq_len[b],
-                           s.first_query_pos[b], rl, &segs[2 * u]);
-        for (int k = 0; k < nseg[u]; ++k) {
-          if (segs[2 * u + k].len > kI32Max / 2) { delete pl; return SEGPAGED_EINVAL; }
-          num_pages += ceil_div(segs[2 * u + k].len, P);
+        const int64_t n = s.seq_len[b];
+        const int kind = s.kind[c];
+        if (grow && kind == SEGPAGED_LOCAL) {
+          const int64_t a = std::min<int64_t>(s.sink[c], n);
+          const int64_t w0 = std::max<int64_t>(s.sink[c], n - s.window[c]);
+          segs[2 * u] = {0, a};
+          segs[2 * u + 1] = {w0, std::max<int64_t>(n - w0, 0)};
+          nseg[u] = 2;
+          res_pages[u] = ceil_div(s.sink[c], P) + ceil_div(s.window[c], P) + 1;
+        } else if (grow && kind != SEGPAGED_RETRIEVAL) {
+          segs[2 * u] = {0, n};
+          nseg[u] = 1;
+          res_pages[u] = ceil_div(n + pl->append_cap, P);
+        } else {
+          nseg[u] = retained(kind, s.sink[c], s.window[c], n, s.first_query_pos[b], rl,
+                             &segs[2 * u]);
+          res_pages[u] = 0;
+          for (int k = 0; k < nseg[u]; ++k) res_pages[u] += ceil_div(segs[2 * u + k].len, P);
         }
-        if (s.kind[c] == SEGPAGED_RETRIEVAL) num_retr += rl;
+        for (int k = 0; k < nseg[u]; ++k)
+          if (segs[2 * u + k].len > kI32Max / 2) { delete pl; return SEGPAGED_EINVAL; }
+        num_pages += res_pages[u];
+        if (kind == SEGPAGED_RETRIEVAL) num_retr += rl;
       }
   if (num_pages > kI32Max || num_retr > kI32Max) { delete pl; return SEGPAGED_EINVAL; }
 
@@ -262,7 +442,7 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
   pl->split = (int32_t)split;
 
   std::vector<int32_t>& t = pl->buf;
-  t.assign(pl->table_len + 2 * U, 0);
+  t.assign(pl->table_len, 0);
   pl->off_decunits = pl->table_len;
 
   // header and sequences
@@ -272,51 +452,33 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
                                     (int32_t)pl->off_units, (int32_t)pl->off_pages,
                                     (int32_t)pl->off_retr, (int32_t)pl->table_len};
   std::memcpy(t.data(), hdr, sizeof(hdr));
-  {
-    int64_t kvo = 0, qo = 0;
-    for (int64_t b = 0; b < B; ++b) {
-      int32_t* r = &t[pl->off_seqs + kSeqInts * b];
-      r[S_N] = s.seq_len[b]; r[S_Q0] = s.first_query_pos[b];
-      r[S_KVOFF] = (int32_t)kvo; r[S_QOFF] = (int32_t)qo;
-      kvo += s.seq_len[b];
-      qo += s.seq_len[b] - s.first_query_pos[b];
-    }
-  }
+  write_seq_rows(pl, s.seq_len, s.first_query_pos);
 
-  // ---- pass 2: unit records, page ids, retrieval positions, work lists, stats
-  std::vector<int32_t> dec_items, pre_items;
+  // ---- pass 2: unit records, page ids, retrieval positions
   pl->layers.resize(L);
   pl->stats.assign(L, segpaged_stats{});
   int64_t page_cursor = 0, retr_cursor = 0;
-  const int64_t BQ = kPrefillRows / G;
+  int64_t dec_cap = 0;
   for (int64_t l = 0; l < L; ++l) {
     LayerRange& lr = pl->layers[l];
-    segpaged_stats& st = pl->stats[l];
     lr.unit_b = l * B * Hkv; lr.unit_e = (l + 1) * B * Hkv;
     lr.page_b = page_cursor; lr.retr_b = retr_cursor;
-    lr.dec_b = (int64_t)dec_items.size() / kDecItemInts;
-    lr.pre_b = (int64_t)pre_items.size() / kPreItemInts;
-    lr.max_unit_items = 0;
-    struct PreTile { int64_t cost, unit, r0; };
-    std::vector<PreTile> tiles;
     for (int64_t b = 0; b < B; ++b)
       for (int64_t h = 0; h < Hkv; ++h) {
         const int64_t u = (l * B + b) * Hkv + h, c = l * Hkv + h;
         const int kind = s.kind[c];
         const int eff = kind == SEGPAGED_DENSE ? SEGPAGED_GLOBAL : kind;
-        const int64_t n = s.seq_len[b], q0 = s.first_query_pos[b];
         int32_t* r = &t[pl->off_units + kUnitInts * u];
         r[U_KIND] = eff; r[U_B] = (int32_t)b; r[U_L] = (int32_t)l; r[U_H] = (int32_t)h;
-        r[U_N] = (int32_t)n; r[U_Q0] = (int32_t)q0; r[U_SINK] = s.sink[c]; r[U_WIN] = s.window[c];
+        r[U_N] = s.seq_len[b]; r[U_Q0] = s.first_query_pos[b];
+        r[U_SINK] = s.sink[c]; r[U_WIN] = s.window[c];
         r[U_NSEG] = nseg[u];
         r[U_PAGEOFF] = (int32_t)page_cursor;
         r[U_RETROFF] = -1;
-        const int32_t* rpos = nullptr;
-        int64_t rl = 0;
         if (kind == SEGPAGED_RETRIEVAL) {
           r[U_RETROFF] = (int32_t)retr_cursor;
-          rl = s.retr_offsets[u + 1] - s.retr_offsets[u];
-          rpos = s.retr_pos + s.retr_offsets[u];
+          const int64_t rl = s.retr_offsets[u + 1] - s.retr_offsets[u];
+          const int32_t* rpos = s.retr_pos + s.retr_offsets[u];
           std::copy(rpos, rpos + rl, t.begin() + pl->off_retr + retr_cursor);
           retr_cursor += rl;
         }
@@ -326,96 +488,37 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
           r[U_S0POS + 2 * k] = (int32_t)sg.pos0;
           r[U_S0LEN + 2 * k] = (int32_t)sg.len;
           kv_len += sg.len;
-          const int64_t np = ceil_div(sg.len, P);
-          for (int64_t p = 0; p < np; ++p, ++page_cursor)
-            t[pl->off_pages + page_cursor] = s.free_list ? s.free_list[page_cursor]
-                                                          : (int32_t)page_cursor;
         }
         r[U_KVLEN] = (int32_t)kv_len;
-
-        // stats
-        st.units += 1;
-        st.retained_tokens += kv_len;
-        st.q_rows += n - q0;
-        if (eff == SEGPAGED_GLOBAL) {
-          st.prefill_pairs += pairs_global(n, q0);
-        } else if (eff == SEGPAGED_LOCAL) {
-          st.prefill_pairs += pairs_local(n, q0, s.sink[c], s.window[c]);
-        } else {
-          st.prefill_pairs += pairs_retrieval(n, q0, rpos, rl);
-        }
-
-        // decode items: visible slot ranges of row n - 1, cut into <= split keys
-        int32_t* du = &t[pl->off_decunits + 2 * u];
-        du[0] = (int32_t)(dec_items.size() / kDecItemInts);
-        SlotRange rr[4];
-        const int nr = decode_ranges(kind, s.sink[c], s.window[c], n, &segs[2 * u], nseg[u], P, rr);
-        for (int k = 0; k < nr; ++k) st.decode_tokens += rr[k].hi - rr[k].lo;
-        int k0 = 0;
-        if (nr == 2 && rr[1].lo == ceil_div(rr[0].hi, P) * P && rr[0].hi < rr[1].lo &&
-            rr[0].hi - rr[0].lo <= split) {
-          // a short first range (a sink) and a range starting on the next page: one
-          // item covers both, the zero tail of the first range's last page is a gap
-          const int64_t hi0 = std::min(rr[1].lo + split, rr[1].hi);
-          dec_items.push_back((int32_t)u);
-          dec_items.push_back((int32_t)rr[0].lo);
-          dec_items.push_back((int32_t)hi0);
-          dec_items.push_back((int32_t)rr[0].hi);
-          rr[1].lo = hi0;
-          k0 = 1;
-        }
-        for (int k = k0; k < nr; ++k) {
-          for (int64_t lo = rr[k].lo; lo < rr[k].hi; lo += split) {
-            dec_items.push_back((int32_t)u);
-            dec_items.push_back((int32_t)lo);
-            dec_items.push_back((int32_t)std::min(lo + split, rr[k].hi));
-            dec_items.push_back(0);
-          }
-        }
-        du[1] = (int32_t)(dec_items.size() / kDecItemInts);
-        lr.max_unit_items = std::max<int64_t>(lr.max_unit_items, du[1] - du[0]);
-
-        // prefill tiles
-        for (int64_t r0 = q0; r0 < n; r0 += BQ) {
-          const int64_t r1 = std::min(n, r0 + BQ);
-          tiles.push_back({tile_cost(eff, s.sink[c], s.window[c], r0, r1, &segs[2 * u], nseg[u],
-                                     rpos),
-                           u, r0});
+        for (int64_t p = 0; p < res_pages[u]; ++p, ++page_cursor)
+          t[pl->off_pages + page_cursor] = s.free_list ? s.free_list[page_cursor]
+                                                        : (int32_t)page_cursor;
+        if (grow) {  // most decode items this unit can ever need
+          if (eff == SEGPAGED_LOCAL)
+            dec_cap += ceil_div(s.sink[c], split) + ceil_div(s.window[c], split) + 2;
+          else
+            dec_cap += ceil_div(segs[2 * u].len + pl->append_cap, split) + 1;
         }
       }
-    std::stable_sort(tiles.begin(), tiles.end(),
-                     [](const PreTile& a, const PreTile& b) { return a.cost > b.cost; });
-    for (const PreTile& tl : tiles) {
-      pre_items.push_back((int32_t)tl.unit);
-      pre_items.push_back((int32_t)tl.r0);
-    }
     lr.page_e = page_cursor; lr.retr_e = retr_cursor;
-    lr.dec_e = (int64_t)dec_items.size() / kDecItemInts;
-    lr.pre_e = (int64_t)pre_items.size() / kPreItemInts;
-    st.pages = lr.page_e - lr.page_b;
-    st.decode_items = lr.dec_e - lr.dec_b;
-    st.prefill_items = lr.pre_e - lr.pre_b;
-    pl->max_unit_items = std::max(pl->max_unit_items, lr.max_unit_items);
+    pl->stats[l].pages = lr.page_e - lr.page_b;
   }
-  pl->n_dec = (int64_t)dec_items.size() / kDecItemInts;
-  pl->n_pre = (int64_t)pre_items.size() / kPreItemInts;
-  pl->off_dec = pl->off_decunits + 2 * U;
-  pl->off_pre = pl->off_dec + (int64_t)dec_items.size();
-  pl->off_ctr = pl->off_pre + (int64_t)pre_items.size();
-  pl->total_ints = pl->off_ctr + (int64_t)kCtrInts * (L + 1);
-  if (pl->total_ints > kI32Max) { delete pl; return SEGPAGED_EINVAL; }
-  t.insert(t.end(), dec_items.begin(), dec_items.end());
-  t.insert(t.end(), pre_items.begin(), pre_items.end());
-  t.resize(pl->total_ints, 0);  // prefill work counters, zero between calls
 
-  segpaged_stats& tot = pl->total;
-  tot = segpaged_stats{};
-  for (const segpaged_stats& st : pl->stats) {
-    tot.units += st.units; tot.pages += st.pages; tot.retained_tokens += st.retained_tokens;
-    tot.decode_tokens += st.decode_tokens; tot.prefill_pairs += st.prefill_pairs;
-    tot.q_rows += st.q_rows; tot.decode_items += st.decode_items;
-    tot.prefill_items += st.prefill_items;
-  }
+  // ---- work lists after the table: decode units, decode items, prefill items,
+  // then the prefill work counters (and, in append mode, the append list)
+  WorkLists wl;
+  make_work_lists(pl, wl);
+  pl->dec_cap = grow ? std::max<int64_t>(dec_cap, wl.n_dec()) : wl.n_dec();
+  pl->pre_cap = grow ? std::max<int64_t>(U, wl.n_pre()) : wl.n_pre();
+  pl->off_dec = pl->off_decunits + 2 * U;
+  pl->off_pre = pl->off_dec + kDecItemInts * pl->dec_cap;
+  pl->off_ctr = pl->off_pre + kPreItemInts * pl->pre_cap;
+  pl->off_app = pl->off_ctr + (int64_t)kCtrInts * (L + 1);
+  pl->total_ints = pl->off_app + (grow ? 2 * B + 1 : 0);
+  if (pl->total_ints > kI32Max) { delete pl; return SEGPAGED_EINVAL; }
+  t.resize(pl->total_ints, 0);  // work counters and append list start at zero
+  store_work_lists(pl, wl);
+  pl->pages_dirty.assign(L, 0);
   *plan_out = pl;
   if (sizes) segpaged_plan_sizes(pl, sizes);
   return SEGPAGED_OK;
@@ -435,8 +538,69 @@ SEGPAGED_API int segpaged_plan_sizes(const segpaged_plan* pl, segpaged_sizes* z)
   z->kv_rows = pl->kv_rows;
   z->decode_items = pl->n_dec;
   z->prefill_items = pl->n_pre;
-  z->decode_workspace_bytes = pl->n_dec * (int64_t)pl->G * (pl->D + 4) * 4;
+  z->decode_workspace_bytes = pl->dec_cap * (int64_t)pl->G * (pl->D + 4) * 4;
   z->prefill_workspace_bytes = 0;
+  return SEGPAGED_OK;
+}
+
+SEGPAGED_API int segpaged_plan_append(segpaged_plan* pl, const int32_t* n_new) {
+  if (!pl || !n_new) return SEGPAGED_EINVAL;
+  if (pl->append_cap <= 0) return SEGPAGED_ESTATE;
+  std::vector<int32_t>& t = pl->buf;
+  const int64_t B = pl->B, P = pl->P;
+  std::vector<int32_t> n_old(B), n_now(B), q0(B);
+  for (int64_t b = 0; b < B; ++b) {
+    n_old[b] = t[pl->off_seqs + kSeqInts * b + S_N];
+    if (n_new[b] < 0) return SEGPAGED_EINVAL;
+    if (n_old[b] + (int64_t)n_new[b] > pl->n_max[b]) return SEGPAGED_ENOSPACE;
+    n_now[b] = n_old[b] + n_new[b];
+    q0[b] = std::max(n_now[b] - 1, 0);
+  }
+  write_seq_rows(pl, n_now.data(), q0.data());
+  // append list: where each sequence's new K/V rows start, and their positions
+  int32_t* app = &t[pl->off_app];
+  int64_t row = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    app[b] = (int32_t)row;
+    app[B + 1 + b] = n_old[b];
+    row += n_new[b];
+  }
+  app[B] = (int32_t)row;
+  // unit records; a local head's window keeps positions [p0, N): when that
+  // outgrows its ring of pages, p0 moves on by a page and the page that held
+  // the oldest positions becomes the last one
+  for (int64_t u = 0; u < pl->num_units; ++u) {
+    int32_t* r = &t[pl->off_units + kUnitInts * u];
+    const int32_t n = n_now[r[U_B]];
+    r[U_N] = n;
+    r[U_Q0] = q0[r[U_B]];
+    if (r[U_KIND] == SEGPAGED_GLOBAL) {
+      r[U_S0LEN] = n;
+      r[U_KVLEN] = n;
+    } else if (r[U_KIND] == SEGPAGED_LOCAL) {
+      const int64_t sink = r[U_SINK], win = r[U_WIN];
+      const int64_t len0 = std::min<int64_t>(sink, n);
+      const int64_t ring_pages = ceil_div(win, P) + 1;
+      int64_t p0 = r[U_S1POS];
+      int64_t len1 = std::max<int64_t>(n - p0, 0);
+      int32_t* ring = &t[pl->off_pages + r[U_PAGEOFF] + ceil_div(sink, P)];
+      while (len1 > ring_pages * P) {
+        p0 += P;
+        len1 -= P;
+        std::rotate(ring, ring + 1, ring + ring_pages);
+        pl->pages_dirty[r[U_L]] = 1;
+      }
+      r[U_S0LEN] = (int32_t)len0;
+      r[U_S1POS] = (int32_t)p0;
+      r[U_S1LEN] = (int32_t)len1;
+      r[U_KVLEN] = (int32_t)(len0 + len1);
+    }
+  }
+  WorkLists wl;
+  make_work_lists(pl, wl);
+  if (wl.n_dec() > pl->dec_cap || wl.n_pre() > pl->pre_cap) return SEGPAGED_ENOSPACE;
+  store_work_lists(pl, wl);
+  pl->app_upload = true;
   return SEGPAGED_OK;
 }
 

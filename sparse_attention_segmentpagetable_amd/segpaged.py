@@ -37,7 +37,7 @@ class _Spec(ctypes.Structure):
                 ("sink", _i32p), ("window", _i32p), ("retr_offsets", _i64p),
                 ("retr_pos", _i32p), ("free_list", _i32p), ("free_list_len", ctypes.c_int64),
                 ("capacity_pages", ctypes.c_int64), ("decode_split_tokens", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("append_capacity", ctypes.c_int32)]
 
 
 class Sizes(ctypes.Structure):
@@ -77,6 +77,8 @@ def _lib():
         lib.segpaged_plan_table_host.argtypes = [vp, _i32p, ctypes.c_int64]
         lib.segpaged_plan_stats.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(Stats)]
         lib.segpaged_build.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
+        lib.segpaged_plan_append.argtypes = [vp, _i32p]
+        lib.segpaged_append.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
         lib.segpaged_prefill.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_float,
                                          vp, vp, vp, ctypes.c_int64, vp]
         lib.segpaged_decode.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_float,
@@ -110,7 +112,7 @@ class Plan:
     kind, sink, window, retrieval {(b, l, h): positions}, free_list,
     capacity_pages)."""
 
-    def __init__(self, spec, decode_split_tokens: int = 0):
+    def __init__(self, spec, decode_split_tokens: int = 0, append_capacity: int = 0):
         B, L, Hkv = len(spec.seq_len), spec.num_layers, spec.num_kv_heads
         self.num_seqs, self.num_layers = B, L
         self.num_q_heads, self.num_kv_heads = spec.num_q_heads, Hkv
@@ -155,7 +157,7 @@ class Plan:
                   window=keep["window"].ctypes.data_as(_i32p),
                   retr_offsets=ptr_offs, retr_pos=ptr_pos, free_list=ptr_free,
                   free_list_len=fl_len, capacity_pages=int(getattr(spec, "capacity_pages", 0) or 0),
-                  decode_split_tokens=decode_split_tokens, reserved=0)
+                  decode_split_tokens=decode_split_tokens, append_capacity=append_capacity)
         self._h = ctypes.c_void_p()
         self.sizes = Sizes()
         _check(_lib().segpaged_plan_create(ctypes.byref(c), ctypes.byref(self._h),
@@ -170,6 +172,16 @@ class Plan:
         _check(_lib().segpaged_plan_table_host(self._h, out.ctypes.data_as(_i32p), len(out)),
                "segpaged_plan_table_host")
         return out
+
+    def append(self, n_new: Sequence[int]):
+        """segpaged_plan_append: every sequence b gains n_new[b] tokens (host only);
+        then segpaged_append writes their K/V, layer by layer or all at once."""
+        a = _arr32(n_new)
+        if len(a) != self.num_seqs:
+            raise ValueError("n_new needs one count per sequence")
+        _check(_lib().segpaged_plan_append(self._h, a.ctypes.data_as(_i32p)), "segpaged_plan_append")
+        self.t_new = int(a.sum())
+        _check(_lib().segpaged_plan_sizes(self._h, ctypes.byref(self.sizes)), "segpaged_plan_sizes")
 
     def stats(self, layer: int = -1) -> Dict[str, int]:
         st = Stats()
@@ -272,6 +284,24 @@ def prefill(plan: Plan, layer: int, q, table, k_pool, v_pool, scale: float, o, l
                                    _ptr(v_pool, "vp", torch.bfloat16), float(scale),
                                    _ptr(o, "o"), _ptr(lse, "lse"), _ptr(workspace, "ws"), wsb,
                                    _stream(stream)), "segpaged_prefill")
+
+
+def append(plan: Plan, layer: int, k_new, v_new, table, k_pool, v_pool, stream=None):
+    """segpaged_append: K/V of the tokens the last Plan.append added (bf16
+    [T_new][Hkv][D], [L][T_new][Hkv][D] when layer = -1) into their pages."""
+    import torch
+    t_new = getattr(plan, "t_new", 0)
+    nl = plan.num_layers if layer < 0 else 1
+    if t_new > 0:
+        for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+            _ptr(t, nm, torch.bfloat16)
+            _need(t, nl * t_new * plan.num_kv_heads * plan.head_dim, nm)
+    _ptr(table, "table", torch.int32)
+    _need(table, plan.sizes.table_int32s, "table")
+    _check(_lib().segpaged_append(plan.handle, layer, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
+                                  _ptr(table, "t"), _ptr(k_pool, "kp", torch.bfloat16),
+                                  _ptr(v_pool, "vp", torch.bfloat16), _stream(stream)),
+           "segpaged_append")
 
 
 def decode(plan: Plan, layer: int, q, table, k_pool, v_pool, scale: float, o, lse=None,
