@@ -477,7 +477,68 @@ def extra_configs(torch, W, sp, dev, stream, log):
     res["long_prefill_decode_form_build"] = decode_form_build(torch, W, sp, dev, timed, log)
     res["decode_context_sweep"] = decode_context_sweep(torch, W, sp, dev, timed, log)
     res["decode_loop_append"] = decode_loop_append(torch, W, sp, dev, stream, log)
+    res["chunked_prefill"] = chunked_prefill(torch, W, sp, dev, stream, log)
     return res
+
+
+def chunked_prefill(torch, W, sp, dev, stream, log):
+    """The long-prefill workload (131072 tokens, 2 layers) taken in 8 chunks of
+    16384 over a cache planned for growth: local heads hold their sink and a ring
+    of ceil((8192 + 16384 - 1)/64) + 1 pages instead of the whole prompt. Per
+    chunk: segpaged_plan_append, segpaged_append of the chunk's K/V, then the
+    chunk's prefill rows per layer. Reports prefill TFLOP/s over all chunks, the
+    append time, and the pool bytes against the one-shot (prefill-form) plan."""
+    from dataclasses import replace as _replace
+    N, chunk, L = 131072, 16384, 2
+    full = W.long_prefill(num_layers=L, n=N)
+    Hq, Hkv, D = full.num_q_heads, full.num_kv_heads, full.head_dim
+    spec = _replace(full, seq_len=[chunk], first_query_pos=[0])
+    plan = sp.Plan(spec, append_capacity=N - chunk, append_chunk=chunk)
+    one_shot_pool = sp.Plan(full).sizes.pool_bytes
+    bufs = plan.allocate(dev, workspace=False)
+    k = W.randn_bf16_device((N, Hkv, D), full.seed, W.TAG_K, 0, dev)
+    v = W.randn_bf16_device((N, Hkv, D), full.seed, W.TAG_V, 0, dev)
+    q = W.randn_bf16_device((N, Hq, D), full.seed, W.TAG_Q, 0, dev)
+    o = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(D)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for l in range(L):
+        sp.build(plan, l, k[:chunk], v[:chunk], bufs["table"], bufs["k_pool"], bufs["v_pool"])
+    pre, app, flops = [], [], 0
+    n = chunk
+    for c in range(N // chunk):
+        if c > 0:
+            plan.append([chunk])
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            for l in range(L):
+                sp.append(plan, l, k[n:n + chunk], v[n:n + chunk], bufs["table"], bufs["k_pool"],
+                          bufs["v_pool"])
+            e1.record(stream)
+            app.append((e0, e1))
+            n += chunk
+        for l in range(L):
+            flops += 4 * D * full.group * plan.stats(l)["prefill_pairs"]
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            sp.prefill(plan, l, q[n - chunk:n], bufs["table"], bufs["k_pool"], bufs["v_pool"], scale,
+                       o[n - chunk:n])
+            e1.record(stream)
+            pre.append((e0, e1))
+    torch.cuda.synchronize()
+    pre_ms = sum(a.elapsed_time(b) for a, b in pre)
+    app_ms = sum(a.elapsed_time(b) for a, b in app)
+    tf = flops / (pre_ms * 1e-3) / 1e12
+    log(f"chunked prefill: {pre_ms / L:.1f} ms/layer over {N // chunk} chunks ({tf:.0f} TF/s), "
+        f"append {app_ms / L:.3f} ms/layer, pool {plan.sizes.pool_bytes / 1e6:.0f} MB vs "
+        f"{one_shot_pool / 1e6:.0f} MB one-shot")
+    pool = plan.sizes.pool_bytes
+    del plan, bufs, k, v, q, o
+    torch.cuda.empty_cache()
+    return {"workload": f"long-prefill {N} tokens x {L} layers in {N // chunk} chunks of {chunk}",
+            "prefill_ms_per_layer": round(pre_ms / L, 3), "prefill_tflops": round(tf, 1),
+            "append_ms_per_layer": round(app_ms / L, 4),
+            "pool_bytes_per_tensor": pool, "one_shot_pool_bytes_per_tensor": one_shot_pool}
 
 
 def decode_loop_append(torch, W, sp, dev, stream, log):

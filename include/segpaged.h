@@ -85,7 +85,11 @@ typedef struct {
   int64_t capacity_pages;       /* pages of the pool the caller provides; 0 = exactly the pages needed.
                                    Every page id must be < capacity. */
   int32_t decode_split_tokens;  /* keys per decode work item, a multiple of 64; 0 = automatic */
-  int32_t append_capacity;      /* tokens each sequence may gain after planning (decode form only); 0 = none */
+  int32_t append_capacity;      /* tokens each sequence may gain after planning; 0 = none */
+  int32_t append_chunk;         /* most tokens one append adds to a sequence (with append_capacity;
+                                   0 = 1): local heads keep a ring of ceil((W + chunk - 1) / P) + 1
+                                   pages, enough for every row of the newest chunk */
+  int32_t reserved;             /* 0 */
 } segpaged_spec;
 
 /* Sizes the caller allocates. */
@@ -128,12 +132,13 @@ typedef struct segpaged_plan segpaged_plan;  /* opaque, host heap */
  * per-head varlen work lists of the prefill and decode kernels [RT section 4].
  * Host only: makes no HIP call, so it runs without a GPU. The layout is built
  * once here and reused by every call [RT section 5].
- * append_capacity > 0 (every sequence in decode form, q0_b = max(N_b - 1, 0))
- * plans for a decode loop: global heads reserve the pages of N_b +
- * append_capacity; local heads keep two segments, the sink (ceil(sink/P) pages
- * reserved) and the window [max(sink, N_b - W), N_b) in a ring of ceil(W/P) + 1
- * pages; the work-list regions and the decode workspace are sized for the
- * largest lengths (see segpaged_plan_append).
+ * append_capacity > 0 plans for growth -- a decode loop (chunk 1) or a chunked
+ * prefill: each sequence may hold the rows of at most one chunk,
+ * N_b - q0_b <= chunk (decode form: q0_b = N_b - 1); global heads reserve the
+ * pages of N_b + append_capacity; local heads keep two segments, the sink
+ * (ceil(sink/P) pages reserved) and the window [max(sink, q0_b - W + 1), N_b) in
+ * a ring of ceil((W + chunk - 1)/P) + 1 pages; the work-list regions and the
+ * decode workspace are sized for the largest lengths (see segpaged_plan_append).
  * Returns EINVAL for a bad spec, EUNSUPPORTED for an unsupported D/P/group,
  * ENOSPACE when the free list or capacity is too small. *plan is NULL on error. */
 SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan** plan,
@@ -202,14 +207,16 @@ SEGPAGED_API int segpaged_prefill(const segpaged_plan* plan, int32_t layer, cons
                                   const void* v_pool, float scale, void* o, float* lse,
                                   void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Decode-loop growth, host side (the layout is written once, when K/V is
- * written, and then only extended [RT section 5]): every sequence b gains
- * n_new[b] >= 0 tokens, N_b += n_new[b], q0_b = N_b - 1. Only for plans made
- * with append_capacity > 0 (ESTATE otherwise); ENOSPACE if a sequence would pass
- * its planned length plus append_capacity, EINVAL for a negative count. Updates
+/* Growth, host side (the layout is written once, when K/V is written, and then
+ * only extended [RT section 5]): every sequence b gains 0 <= n_new[b] <= chunk
+ * tokens, N_b += n_new[b]; its rows become the new tokens, q0_b = N_b - n_new[b]
+ * (the last row, N_b - 1, when it gains none), so a prefill call computes the
+ * newest chunk and a decode call row N_b - 1. Only for plans made with
+ * append_capacity > 0 (ESTATE otherwise); ENOSPACE if a sequence would pass its
+ * planned length plus append_capacity, EINVAL for a count < 0 or > chunk. Updates
  * the plan's image: sequence rows; unit records (a global head's segment grows
  * into its reserved pages; a local head keeps its sink and the window positions
- * [p0, N) in a ring of ceil(W/P) + 1 pages: when the window outgrows the ring,
+ * [p0, N) in a ring of ceil((W + chunk - 1)/P) + 1 pages: when it outgrows the ring,
  * p0 moves on by P and the id of the page that held the oldest positions moves
  * to the end of the ring); the work lists; and the append list the next
  * segpaged_append reads. Sizes (table_int32s, pools, workspace) do not change.

@@ -245,52 +245,57 @@ def retained_kv_bytes(spec: Spec, bytes_per_elem: int = 2) -> int:
 
 
 # ----------------------------------------------------------------------------
-# Growth for a decode loop (append mode). The layout is written once, when K/V
-# is written, and afterwards only extended (runtime explainer, section 5); local
-# heads keep only sink + recent tokens (section 3). The rules, for a plan made
-# in decode form at lengths N0_b with an append capacity `cap`:
+# Growth (append mode: a decode loop, or a prefill taken in chunks). The layout
+# is written once, when K/V is written, and afterwards only extended (runtime
+# explainer, section 5); local heads keep only sink + recent tokens (section 3).
+# The rules, for a plan made at lengths N0_b with first rows q0_b
+# (N0_b - q0_b <= chunk), an append capacity `cap` and at most `chunk` tokens
+# per append:
 #   * reserved pages per unit (ids taken from the free list in unit order):
 #       GLOBAL / DENSE  ceil((N0 + cap) / P)
-#       LOCAL(s, W)     ceil(s / P) sink pages, then a ring of R = ceil(W / P) + 1
+#       LOCAL(s, W)     ceil(s / P) sink pages, then a ring of
+#                       R = ceil((W + chunk - 1) / P) + 1
 #       RETRIEVAL(R)    ceil(|R| / P)
 #   * GLOBAL position p: unit page p // P, slot p % P.
 #   * LOCAL position p < s: unit page p // P, slot p % P (the sink).
-#   * LOCAL position p >= w0 = max(s, N0 - W): ring offset o = (p - w0) mod (R P),
-#     unit page ceil(s / P) + o // P, slot o % P -- a ring buffer whose newest
-#     R P - (its fill within the last page) positions are kept, so every key in
-#     the window (N - W, N] is still held.
+#   * LOCAL position p >= w0 = max(s, q0 - W + 1): ring offset o = (p - w0) mod
+#     (R P), unit page ceil(s / P) + o // P, slot o % P -- a ring buffer holding
+#     more than W + chunk - 1 recent positions, so every key a row of the
+#     newest chunk sees is still held.
 # ----------------------------------------------------------------------------
 
-def append_reserved_pages(spec: Spec, cap: int, b: int, l: int, h: int) -> int:
+def append_reserved_pages(spec: Spec, cap: int, b: int, l: int, h: int, chunk: int = 1) -> int:
     kind, s, w = spec.head_class(l, h)
     P = spec.page_size
     if kind == LOCAL:
-        return ceil_div(s, P) + ceil_div(w, P) + 1
+        return ceil_div(s, P) + ceil_div(w + chunk - 1, P) + 1
     if kind == RETRIEVAL:
         return ceil_div(len(spec.retrieval.get((b, l, h), [])), P)
     return ceil_div(spec.seq_len[b] + cap, P)
 
 
-def append_unit_pages(spec: Spec, cap: int) -> Dict[Tuple[int, int, int], List[int]]:
+def append_unit_pages(spec: Spec, cap: int, chunk: int = 1
+                      ) -> Dict[Tuple[int, int, int], List[int]]:
     """Reserved page ids of every unit (b, l, h), in allocation order."""
     out, cursor = {}, 0
     fl = spec.free_list
     for (u, b, l, h) in units(spec):
-        n = append_reserved_pages(spec, cap, b, l, h)
+        n = append_reserved_pages(spec, cap, b, l, h, chunk)
         out[(b, l, h)] = [int(fl[cursor + i]) if fl is not None else cursor + i
                           for i in range(n)]
         cursor += n
     return out
 
 
-def append_slot(spec: Spec, b: int, l: int, h: int, p: int) -> Tuple[int, int]:
+def append_slot(spec: Spec, b: int, l: int, h: int, p: int, chunk: int = 1) -> Tuple[int, int]:
     """(unit page index, slot) of position p of unit (b, l, h) in append mode
-    (positions a local head no longer keeps map onto the slot that replaced them)."""
+    (positions a local head no longer keeps map onto the slot that replaced them);
+    `spec` is the spec the plan was made from."""
     kind, s, w = spec.head_class(l, h)
     P = spec.page_size
     if kind == LOCAL and p >= s:
-        w0 = max(s, spec.seq_len[b] - w)
-        ring = (ceil_div(w, P) + 1) * P
+        w0 = max(s, spec.first_query_pos[b] - w + 1)
+        ring = (ceil_div(w + chunk - 1, P) + 1) * P
         o = (p - w0) % ring
         return ceil_div(s, P) + o // P, o % P
     return p // P, p % P

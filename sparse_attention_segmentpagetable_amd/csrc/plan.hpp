@@ -55,6 +55,7 @@ struct segpaged_plan {
   segpaged_stats total{};
   // append mode (spec.append_capacity > 0): sequences grow after planning
   int64_t append_cap = 0;                    // tokens each sequence may gain
+  int64_t append_chunk = 1;                  // most tokens one append adds to a sequence
   std::vector<int64_t> n_max;                // per sequence: length limit
   int64_t dec_cap = 0, pre_cap = 0;          // work-list capacities (items)
   int64_t off_app = 0;                       // append list: row offsets [B+1], first positions [B]

@@ -298,7 +298,8 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
   if (!s.seq_len || !s.first_query_pos || !s.kind || !s.sink || !s.window) return SEGPAGED_EINVAL;
   if (s.decode_split_tokens < 0 || s.decode_split_tokens % 64 != 0) return SEGPAGED_EINVAL;
   if (s.capacity_pages < 0 || s.free_list_len < 0) return SEGPAGED_EINVAL;
-  if (s.append_capacity < 0) return SEGPAGED_EINVAL;
+  if (s.append_capacity < 0 || s.append_chunk < 0) return SEGPAGED_EINVAL;
+  const int64_t chunk = std::max<int64_t>(s.append_chunk, 1);
 
   const int64_t B = s.num_seqs, L = s.num_layers, Hkv = s.num_kv_heads, P = s.page_size;
   const int64_t U = L * B * Hkv;
@@ -314,10 +315,10 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
   }
   if (kv_rows > kI32Max || q_rows > kI32Max) return SEGPAGED_EINVAL;
   if (s.append_capacity > 0) {
-    // growth is for the decode loop: every sequence in decode form
+    // growth: every sequence holds the rows of at most one chunk
     if (kv_rows + (int64_t)s.append_capacity * B > kI32Max) return SEGPAGED_EINVAL;
     for (int64_t b = 0; b < B; ++b)
-      if (s.first_query_pos[b] != std::max(s.seq_len[b] - 1, 0)) return SEGPAGED_EINVAL;
+      if ((int64_t)s.seq_len[b] - s.first_query_pos[b] > chunk) return SEGPAGED_EINVAL;
   }
 
   bool any_retr = false;
@@ -357,6 +358,7 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
   while ((1 << pl->log2P) < P) ++pl->log2P;
   pl->num_units = U; pl->q_rows = q_rows; pl->kv_rows = kv_rows;
   pl->append_cap = s.append_capacity;
+  pl->append_chunk = chunk;
   if (pl->append_cap > 0) {
     pl->n_max.resize(B);
     for (int64_t b = 0; b < B; ++b) pl->n_max[b] = (int64_t)s.seq_len[b] + pl->append_cap;
@@ -365,7 +367,8 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
   // ---- pass 1: segments per unit, reserved pages, retrieval totals
   // Append mode keeps room to grow: a global head reserves the pages of its
   // length limit; a local head always has two segments, the sink (its pages
-  // reserved) and the window, whose pages form a ring of ceil(W/P) + 1.
+  // reserved) and the window, whose pages form a ring of
+  // ceil((W + chunk - 1)/P) + 1, enough for the windows of a chunk's rows.
   const bool grow = pl->append_cap > 0;
   std::vector<Seg> segs(U * 2);
   std::vector<int> nseg(U);
@@ -380,11 +383,11 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
         const int kind = s.kind[c];
         if (grow && kind == SEGPAGED_LOCAL) {
           const int64_t a = std::min<int64_t>(s.sink[c], n);
-          const int64_t w0 = std::max<int64_t>(s.sink[c], n - s.window[c]);
+          const int64_t w0 = std::max<int64_t>(s.sink[c], s.first_query_pos[b] - s.window[c] + 1);
           segs[2 * u] = {0, a};
           segs[2 * u + 1] = {w0, std::max<int64_t>(n - w0, 0)};
           nseg[u] = 2;
-          res_pages[u] = ceil_div(s.sink[c], P) + ceil_div(s.window[c], P) + 1;
+          res_pages[u] = ceil_div(s.sink[c], P) + ceil_div(s.window[c] + chunk - 1, P) + 1;
         } else if (grow && kind != SEGPAGED_RETRIEVAL) {
           segs[2 * u] = {0, n};
           nseg[u] = 1;
@@ -509,7 +512,8 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
   WorkLists wl;
   make_work_lists(pl, wl);
   pl->dec_cap = grow ? std::max<int64_t>(dec_cap, wl.n_dec()) : wl.n_dec();
-  pl->pre_cap = grow ? std::max<int64_t>(U, wl.n_pre()) : wl.n_pre();
+  pl->pre_cap = grow ? std::max<int64_t>(U * ceil_div(chunk, kPrefillRows / G), wl.n_pre())
+                     : wl.n_pre();
   pl->off_dec = pl->off_decunits + 2 * U;
   pl->off_pre = pl->off_dec + kDecItemInts * pl->dec_cap;
   pl->off_ctr = pl->off_pre + kPreItemInts * pl->pre_cap;
@@ -551,10 +555,10 @@ SEGPAGED_API int segpaged_plan_append(segpaged_plan* pl, const int32_t* n_new) {
   std::vector<int32_t> n_old(B), n_now(B), q0(B);
   for (int64_t b = 0; b < B; ++b) {
     n_old[b] = t[pl->off_seqs + kSeqInts * b + S_N];
-    if (n_new[b] < 0) return SEGPAGED_EINVAL;
+    if (n_new[b] < 0 || n_new[b] > pl->append_chunk) return SEGPAGED_EINVAL;
     if (n_old[b] + (int64_t)n_new[b] > pl->n_max[b]) return SEGPAGED_ENOSPACE;
     n_now[b] = n_old[b] + n_new[b];
-    q0[b] = std::max(n_now[b] - 1, 0);
+    q0[b] = std::max(n_now[b] - std::max(n_new[b], 1), 0);
   }
   write_seq_rows(pl, n_now.data(), q0.data());
   // append list: where each sequence's new K/V rows start, and their positions
@@ -580,7 +584,7 @@ SEGPAGED_API int segpaged_plan_append(segpaged_plan* pl, const int32_t* n_new) {
     } else if (r[U_KIND] == SEGPAGED_LOCAL) {
       const int64_t sink = r[U_SINK], win = r[U_WIN];
       const int64_t len0 = std::min<int64_t>(sink, n);
-      const int64_t ring_pages = ceil_div(win, P) + 1;
+      const int64_t ring_pages = ceil_div(win + pl->append_chunk - 1, P) + 1;
       int64_t p0 = r[U_S1POS];
       int64_t len1 = std::max<int64_t>(n - p0, 0);
       int32_t* ring = &t[pl->off_pages + r[U_PAGEOFF] + ceil_div(sink, P)];

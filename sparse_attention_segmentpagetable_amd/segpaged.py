@@ -37,7 +37,8 @@ class _Spec(ctypes.Structure):
                 ("sink", _i32p), ("window", _i32p), ("retr_offsets", _i64p),
                 ("retr_pos", _i32p), ("free_list", _i32p), ("free_list_len", ctypes.c_int64),
                 ("capacity_pages", ctypes.c_int64), ("decode_split_tokens", ctypes.c_int32),
-                ("append_capacity", ctypes.c_int32)]
+                ("append_capacity", ctypes.c_int32),
+                ("append_chunk", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class Sizes(ctypes.Structure):
@@ -112,7 +113,8 @@ class Plan:
     kind, sink, window, retrieval {(b, l, h): positions}, free_list,
     capacity_pages)."""
 
-    def __init__(self, spec, decode_split_tokens: int = 0, append_capacity: int = 0):
+    def __init__(self, spec, decode_split_tokens: int = 0, append_capacity: int = 0,
+                 append_chunk: int = 0):
         B, L, Hkv = len(spec.seq_len), spec.num_layers, spec.num_kv_heads
         self.num_seqs, self.num_layers = B, L
         self.num_q_heads, self.num_kv_heads = spec.num_q_heads, Hkv
@@ -157,7 +159,8 @@ class Plan:
                   window=keep["window"].ctypes.data_as(_i32p),
                   retr_offsets=ptr_offs, retr_pos=ptr_pos, free_list=ptr_free,
                   free_list_len=fl_len, capacity_pages=int(getattr(spec, "capacity_pages", 0) or 0),
-                  decode_split_tokens=decode_split_tokens, append_capacity=append_capacity)
+                  decode_split_tokens=decode_split_tokens, append_capacity=append_capacity,
+                  append_chunk=append_chunk, reserved=0)
         self._h = ctypes.c_void_p()
         self.sizes = Sizes()
         _check(_lib().segpaged_plan_create(ctypes.byref(c), ctypes.byref(self._h),

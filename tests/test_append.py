@@ -33,22 +33,32 @@ def _visible(spec, b, l, h, n):
     return list(np.nonzero(OA.visibility_mask(kind, s, w, r, np.array([n - 1]), n)[0])[0])
 
 
-@pytest.mark.parametrize("s,w,P,n0", [(0, 1, 16, 0), (3, 37, 16, 50), (20, 5, 16, 3),
-                                      (4, 64, 64, 200), (0, 63, 32, 1), (5, 16, 16, 21)])
-def test_ring_model_keeps_every_visible_key(s, w, P, n0):
+@pytest.mark.parametrize("s,w,P,n0,chunk", [(0, 1, 16, 0, 1), (3, 37, 16, 50, 1),
+                                            (20, 5, 16, 3, 1), (4, 64, 64, 200, 1),
+                                            (0, 63, 32, 1, 1), (5, 16, 16, 21, 1),
+                                            (3, 37, 16, 50, 9), (4, 64, 64, 200, 100),
+                                            (0, 20, 16, 7, 7), (2, 5, 32, 40, 40)])
+def test_ring_model_keeps_every_visible_key(s, w, P, n0, chunk):
+    q0 = max(n0 - chunk, 0)
     spec = W.Spec(name="r", num_layers=1, num_q_heads=1, num_kv_heads=1, head_dim=64,
-                  page_size=P, seq_len=[n0], first_query_pos=[max(n0 - 1, 0)], kind=[W.LOCAL],
+                  page_size=P, seq_len=[n0], first_query_pos=[q0], kind=[W.LOCAL],
                   sink=[s], window=[w], seed=1)
-    res = OL.append_reserved_pages(spec, 0, 0, 0, 0)
-    for n in range(n0, n0 + 5 * (w + P) + 3):
-        vis = _visible(spec, 0, 0, 0, n)
+    res = OL.append_reserved_pages(spec, 0, 0, 0, 0, chunk)
+    w0 = max(s, q0 - w + 1)
+    for n in range(n0, n0 + 5 * (w + P + chunk) + 3):
         cells = {}
         for p in range(n):  # replay writes in position order; the last writer owns a cell
-            if p < n0 and not (p < s or p >= max(s, n0 - w)):
+            if p < n0 and not (p < s or p >= w0):
                 continue  # never stored: dropped before planning
-            cells[OL.append_slot(spec, 0, 0, 0, p)] = p
-        for p in vis:
-            pg, slot = OL.append_slot(spec, 0, 0, 0, p)
+            cells[OL.append_slot(spec, 0, 0, 0, p, chunk)] = p
+        # every key any row of the newest chunk (rows n - chunk .. n - 1) sees
+        rows = np.arange(max(n - chunk, q0 if n == n0 else 0), n)
+        rows = rows[rows >= 0]
+        need = set()
+        for i in rows:
+            need |= set(np.nonzero(OA.visibility_mask(W.LOCAL, s, w, None, np.array([i]), n)[0])[0])
+        for p in sorted(need):
+            pg, slot = OL.append_slot(spec, 0, 0, 0, int(p), chunk)
             assert 0 <= pg < res and 0 <= slot < P
             assert cells[(pg, slot)] == p, (n, p)
 
@@ -74,8 +84,8 @@ def test_planner_image_follows_the_ring_model(free):
     cap = 120
     if free:
         spec = replace(spec, free_list=W.seeded_free_list(400, 5), capacity_pages=400)
-    plan = sp.Plan(spec, append_capacity=cap)
-    pages = OL.append_unit_pages(spec, cap)
+    plan = sp.Plan(spec, append_capacity=cap, append_chunk=3)
+    pages = OL.append_unit_pages(spec, cap, 3)
     rng = np.random.default_rng(3)
     n = list(spec.seq_len)
     for step in range(40):
@@ -85,20 +95,20 @@ def test_planner_image_follows_the_ring_model(free):
         n = [a + x for a, x in zip(n, add)]
         t = plan.table_host()
         for b in range(len(n)):
-            assert t[16 + 4 * b] == n[b] and t[16 + 4 * b + 1] == max(n[b] - 1, 0)
+            assert t[16 + 4 * b] == n[b] and t[16 + 4 * b + 1] == max(n[b] - max(add[b], 1), 0)
         for (u, b, l, h) in OL.units(spec):
             kind, _, _ = spec.head_class(l, h)
             if kind == W.RETRIEVAL:
                 continue
             for p in _visible(spec, b, l, h, n[b]):
-                pg, slot = OL.append_slot(spec, b, l, h, p)
+                pg, slot = OL.append_slot(spec, b, l, h, p, 3)
                 assert _slot_from_table(t, u, p, spec.page_size) == (pages[(b, l, h)][pg], slot)
 
 
 def test_decode_items_cover_visible_keys_after_appends():
     spec = _spec(ps=16)
     cap = 200
-    plan = sp.Plan(spec, append_capacity=cap, decode_split_tokens=64)
+    plan = sp.Plan(spec, append_capacity=cap, decode_split_tokens=64, append_chunk=70)
     n = list(spec.seq_len)
     for add in ([1, 1, 1, 1], [3, 0, 2, 5], [64, 1, 0, 40], [0, 0, 0, 0], [17, 33, 70, 2]):
         plan.append(add)
@@ -135,10 +145,15 @@ def test_decode_items_cover_visible_keys_after_appends():
 
 def test_append_errors():
     spec = _spec()
-    plan = sp.Plan(spec, append_capacity=5)
+    plan = sp.Plan(spec, append_capacity=5, append_chunk=5)
     with pytest.raises(sp.SegPagedError) as e:
         plan.append([6, 0, 0, 0])
-    assert e.value.status == -3
+    assert e.value.status == -1  # more than one chunk
+    plan.append([3, 0, 0, 0])
+    with pytest.raises(sp.SegPagedError) as e:
+        plan.append([3, 0, 0, 0])
+    assert e.value.status == -3  # past the capacity
+    plan = sp.Plan(spec, append_capacity=5, append_chunk=5)
     with pytest.raises(sp.SegPagedError) as e:
         plan.append([-1, 0, 0, 0])
     assert e.value.status == -1
@@ -148,10 +163,11 @@ def test_append_errors():
     with pytest.raises(sp.SegPagedError) as e:
         sp.Plan(spec).append([1, 0, 0, 0])
     assert e.value.status == -5
-    # growth needs the decode form
+    # growth: at most one chunk of rows per sequence
     with pytest.raises(sp.SegPagedError) as e:
         sp.Plan(replace(spec, first_query_pos=[0, 0, 0, 0]), append_capacity=4)
     assert e.value.status == -1
+    sp.Plan(replace(spec, first_query_pos=[0, 0, 0, 0]), append_capacity=4, append_chunk=50)
     lib = sp.library()
     assert lib.segpaged_append(None, 0, None, None, None, None, None, None) == -1
     assert lib.segpaged_plan_append(None, None) == -1
@@ -159,7 +175,7 @@ def test_append_errors():
 
 def test_sizes_do_not_change_with_appends():
     spec = _spec()
-    plan = sp.Plan(spec, append_capacity=64)
+    plan = sp.Plan(spec, append_capacity=64, append_chunk=64)
     z0 = plan.sizes.as_dict()
     plan.append([64, 10, 0, 3])
     z1 = plan.sizes.as_dict()

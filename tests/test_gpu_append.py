@@ -52,7 +52,7 @@ def test_decode_loop_with_append(name, hd, ps, n0, cap, all_layers):
         kb, vb = W.kv_bits(full, l)
         hist.append(([kb[kvo[b]:kvo[b] + full.seq_len[b]] for b in range(B)],
                      [vb[kvo[b]:kvo[b] + full.seq_len[b]] for b in range(B)]))
-    plan = sp.Plan(spec, append_capacity=cap, decode_split_tokens=64)
+    plan = sp.Plan(spec, append_capacity=cap, decode_split_tokens=64, append_chunk=13)
     bufs = plan.allocate(DEV)
     n = list(n0)
     for l in range(L):
@@ -106,7 +106,7 @@ def test_decode_loop_with_append(name, hd, ps, n0, cap, all_layers):
         if kind == W.LOCAL:
             moved += int(t[int(t[12]) + 16 * u + 12]) - max(s, n0[b] - w) >= ps
     assert moved > 0
-    pages = OL.append_unit_pages(spec, cap)
+    pages = OL.append_unit_pages(spec, cap, 13)
     P, D = ps, hd
     kp = to_bits(bufs["k_pool"]).reshape(-1, D // 8, P, 8)
     vp = to_bits(bufs["v_pool"]).reshape(-1, P // 8, D, 8)
@@ -116,9 +116,62 @@ def test_decode_loop_with_append(name, hd, ps, n0, cap, all_layers):
             continue
         vis = np.nonzero(OA.visibility_mask(kind, s, w, None, np.array([n[b] - 1]), n[b])[0])[0]
         for p in vis:
-            pg, slot = OL.append_slot(spec, b, l, h, int(p))
+            pg, slot = OL.append_slot(spec, b, l, h, int(p), 13)
             pid = pages[(b, l, h)][pg]
             kref = hist[l][0][b][p, h]
             vref = hist[l][1][b][p, h]
             assert np.array_equal(kp[pid, :, slot, :].reshape(-1), kref), (name, u, p)
             assert np.array_equal(vp[pid, slot // 8, :, slot % 8], vref), (name, u, p)
+
+
+CHUNK_CASES = [
+    ("d128-p64-chunk128", 128, 64, 16, 128),
+    ("d64-p16-chunk100", 64, 16, 4, 100),
+]
+
+
+@pytest.mark.parametrize("name,hd,ps,hq,chunk", CHUNK_CASES, ids=[c[0] for c in CHUNK_CASES])
+def test_chunked_prefill(name, hd, ps, hq, chunk):
+    """A long prefill taken a chunk at a time over a cache whose local heads hold
+    only sink + a ring: each chunk's rows equal the oracle's full prefill rows."""
+    final = [700, 333, 1029]
+    kind = [W.GLOBAL, W.LOCAL, W.LOCAL, W.DENSE]
+    s0 = W.Spec(name="chunked", num_layers=1, num_q_heads=hq, num_kv_heads=4, head_dim=hd,
+                page_size=ps, seq_len=final, first_query_pos=[0, 0, 0], kind=kind,
+                sink=[0, 4, 0, 0], window=[1, 130, 64, 1], seed=33)
+    kb, vb = W.kv_bits(s0, 0)
+    kvo = s0.kv_row_offsets()
+    K = [kb[kvo[b]:kvo[b] + final[b]] for b in range(3)]
+    V = [vb[kvo[b]:kvo[b] + final[b]] for b in range(3)]
+    n = [min(chunk, f) for f in final]
+    spec = replace(s0, seq_len=list(n), first_query_pos=[0, 0, 0])
+    plan = sp.Plan(spec, append_capacity=max(final) - chunk, append_chunk=chunk)
+    assert plan.sizes.num_pages < sp.Plan(s0).sizes.num_pages  # local heads: sink + ring only
+    bufs = plan.allocate(DEV)
+    sp.build(plan, 0, to_dev(_pack(K, n)), to_dev(_pack(V, n)), bufs["table"], bufs["k_pool"],
+             bufs["v_pool"])
+    q0 = [0, 0, 0]
+    scale = 1.0 / np.sqrt(hd)
+    step = 0
+    while True:
+        cur = replace(s0, seq_len=list(n), first_query_pos=list(q0))
+        qb = W.q_bits(cur, 0, seed=200 + step)
+        q = to_dev(qb)
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device=DEV)
+        sp.prefill(plan, 0, q, bufs["table"], bufs["k_pool"], bufs["v_pool"], scale, o, lse)
+        torch.cuda.synchronize()
+        ref, ref_lse = OA.attention(cur, 0, qb, _pack(K, n), _pack(V, n), scale)
+        parity(to_f64(o), ref, f"{name} chunk {step} n={n} q0={q0}")
+        lse_parity(lse.cpu().numpy(), ref_lse, f"{name} chunk {step}")
+        add = [min(chunk, f - x) for f, x in zip(final, n)]
+        if not any(add):
+            break
+        plan.append(add)
+        nk = np.concatenate([K[b][n[b]:n[b] + add[b]] for b in range(3)])
+        nv = np.concatenate([V[b][n[b]:n[b] + add[b]] for b in range(3)])
+        sp.append(plan, 0, to_dev(nk), to_dev(nv), bufs["table"], bufs["k_pool"], bufs["v_pool"])
+        n = [x + a for x, a in zip(n, add)]
+        q0 = [x - max(a, 1) for x, a in zip(n, add)]
+        step += 1
+    assert n == final and step >= 7
