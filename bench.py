@@ -478,7 +478,42 @@ def extra_configs(torch, W, sp, dev, stream, log):
     res["decode_context_sweep"] = decode_context_sweep(torch, W, sp, dev, timed, log)
     res["decode_loop_append"] = decode_loop_append(torch, W, sp, dev, stream, log)
     res["chunked_prefill"] = chunked_prefill(torch, W, sp, dev, stream, log)
+    res["retrieval_selection"] = retrieval_selection(torch, W, sp, dev, timed, log)
     return res
+
+
+def retrieval_selection(torch, W, sp, dev, timed, log):
+    """Top-p retrieval-set selection (segpaged_select_topp) on one Llama-shaped
+    layer, 8 sequences x 32768 keys, KV heads 0-1 retrieval (16 (sequence, head)
+    pairs): the decode row's attention over the dense history, then top-p = 0.9.
+    The scoring pass reads each pair's dense K once (the algorithmic bytes)."""
+    from dataclasses import replace as _replace
+    n = 32768
+    base = W.llama70b_decode(num_layers=1, n=n)
+    kind = [W.RETRIEVAL, W.RETRIEVAL] + [W.LOCAL] * 6
+    retr = {(b, 0, h): np.zeros(0, np.int32) for b in range(base.num_seqs) for h in (0, 1)}
+    spec = _replace(base, kind=kind, retrieval=retr)
+    B, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    plan = sp.Plan(spec)
+    bufs = plan.allocate(dev, workspace=False)
+    k = W.randn_bf16_device((B * n, Hkv, D), spec.seed, W.TAG_K, 0, dev)
+    sp.build(plan, 0, k, k, bufs["table"], bufs["k_pool"], bufs["v_pool"])
+    q = W.randn_bf16_device((B, Hq, D), spec.seed, W.TAG_Q, 0, dev) * 4
+    T = plan.sizes.kv_rows
+    out_pos = torch.empty(Hkv * T, dtype=torch.int32, device=dev)
+    out_cnt = torch.empty(B * Hkv, dtype=torch.int32, device=dev)
+    ws = torch.empty(plan.sizes.select_workspace_bytes // 4, dtype=torch.float32, device=dev)
+    ms, _ = timed(lambda: sp.select_topp(plan, 0, q, k, bufs["table"], 1 / math.sqrt(D), 0.9,
+                                         out_pos, out_cnt, ws), 10)
+    kept = float(out_cnt.view(B, Hkv)[:, :2].float().mean())
+    kbytes = 2 * B * n * D * 2
+    log(f"retrieval selection: {ms:.3f} ms for {2 * B} pairs x {n} keys "
+        f"({kbytes / (ms * 1e-3) / 1e9:.0f} GB/s of dense K), {kept:.0f} keys kept per pair at p 0.9")
+    del plan, bufs, k, q, out_pos, out_cnt, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"llama-shaped layer, {B} seqs x {n} keys, 2 retrieval KV heads, top-p 0.9",
+            "ms": round(ms, 4), "dense_k_gbs": round(kbytes / (ms * 1e-3) / 1e9, 1),
+            "keys_kept_per_pair": round(kept, 1)}
 
 
 def chunked_prefill(torch, W, sp, dev, stream, log):

@@ -106,6 +106,7 @@ typedef struct {
   int64_t prefill_items;    /* prefill work items, all layers */
   int64_t decode_workspace_bytes;  /* workspace a decode call over all layers needs */
   int64_t prefill_workspace_bytes; /* workspace a prefill call needs (0 in this version) */
+  int64_t select_workspace_bytes;  /* workspace segpaged_select_topp needs (largest lengths) */
 } segpaged_sizes;
 
 /* Algorithmic work of one layer (or all layers when layer = -1), for throughput
@@ -236,6 +237,31 @@ SEGPAGED_API int segpaged_plan_append(segpaged_plan* plan, const int32_t* n_new)
 SEGPAGED_API int segpaged_append(segpaged_plan* plan, int32_t layer, const void* k_new,
                                  const void* v_new, int32_t* d_table, void* k_pool,
                                  void* v_pool, void* stream);
+
+/* Retrieval-set selection, top-p by attention mass ([RT] section 2: retrieval
+ * heads keep the top-p important tokens, looked up on demand): for every
+ * RETRIEVAL KV head h of `layer` and every sequence b, the decode row's (position
+ * N_b - 1) attention over all N_b keys of the dense history, averaged over the G
+ * query heads of the group, is the mass of each key; the selected set is the
+ * shortest prefix of the keys ordered by mass (larger first, equal masses by
+ * position) whose mass reaches p of the total, as sorted positions. It is the
+ * retrieval set a new plan (segpaged_spec.retr_pos) then keeps.
+ *   q        device bf16 [B][Hq][D]: the decode row of each sequence
+ *   k_dense  device bf16 [T_total][Hkv][D] of this layer (sequences packed in order)
+ *   d_table  as built for this plan (sequence lengths and head classes)
+ *   scale    softmax scale; p in (0, 1]
+ *   out_pos  device int32 [Hkv][T_total]: the set of (b, h) at h * T_total +
+ *            (first dense row of b), out_cnt[b * Hkv + h] entries
+ *   out_cnt  device int32 [B * Hkv] (0 for other classes and empty sequences)
+ *   workspace/workspace_bytes: select_workspace_bytes
+ * Sums run in a fixed order, so repeated calls return the same set; where fp32
+ * rounding of the masses decides between keys of nearly equal mass the set may
+ * differ from an exact computation in those keys only. EINVAL / ENOSPACE / ESTATE
+ * (layer = -1 is not accepted) as above. */
+SEGPAGED_API int segpaged_select_topp(const segpaged_plan* plan, int32_t layer, const void* q,
+                                      const void* k_dense, const int32_t* d_table, float scale,
+                                      float p, int32_t* out_pos, int32_t* out_cnt, void* workspace,
+                                      int64_t workspace_bytes, void* stream);
 
 /* Split-K decode [RT section 4; KV section 10.2]: the query at position N_b - 1 of
  * each sequence attends to every key it can see. Work items are (unit, key

@@ -7,7 +7,8 @@ pages. The compute path is libsegpaged.so (HIP, gfx950); this package is its
 ctypes binding.
 """
 from .segpaged import (DENSE, GLOBAL, LIB_PATH, LOCAL, RETRIEVAL, Plan, SegPagedError,
-                       Sizes, Stats, append, build, decode, library, prefill)
+                       Sizes, Stats, append, build, decode, library, prefill,
+                       select_topp)
 
-__all__ = ["Plan", "build", "append", "prefill", "decode", "library", "SegPagedError", "Sizes", "Stats",
+__all__ = ["Plan", "build", "append", "prefill", "decode", "select_topp", "library", "SegPagedError", "Sizes", "Stats",
            "GLOBAL", "LOCAL", "RETRIEVAL", "DENSE", "LIB_PATH"]

@@ -39,7 +39,7 @@ def _compile(sources, out, verbose):
 
 def build_library(verbose: bool = False) -> str:
     _compile(["probe.hip"], PROBE_LIB, verbose)
-    return _compile(["planner.cpp", "kernels.hip"], LIB, verbose)
+    return _compile(["planner.cpp", "kernels.hip", "select.hip"], LIB, verbose)
 
 
 if __name__ == "__main__":

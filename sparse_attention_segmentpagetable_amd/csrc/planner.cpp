@@ -544,6 +544,18 @@ SEGPAGED_API int segpaged_plan_sizes(const segpaged_plan* pl, segpaged_sizes* z)
   z->prefill_items = pl->n_pre;
   z->decode_workspace_bytes = pl->dec_cap * (int64_t)pl->G * (pl->D + 4) * 4;
   z->prefill_workspace_bytes = 0;
+  {  // scores, masses and block partials of segpaged_select_topp at the largest lengths
+    int64_t t_max = 0, n_max = 0;
+    for (int64_t b = 0; b < pl->B; ++b) {
+      const int64_t n = pl->append_cap > 0 ? pl->n_max[b]
+                                           : pl->buf[pl->off_seqs + kSeqInts * b + S_N];
+      t_max += n;
+      n_max = std::max(n_max, n);
+    }
+    const int64_t nblk = std::max<int64_t>(1, (n_max + 255) / 256);
+    z->select_workspace_bytes =
+        4 * (pl->Hkv * t_max * (pl->G + 1) + pl->Hkv * (int64_t)pl->B * nblk * pl->G * 2);
+  }
   return SEGPAGED_OK;
 }
 

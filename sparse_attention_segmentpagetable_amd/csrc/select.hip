@@ -1,0 +1,383 @@
+// Retrieval-set selection on the GPU: top-p by attention mass. Retrieval heads
+// keep the tokens that carry the attention [runtime explainer, section 2;
+// RedKnot summary: retrieval heads look up the important tokens on demand]. For
+// each (sequence b, retrieval KV head h) of a layer: the decode row's (position
+// N_b - 1) attention over every key of the dense history, averaged over the G
+// query heads of the group, gives a mass per key; the set is the shortest
+// mass-ordered prefix (larger first, equal masses by position) reaching p of the
+// total, returned as sorted positions.
+//
+//   select_scores_kernel  scores of 256 keys x G heads per workgroup (fp32, log2
+//                         units), with each block's max and exp-sum per head
+//   select_topp_kernel    one workgroup per pair: the masses, then a radix
+//                         select on their bits (8 bits per pass, larger first)
+//                         with each bin's mass summed alongside in fixed point,
+//                         then the positions taken in order by a block scan
+// Every sum is taken in a fixed order or in exact integer arithmetic, so the set
+// is the same on every call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "plan.hpp"
+
+using namespace segpaged;
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kSelKeys = 256;  // keys per scoring workgroup
+constexpr int kSelThreads = 256;
+constexpr float kLog2eSel = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Scores of 256 keys for the G query heads of (b, h): a wave reads 4 key rows per
+// load, 16 lanes per row (16 bytes each, coalesced), and the 16 partial dot
+// products of a row meet by lane shuffles. Writes s[g] = c * q_g . k_j (log2
+// units) and, per block and head, the max and the sum of exp2(s - max).
+template <int D>
+__global__ __launch_bounds__(kSelThreads) void select_scores_kernel(
+    const int32_t* __restrict__ tab, int32_t off_seqs, int32_t off_units, int32_t layer, int32_t B,
+    int32_t Hkv, int32_t G, int32_t Hq, int32_t T, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ kd, float c, float* __restrict__ ws_s,
+    float* __restrict__ ws_part, int32_t nblk) {
+  constexpr int LPR = D / 8;       // lanes per key row (16 bytes each)
+  constexpr int RPW = 64 / LPR;    // rows per wave load
+  const int b = blockIdx.y / Hkv, h = blockIdx.y % Hkv, blk = blockIdx.x;
+  const int32_t* ur = tab + off_units + kUnitInts * ((layer * B + b) * Hkv + h);
+  if (ur[U_KIND] != SEGPAGED_RETRIEVAL) return;
+  const int32_t N = tab[off_seqs + kSeqInts * b + S_N];
+  const int32_t kvo = tab[off_seqs + kSeqInts * b + S_KVOFF];
+  if (blk * kSelKeys >= N) return;  // uniform over the workgroup
+  __shared__ float ssc[kSelKeys][kMaxGroup];
+  __shared__ float red[kMaxGroup][4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sub = lane % LPR, rr = lane / LPR;
+  // this lane's 8 dims of every query head
+  float qv[kMaxGroup][8];
+#pragma unroll
+  for (int g = 0; g < kMaxGroup; ++g) {
+    if (g < G) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * Hq + h * G + g) * D + sub * 8);
+      qv[g][0] = bf16_lo(w.x); qv[g][1] = bf16_hi(w.x); qv[g][2] = bf16_lo(w.y);
+      qv[g][3] = bf16_hi(w.y); qv[g][4] = bf16_lo(w.z); qv[g][5] = bf16_hi(w.z);
+      qv[g][6] = bf16_lo(w.w); qv[g][7] = bf16_hi(w.w);
+    }
+  }
+  // wave w scores keys [64 w, 64 w + 64) of the block, RPW rows per step
+  for (int r0 = 0; r0 < 64; r0 += RPW) {
+    const int kb = wave * 64 + r0 + rr;  // key within the block
+    const int32_t j = blk * kSelKeys + kb;
+    float kv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (j < N) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(kd + ((int64_t)(kvo + j) * Hkv + h) * D + sub * 8);
+      kv[0] = bf16_lo(w.x); kv[1] = bf16_hi(w.x); kv[2] = bf16_lo(w.y); kv[3] = bf16_hi(w.y);
+      kv[4] = bf16_lo(w.z); kv[5] = bf16_hi(w.z); kv[6] = bf16_lo(w.w); kv[7] = bf16_hi(w.w);
+    }
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) {
+      if (g < G) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(kv[e], qv[g][e], d);
+#pragma unroll
+        for (int off = LPR / 2; off > 0; off >>= 1) d += __shfl_xor(d, off, 64);
+        if (sub == 0) ssc[kb][g] = d * c;
+      }
+    }
+  }
+  __syncthreads();
+  // thread t: key t of the block
+  const int32_t j = blk * kSelKeys + (int32_t)threadIdx.x;
+  const bool ok = j < N;
+  float* srow = ws_s + ((int64_t)h * T + kvo + j) * G;
+#pragma unroll
+  for (int g = 0; g < kMaxGroup; ++g) {
+    if (g < G) {
+      const float sv = ssc[threadIdx.x][g];
+      if (ok) srow[g] = sv;
+      const float m = wave_max(ok ? sv : -INFINITY);
+      if (lane == 0) red[g][wave] = m;
+    }
+  }
+  __syncthreads();
+  float mb[kMaxGroup];
+#pragma unroll
+  for (int g = 0; g < kMaxGroup; ++g)
+    mb[g] = g < G ? fmaxf(fmaxf(red[g][0], red[g][1]), fmaxf(red[g][2], red[g][3])) : 0.f;
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < kMaxGroup; ++g) {
+    if (g < G) {
+      const float e = ok ? exp2f(ssc[threadIdx.x][g] - mb[g]) : 0.f;
+      const float l = wave_sum(e);
+      if (lane == 0) red[g][wave] = l;
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < G) {
+    const int g = threadIdx.x;
+    float* part = ws_part + (((int64_t)h * B + b) * nblk + blk) * G * 2 + 2 * g;
+    part[0] = mb[g];
+    part[1] = (red[g][0] + red[g][1]) + (red[g][2] + red[g][3]);
+  }
+}
+
+// Top-p over the keys of (b, h), one workgroup of kTopThreads per pair: the
+// pair's normalisers from the block partials, the masses (kept in LDS up to
+// kLdsKeys keys, else in the workspace), then a radix select on the masses'
+// bits, 8 bits per pass, larger values first. Each bin's mass is summed in
+// fixed point (mass * 2^40, 64-bit integer adds in LDS), so the sums are exact
+// and the same on every call.
+constexpr int kTopThreads = 1024;
+constexpr int kTopWaves = kTopThreads / 64;
+constexpr int kLdsKeys = 32768;
+
+__device__ __forceinline__ unsigned long long to_fx(float m) {
+  return (unsigned long long)(m * 1099511627776.0f);  // exact scaling, truncated
+}
+
+__device__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// fixed-order reductions over the workgroup
+__device__ float block_max_top(float v, float* red) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = red[0];
+  for (int w = 1; w < kTopWaves; ++w) t = fmaxf(t, red[w]);
+  return t;
+}
+__device__ float block_sum_top(float v, float* red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int w = 0; w < kTopWaves; ++w) t += red[w];
+  return t;
+}
+__device__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long* red) {
+  v = wave_sum_u64(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  unsigned long long t = 0;
+  for (int w = 0; w < kTopWaves; ++w) t += red[w];
+  return t;
+}
+// exclusive prefix sum in thread order
+__device__ int block_scan_top(int v, int* wtot, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) wtot[wave] = x;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+  for (int w = 0; w < kTopWaves; ++w) {
+    if (w < wave) base += wtot[w];
+    total += wtot[w];
+  }
+  return base + x - v;
+}
+
+__global__ __launch_bounds__(kTopThreads) void select_topp_kernel(
+    const int32_t* __restrict__ tab, int32_t off_seqs, int32_t off_units, int32_t layer, int32_t B,
+    int32_t Hkv, int32_t G, int32_t T, const float* __restrict__ ws_s,
+    const float* __restrict__ ws_part, int32_t nblk, float* __restrict__ ws_m, float p,
+    int32_t* __restrict__ out_pos, int32_t* __restrict__ out_cnt) {
+  const int b = blockIdx.x / Hkv, h = blockIdx.x % Hkv;
+  const int tid = threadIdx.x;
+  const int32_t* ur = tab + off_units + kUnitInts * ((layer * B + b) * Hkv + h);
+  const int32_t N = tab[off_seqs + kSeqInts * b + S_N];
+  const int32_t kvo = tab[off_seqs + kSeqInts * b + S_KVOFF];
+  if (ur[U_KIND] != SEGPAGED_RETRIEVAL || N == 0) {
+    if (tid == 0) out_cnt[b * Hkv + h] = 0;
+    return;
+  }
+  __shared__ float sM[kLdsKeys];
+  __shared__ unsigned int hc[256];
+  __shared__ unsigned long long hs[256];
+  __shared__ float sm[kMaxGroup], sl[kMaxGroup], redf[kTopWaves];
+  __shared__ unsigned long long redu[kTopWaves];
+  __shared__ int wtot[kTopWaves];
+  __shared__ int s_chosen;
+  __shared__ unsigned long long s_acc;
+  const bool in_lds = N <= kLdsKeys;
+  float* Mg = ws_m + (int64_t)h * T + kvo;
+  // normalisers of the G heads over all N keys
+  const int nb = (N + kSelKeys - 1) / kSelKeys;
+  const float* part = ws_part + ((int64_t)h * B + b) * nblk * G * 2;
+  for (int g = 0; g < G; ++g) {
+    float m = -INFINITY;
+    for (int k = tid; k < nb; k += kTopThreads) m = fmaxf(m, part[((int64_t)k * G + g) * 2]);
+    const float mx = block_max_top(m, redf);
+    float l = 0.f;
+    for (int k = tid; k < nb; k += kTopThreads)
+      l += part[((int64_t)k * G + g) * 2 + 1] * exp2f(part[((int64_t)k * G + g) * 2] - mx);
+    const float ls = block_sum_top(l, redf);
+    if (tid == 0) { sm[g] = mx; sl[g] = 1.f / ls; }
+  }
+  __syncthreads();
+  // masses, and their total in fixed point
+  const float* S = ws_s + ((int64_t)h * T + kvo) * G;
+  const float inv_g = 1.f / (float)G;
+  unsigned long long tfx = 0;
+  for (int32_t j = tid; j < N; j += kTopThreads) {
+    float m = 0.f;
+    for (int g = 0; g < G; ++g) m += exp2f(S[(int64_t)j * G + g] - sm[g]) * sl[g];
+    m *= inv_g;
+    if (in_lds) sM[j] = m; else Mg[j] = m;
+    tfx += to_fx(m);
+  }
+  const unsigned long long total = block_sum_u64(tfx, redu);
+  const float* M = in_lds ? sM : Mg;
+  unsigned long long R = (unsigned long long)((double)p * (double)total);  // still to take
+  if (R == 0) R = 1;
+  uint32_t prefix = 0, mask = 0;
+  unsigned int c_eq = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int k = tid; k < 256; k += kTopThreads) { hc[k] = 0; hs[k] = 0; }
+    __syncthreads();
+    for (int32_t j = tid; j < N; j += kTopThreads) {
+      const float m = M[j];
+      const uint32_t u = __float_as_uint(m);
+      if ((u & mask) != prefix) continue;
+      const uint32_t bin = (u >> shift) & 255u;
+      atomicAdd(&hc[bin], 1u);
+      atomicAdd(&hs[bin], to_fx(m));
+    }
+    __syncthreads();
+    if (tid == 0) {  // the bin holding the last value taken, from the largest bin down
+      unsigned long long acc = 0;
+      int chosen = -1, lowest = -1;
+      for (int k = 255; k >= 0; --k) {
+        if (hc[k] == 0) continue;
+        lowest = k;
+        if (acc + hs[k] >= R) { chosen = k; break; }
+        acc += hs[k];
+      }
+      if (chosen < 0) {  // every candidate (masses below the fixed-point step)
+        chosen = lowest;
+        acc -= hs[lowest];
+      }
+      s_chosen = chosen;
+      s_acc = acc;
+    }
+    __syncthreads();
+    R -= s_acc;
+    prefix |= (uint32_t)s_chosen << shift;
+    mask |= 255u << shift;
+    c_eq = hc[s_chosen];
+    __syncthreads();
+  }
+  // keys of mass above the threshold, then the first t (by position) equal to it
+  const unsigned long long tau_fx = to_fx(__uint_as_float(prefix));
+  int t = (int)c_eq;
+  if (tau_fx > 0) t = (int)min((unsigned long long)c_eq, max(1ull, (R + tau_fx - 1) / tau_fx));
+  const int32_t per = (N + kTopThreads - 1) / kTopThreads;
+  const int32_t lo = min(N, tid * per), hi = min(N, lo + per);
+  int ties = 0;
+  for (int32_t j = lo; j < hi; ++j) ties += __float_as_uint(M[j]) == prefix;
+  int ties_total;
+  const int tie_base = block_scan_top(ties, wtot, ties_total);
+  int nsel = 0, tr = tie_base;
+  for (int32_t j = lo; j < hi; ++j) {
+    const uint32_t u = __float_as_uint(M[j]);
+    nsel += u > prefix || (u == prefix && tr < t);
+    tr += u == prefix;
+  }
+  int nsel_total;
+  int pos = block_scan_top(nsel, wtot, nsel_total);
+  int32_t* out = out_pos + (int64_t)h * T + kvo;
+  tr = tie_base;
+  for (int32_t j = lo; j < hi; ++j) {
+    const uint32_t u = __float_as_uint(M[j]);
+    if (u > prefix || (u == prefix && tr < t)) out[pos++] = j;
+    tr += u == prefix;
+  }
+  if (tid == 0) out_cnt[b * Hkv + h] = nsel_total;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+SEGPAGED_API int segpaged_select_topp(const segpaged_plan* pl, int32_t layer, const void* q,
+                                      const void* k_dense, const int32_t* d_table, float scale,
+                                      float p, int32_t* out_pos, int32_t* out_cnt, void* workspace,
+                                      int64_t workspace_bytes, void* stream) {
+  if (!pl || !q || !k_dense || !d_table || !out_pos || !out_cnt || !workspace)
+    return SEGPAGED_EINVAL;
+  if (!aligned16(q) || !aligned16(k_dense) || !aligned4(d_table) || !aligned4(out_pos) ||
+      !aligned4(out_cnt) || !aligned16(workspace))
+    return SEGPAGED_EINVAL;
+  if (!(scale > 0.f) || !std::isfinite(scale) || !(p > 0.f) || !(p <= 1.f)) return SEGPAGED_EINVAL;
+  if (layer < 0 || layer >= pl->L) return SEGPAGED_ESTATE;
+  const int64_t B = pl->B, Hkv = pl->Hkv, G = pl->G, T = pl->kv_rows;
+  int64_t nmax = 0;
+  for (int64_t b = 0; b < B; ++b)
+    nmax = std::max<int64_t>(nmax, pl->buf[pl->off_seqs + kSeqInts * b + S_N]);
+  const int64_t nblk = std::max<int64_t>(1, (nmax + kSelKeys - 1) / kSelKeys);
+  const int64_t s_floats = Hkv * T * G, m_floats = Hkv * T, part_floats = Hkv * B * nblk * G * 2;
+  const int64_t need = 4 * (s_floats + m_floats + part_floats);
+  if (workspace_bytes < need) return SEGPAGED_ENOSPACE;
+  float* ws_s = (float*)workspace;
+  float* ws_m = ws_s + s_floats;
+  float* ws_part = ws_m + m_floats;
+  hipStream_t st = (hipStream_t)stream;
+  const float c = scale * kLog2eSel;
+  const dim3 g1((unsigned)nblk, (unsigned)(B * Hkv)), blk(kSelThreads);
+  if (pl->D == 128)
+    hipLaunchKernelGGL(select_scores_kernel<128>, g1, blk, 0, st, d_table, (int32_t)pl->off_seqs,
+                       (int32_t)pl->off_units, layer, (int32_t)B, (int32_t)Hkv, (int32_t)G, pl->Hq,
+                       (int32_t)T, (const uint16_t*)q, (const uint16_t*)k_dense, c, ws_s, ws_part,
+                       (int32_t)nblk);
+  else
+    hipLaunchKernelGGL(select_scores_kernel<64>, g1, blk, 0, st, d_table, (int32_t)pl->off_seqs,
+                       (int32_t)pl->off_units, layer, (int32_t)B, (int32_t)Hkv, (int32_t)G, pl->Hq,
+                       (int32_t)T, (const uint16_t*)q, (const uint16_t*)k_dense, c, ws_s, ws_part,
+                       (int32_t)nblk);
+  if (hipGetLastError() != hipSuccess) return SEGPAGED_EHIP;
+  hipLaunchKernelGGL(select_topp_kernel, dim3((unsigned)(B * Hkv)), dim3(kTopThreads), 0, st,
+                     d_table, (int32_t)pl->off_seqs, (int32_t)pl->off_units, layer, (int32_t)B,
+                     (int32_t)Hkv, (int32_t)G, (int32_t)T, ws_s, ws_part, (int32_t)nblk, ws_m, p,
+                     out_pos, out_cnt);
+  return hipGetLastError() == hipSuccess ? SEGPAGED_OK : SEGPAGED_EHIP;
+}
+
+}  // extern "C"

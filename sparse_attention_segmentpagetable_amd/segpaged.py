@@ -45,7 +45,7 @@ class Sizes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "num_pages", "pool_pages", "pool_bytes", "table_int32s", "table_len", "num_units",
         "q_rows", "kv_rows", "decode_items", "prefill_items", "decode_workspace_bytes",
-        "prefill_workspace_bytes")]
+        "prefill_workspace_bytes", "select_workspace_bytes")]
 
     def as_dict(self) -> Dict[str, int]:
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -79,6 +79,8 @@ def _lib():
         lib.segpaged_plan_stats.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(Stats)]
         lib.segpaged_build.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
         lib.segpaged_plan_append.argtypes = [vp, _i32p]
+        lib.segpaged_select_topp.argtypes = [vp, ctypes.c_int32, vp, vp, vp, ctypes.c_float,
+                                             ctypes.c_float, vp, vp, vp, ctypes.c_int64, vp]
         lib.segpaged_append.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
         lib.segpaged_prefill.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_float,
                                          vp, vp, vp, ctypes.c_int64, vp]
@@ -305,6 +307,28 @@ def append(plan: Plan, layer: int, k_new, v_new, table, k_pool, v_pool, stream=N
                                   _ptr(table, "t"), _ptr(k_pool, "kp", torch.bfloat16),
                                   _ptr(v_pool, "vp", torch.bfloat16), _stream(stream)),
            "segpaged_append")
+
+
+def select_topp(plan: Plan, layer: int, q, k_dense, table, scale: float, p: float, out_pos,
+                out_cnt, workspace, stream=None):
+    """segpaged_select_topp: the top-p retrieval set of every (sequence, retrieval
+    head) of `layer` from the decode row's attention over the dense history.
+    out_pos int32 [Hkv][T_total], out_cnt int32 [B * Hkv]."""
+    import torch
+    _ptr(q, "q", torch.bfloat16)
+    _need(q, plan.num_seqs * plan.num_q_heads * plan.head_dim, "q")
+    _ptr(k_dense, "k_dense", torch.bfloat16)
+    _need(k_dense, plan.sizes.kv_rows * plan.num_kv_heads * plan.head_dim, "k_dense")
+    _ptr(out_pos, "out_pos", torch.int32)
+    _need(out_pos, plan.num_kv_heads * plan.sizes.kv_rows, "out_pos")
+    _ptr(out_cnt, "out_cnt", torch.int32)
+    _need(out_cnt, plan.num_seqs * plan.num_kv_heads, "out_cnt")
+    wsb = workspace.numel() * workspace.element_size()
+    _check(_lib().segpaged_select_topp(plan.handle, layer, _ptr(q, "q"), _ptr(k_dense, "k_dense"),
+                                       _ptr(table, "t", torch.int32), float(scale), float(p),
+                                       _ptr(out_pos, "out_pos"), _ptr(out_cnt, "out_cnt"),
+                                       _ptr(workspace, "ws"), wsb, _stream(stream)),
+           "segpaged_select_topp")
 
 
 def decode(plan: Plan, layer: int, q, table, k_pool, v_pool, scale: float, o, lse=None,

@@ -1,0 +1,134 @@
+"""Retrieval-set selection on the GPU (segpaged_select_topp) against the oracle
+(oracle/select.py). Where fp32 rounding decides between keys of nearly equal mass
+several sets are correct, so the test compares what is unique -- every key whose
+oracle mass is clearly above the oracle's threshold is taken, none clearly below
+-- and checks that the set reaches p and is minimal; exact ties (identical keys)
+must go by position. Then the selected sets drive a plan + build + decode."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention as OA
+from oracle import select as OS
+from tests.gpu_util import lse_parity, parity, to_dev, to_f64
+
+sp = pytest.importorskip("sparse_attention_segmentpagetable_amd")
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _spec(hd, hq, n, retr=None):
+    kind = [W.RETRIEVAL, W.LOCAL, W.GLOBAL, W.RETRIEVAL]
+    if retr is None:  # the sets before any selection: empty
+        retr = {(b, l, h): np.zeros(0, np.int32) for b in range(len(n)) for l in range(2)
+                for h in range(2) if kind[l * 2 + h] == W.RETRIEVAL}
+    s = W.Spec(name="select", num_layers=2, num_q_heads=hq, num_kv_heads=2, head_dim=hd,
+               page_size=64, seq_len=list(n), first_query_pos=[0] * len(n), kind=kind,
+               sink=[0, 4, 0, 0], window=[1, 100, 1, 1], retrieval=retr, seed=41)
+    return W.decode_form(s)
+
+
+def _scaled_q(spec, layer, factor):
+    qb = W.q_bits(spec, layer)
+    q = OA.bf16_bits_to_f64(qb) * factor  # a power of two: exact in bf16
+    return (q.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _run(spec, layer, qb, kb, p):
+    plan = sp.Plan(spec)
+    bufs = plan.allocate(DEV, workspace=False)
+    vb = kb  # values unused by the selection
+    sp.build(plan, layer, to_dev(kb), to_dev(vb), bufs["table"], bufs["k_pool"], bufs["v_pool"])
+    T, Hkv = plan.sizes.kv_rows, spec.num_kv_heads
+    out_pos = torch.full((Hkv * T,), -7, dtype=torch.int32, device=DEV)
+    out_cnt = torch.full((spec.num_seqs * Hkv,), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(plan.sizes.select_workspace_bytes // 4, dtype=torch.float32, device=DEV)
+    sp.select_topp(plan, layer, to_dev(qb), to_dev(kb), bufs["table"], 1 / np.sqrt(spec.head_dim),
+                   p, out_pos, out_cnt, ws)
+    torch.cuda.synchronize()
+    return out_pos.cpu().numpy().reshape(Hkv, T), out_cnt.cpu().numpy().reshape(-1, Hkv)
+
+
+CASES = [("d128-g4", 128, 8, (700, 1029, 64)), ("d64-g16", 64, 32, (3000, 1, 257))]
+
+
+@pytest.mark.parametrize("name,hd,hq,n", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("p", [0.5, 0.9, 0.99, 1.0])
+def test_select_topp_against_oracle(name, hd, hq, n, p):
+    spec = _spec(hd, hq, n)
+    kvo, G = spec.kv_row_offsets(), spec.group
+    for layer in range(spec.num_layers):
+        qb = _scaled_q(spec, layer, 4.0)
+        kb, _ = W.kv_bits(spec, layer)
+        pos, cnt = _run(spec, layer, qb, kb, p)
+        pos2, cnt2 = _run(spec, layer, qb, kb, p)
+        assert np.array_equal(cnt, cnt2)  # the same set on every call
+        for b, nb in enumerate(n):
+            for h in range(spec.num_kv_heads):
+                kind, _, _ = spec.head_class(layer, h)
+                c = int(cnt[b, h])
+                if kind != W.RETRIEVAL:
+                    assert c == 0
+                    continue
+                got = pos[h, kvo[b]:kvo[b] + c]
+                assert np.array_equal(got, pos2[h, kvo[b]:kvo[b] + c])
+                mass = OS.key_mass(qb[b, h * G:(h + 1) * G], kb[kvo[b]:kvo[b] + nb, h],
+                                   1 / np.sqrt(hd))
+                tau = OS.threshold(mass, p)
+                assert np.all(np.diff(got) > 0) and got[0] >= 0 and got[-1] < nb
+                sel = set(int(x) for x in got)
+                # masses below fp32's resolution of the total (1e-6 of it) are not
+                # ordered reliably: they are in the set or not
+                must = set(np.nonzero(mass > max(tau * (1 + 1e-4), 1e-6))[0].tolist())
+                assert must <= sel, (name, b, h, len(must - sel))
+                assert all(mass[j] >= tau * (1 - 1e-4) for j in sel)
+                tot = mass[got].sum()
+                assert tot >= p - 1e-5, (tot, p)
+                assert tot - mass[got].min() < p + 1e-5 or p == 1.0
+                ref = OS.top_p(mass, p)
+                print(f"[select] {name} p={p} L{layer} b{b} h{h}: {c} keys (oracle {len(ref)})",
+                      flush=True)
+
+
+def test_select_ties_go_by_position():
+    spec = _spec(128, 8, (1000, 333))
+    kb, _ = W.kv_bits(spec, 0)
+    kb[:] = kb[0]  # every key the same: equal masses, exactly, on both sides
+    qb = _scaled_q(spec, 0, 1.0)
+    for p in (0.1, 0.5, 0.9):
+        pos, cnt = _run(spec, 0, qb, kb, p)
+        kvo = spec.kv_row_offsets()
+        for b, nb in enumerate(spec.seq_len):
+            c = int(cnt[b, 0])
+            assert abs(c - p * nb) <= 1.0 and np.array_equal(pos[0, kvo[b]:kvo[b] + c], np.arange(c))
+
+
+def test_selected_sets_drive_a_decode():
+    base = _spec(128, 8, (700, 1029, 64))
+    qb = _scaled_q(base, 0, 4.0)
+    kb, vb = W.kv_bits(base, 0)
+    pos, cnt = _run(base, 0, qb, kb, 0.9)
+    kvo = base.kv_row_offsets()
+    retr = {}
+    for b in range(base.num_seqs):
+        for h in range(base.num_kv_heads):
+            if base.head_class(0, h)[0] == W.RETRIEVAL:
+                retr[(b, 0, h)] = pos[h, kvo[b]:kvo[b] + int(cnt[b, h])].astype(np.int32)
+            if base.head_class(1, h)[0] == W.RETRIEVAL:
+                retr[(b, 1, h)] = np.zeros(0, np.int32)
+    spec = replace(base, retrieval=retr)
+    plan = sp.Plan(spec)
+    bufs = plan.allocate(DEV)
+    sp.build(plan, 0, to_dev(kb), to_dev(vb), bufs["table"], bufs["k_pool"], bufs["v_pool"])
+    q = to_dev(qb)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=DEV)
+    sp.decode(plan, 0, q, bufs["table"], bufs["k_pool"], bufs["v_pool"], 1 / np.sqrt(128), o, lse,
+              workspace=bufs["workspace"])
+    torch.cuda.synchronize()
+    ref, ref_lse = OA.attention(spec, 0, qb, kb, vb, 1 / np.sqrt(128))
+    parity(to_f64(o), ref, "decode over selected retrieval sets")
+    lse_parity(lse.cpu().numpy(), ref_lse, "decode over selected retrieval sets")
