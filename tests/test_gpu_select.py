@@ -52,7 +52,8 @@ def _run(spec, layer, qb, kb, p):
     return out_pos.cpu().numpy().reshape(Hkv, T), out_cnt.cpu().numpy().reshape(-1, Hkv)
 
 
-CASES = [("d128-g4", 128, 8, (700, 1029, 64)), ("d64-g16", 64, 32, (3000, 1, 257))]
+CASES = [("d128-g4", 128, 8, (700, 1029, 64)), ("d64-g16", 64, 32, (3000, 1, 257)),
+         ("d128-g8-long", 128, 16, (40000, 32768, 32769))]  # masses past the LDS limit
 
 
 @pytest.mark.parametrize("name,hd,hq,n", CASES, ids=[c[0] for c in CASES])
