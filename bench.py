@@ -765,6 +765,33 @@ def dense_mask_baseline(torch, W, pspec, dspec, k0, v0, q0, dev, pre_ms_layer, d
                       "speedup_vs_dense_mask": round(t_layer / pre_ms_layer, 2)}
     del q, k, v, mask
     log(f"dense-mask prefill: {t_layer:.1f} ms/layer (extrapolated) vs {pre_ms_layer:.1f}")
+    # the same layer through our own kernel with every head global: causal
+    # attention over the whole context, no block skipping -- separates the gain of
+    # the kernel (dense-mask SDPA vs this) from that of the layout (this vs SegPaged)
+    from dataclasses import replace as _replace
+    import sparse_attention_segmentpagetable_amd as sp
+    gspec = _replace(pspec, num_layers=1, kind=[W.GLOBAL] * Hkv, sink=[0] * Hkv, window=[1] * Hkv)
+    gplan = sp.Plan(gspec)
+    gb = gplan.allocate(dev, workspace=False)
+    sp.build(gplan, 0, k0, v0, gb["table"], gb["k_pool"], gb["v_pool"])
+    go = torch.empty_like(q0)
+    sp.prefill(gplan, 0, q0, gb["table"], gb["k_pool"], gb["v_pool"], 1 / math.sqrt(D), go)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    sp.prefill(gplan, 0, q0, gb["table"], gb["k_pool"], gb["v_pool"], 1 / math.sqrt(D), go)
+    e1.record()
+    torch.cuda.synchronize()
+    t_glob = e0.elapsed_time(e1)
+    gflops = 4 * D * G * gplan.stats(0)["prefill_pairs"]
+    res["prefill_all_global_own_kernel"] = {
+        "ms_per_layer": round(t_glob, 2), "tflops": round(gflops / (t_glob * 1e-3) / 1e12, 1),
+        "kernel_gain_vs_dense_mask": round(t_layer / t_glob, 2),
+        "layout_gain_vs_all_global": round(t_glob / pre_ms_layer, 2)}
+    log(f"all-global prefill with our kernel: {t_glob:.1f} ms/layer "
+        f"({gflops / (t_glob * 1e-3) / 1e12:.0f} TF/s)")
+    del gplan, gb, go
+    torch.cuda.empty_cache()
     # decode: a few layers of the decode workload on dense K/V [B, Hkv, n, D]
     B, n = dspec.num_seqs, args.decode_n
     nl = 4
