@@ -56,6 +56,8 @@ def parse():
                     help="also run a plain 1 GiB elementwise pass (the FETCH/WRITE_SIZE scale reference)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of this script into the traffic file")
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                    help="turn a rocprofv3 --pmc run with the MFMA counters into its summary")
     return ap.parse_args()
 
 
@@ -106,6 +108,61 @@ def summarize_pmc(fetch_dir, write_dir):
     print(json.dumps(out))
 
 
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_prefill.json")
+
+
+def summarize_mfma(pmc_dir):
+    """Matrix-core busy fraction and effective clock of the prefill kernel from a
+    rocprofv3 run with --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16
+    SQ_BUSY_CYCLES GRBM_GUI_ACTIVE: busy = MFMA-busy cycles / (GPU-active cycles x
+    SIMDs); clock = GPU-active cycles / dispatch duration (the GRBM counter comes
+    summed over the XCDs: divided by their number); bf16 MFMA flops = MOPS x 512."""
+    import csv
+    import glob
+    import re
+    simds, xcc = 1024, 8
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*agent_info.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if int(r.get("Simd_Count", 0) or 0) > 0:
+                simds, xcc = int(r["Simd_Count"]), int(r["Num_Xcc"])
+    per = {}
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            m = re.search(r"\b(prefill_kernel|decode_partial_kernel)<\d+[,>]", r["Kernel_Name"])
+            if not m:
+                continue
+            d = per.setdefault((m.group(1), r["Dispatch_Id"]), {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    out = {"kernels_sha256_16": kernels_hash(), "per_kernel": {}}
+    for k in ("prefill_kernel", "decode_partial_kernel"):
+        rows = [v for (kk, _), v in per.items() if kk == k and "GRBM_GUI_ACTIVE" in v]
+        if not rows:
+            continue
+        busy = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"] for v in rows)
+        act = sum(v["GRBM_GUI_ACTIVE"] for v in rows) / xcc
+        ns = sum(v["ns"] for v in rows)
+        flops = sum(v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for v in rows) * 512
+        out["per_kernel"][k] = {"launches": len(rows),
+                                "mfma_busy_frac": round(busy / (act * simds), 4),
+                                "effective_clock_ghz": round(act / ns, 3),
+                                "mfma_bf16_flops_per_launch": round(flops / len(rows))}
+    json.dump(out, open(MFMA_FILE, "w"), indent=1)
+    print(json.dumps(out))
+
+
+def measured_mfma(kernel):
+    """Matrix-core busy fraction and effective clock from the committed counter
+    run, or None when the kernel source changed since it was taken."""
+    try:
+        t = json.load(open(MFMA_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernels_sha256_16") != kernels_hash():
+        return None
+    return t.get("per_kernel", {}).get(kernel)
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch from the committed counter runs, or None when the
     kernel source changed since they were taken."""
@@ -123,6 +180,9 @@ def main():
     args = parse()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -295,6 +355,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(pre_tflops / BF16_PEAK_TFS, 4),
             "frac_of_measured_ceiling": round(pre_tflops / ceil["mfma_bf16_tflops"], 4),
+            "mfma_counters": measured_mfma("prefill_kernel"),
             "traffic": measured_traffic("prefill_kernel"),
             "traffic_unit": "bytes per launch (one layer)",
         },
