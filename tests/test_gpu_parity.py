@@ -30,12 +30,13 @@ def _mixed(q0=(0, 30), free=None, cap=0, n=(37, 45), hd=64, ps=16):
                   free_list=free, capacity_pages=cap, seed=11)
 
 
-def _long_mixed(form, hd=128, ps=64):
-    """Several tiles, ragged tails, two-segment local heads, page boundaries."""
+def _long_mixed(form, hd=128, ps=64, g=8):
+    """Several tiles, ragged tails, two-segment local heads, page boundaries; g Q heads
+    per KV head (a tile holds 256 // g positions, so g = 3 leaves a row of it unused)."""
     kind = [W.GLOBAL, W.LOCAL, W.LOCAL, W.RETRIEVAL]
     lens = [700, 333, 1029]
     retr = W.seeded_retrieval_sets(lens, kind, 1, 4, 7, 0.1)
-    s = W.Spec(name="long-mixed", num_layers=1, num_q_heads=32, num_kv_heads=4, head_dim=hd,
+    s = W.Spec(name="long-mixed", num_layers=1, num_q_heads=4 * g, num_kv_heads=4, head_dim=hd,
                page_size=ps, seq_len=lens, first_query_pos=[0, 0, 0], kind=kind,
                sink=[4, 4, 0, 0], window=[1, 130, 64, 1], retrieval=retr, seed=12)
     if form == "decode":
@@ -118,6 +119,10 @@ PREFILL_SPECS = [
     ("long-mixed", lambda: _long_mixed("prefill")),
     ("long-mixed-mid", lambda: _long_mixed("mid")),
     ("long-mixed-p16", lambda: _long_mixed("prefill", ps=16)),
+    ("long-mixed-p128", lambda: _long_mixed("prefill", ps=128)),
+    ("long-mixed-g1", lambda: _long_mixed("prefill", g=1)),
+    ("long-mixed-g3-d64", lambda: _long_mixed("prefill", hd=64, g=3)),
+    ("long-mixed-g16", lambda: _long_mixed("prefill", g=16)),
     ("mistral-small", lambda: W.mistral_layer("prefill", seqs=2, n=777, window=128)),
     ("llama-g8-small", lambda: replace(W.long_prefill(num_layers=2, n=1500, window=256),
                                        seq_len=[1500, 260], first_query_pos=[0, 0])),
@@ -141,6 +146,10 @@ DECODE_SPECS = [
     ("mixed-free", lambda: replace(_mixed(q0=(36, 44), free=W.seeded_free_list(64, 2), cap=64))),
     ("long-mixed", lambda: _long_mixed("decode")),
     ("long-mixed-p16", lambda: _long_mixed("decode", ps=16)),
+    ("long-mixed-p128", lambda: _long_mixed("decode", ps=128)),
+    ("long-mixed-g1", lambda: _long_mixed("decode", g=1)),
+    ("long-mixed-g3-d64", lambda: _long_mixed("decode", hd=64, g=3)),
+    ("long-mixed-g16", lambda: _long_mixed("decode", g=16)),
     ("mistral-small", lambda: W.mistral_layer("decode", seqs=3, n=2000, window=300)),
     ("llama70b-small", lambda: W.llama70b_decode(num_layers=3, seqs=2, n=3000, window=512)),
     ("varlen-small", lambda: W.mixed_varlen_decode(seqs=5, num_layers=2, lo=100, hi=6000,
