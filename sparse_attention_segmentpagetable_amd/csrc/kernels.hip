@@ -492,21 +492,14 @@ __device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p) {
   return v;
 }
 
-// LDS-DMA: each lane's 16 (or 4) bytes at gsrc land at lds_wave_base + lane * 16
-// (or * 4). Issued as inline asm so the compiler's wait-count pass does not see
-// an LDS write it cannot place in the ring and drain every transfer in flight
-// before each LDS read; the kernel waits on vmcnt for exactly the block it
-// needs, then passes a barrier. M0 carries the wave's LDS base (the kernel uses
+// LDS-DMA: each lane's 4 bytes at gsrc land at lds_wave_base + lane * 4 (the
+// 16-byte forms below: + lane * 16). Issued as inline asm so the compiler's
+// wait-count pass does not see an LDS write it cannot place in the ring and
+// drain every transfer in flight before each LDS read; the kernel waits on
+// vmcnt for exactly the block it needs, then passes a barrier. M0 carries the wave's LDS base (the kernel uses
 // M0 for nothing else).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-__device__ __forceinline__ void lds_dma16(const uint16_t* gsrc, uint16_t* lds_wave_base) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gsrc), "s"(m0v)
-               : "memory");
 }
 __device__ __forceinline__ void lds_dma4(const int32_t* gsrc, int32_t* lds_wave_base) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
@@ -515,7 +508,7 @@ __device__ __forceinline__ void lds_dma4(const int32_t* gsrc, int32_t* lds_wave_
                : "v"(gsrc), "s"(m0v)
                : "memory");
 }
-// The same transfer with the LDS destination as a wave-uniform byte address,
+// The 16-byte transfer with the LDS destination as a wave-uniform byte address,
 // and a variant whose source is a wave-uniform 64-bit base in SGPRs plus a
 // per-lane 32-bit byte offset (no per-lane address arithmetic).
 __device__ __forceinline__ void lds_dma16_a(const uint16_t* gsrc, uint32_t lds_base) {
@@ -553,11 +546,6 @@ __device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "m
 // s_waitcnt vmcnt(n) lgkmcnt(0): also every LDS read and scalar load issued so far
 #define WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt((0x0070) | ((n) & 15) | (((n) >> 4) << 14))
 
-// acc + the two bf16 halves of w (v_dot2_f32_bf16 against (1, 1))
-__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
-}
 
 // Nonempty block runs of a tile in visiting order: first block within its
 // segment, block count, segment.

@@ -45,11 +45,6 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
   return v;
 }
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
 
 // Scores of 256 keys for the G query heads of (b, h): a wave reads 4 key rows per
 // load, 16 lanes per row (16 bytes each, coalesced), and the 16 partial dot
