@@ -292,6 +292,20 @@ def main():
     dec_ms = [a.elapsed_time(b) for a, b in reps]
     dec_med = float(np.median(dec_ms))
 
+    # the same decode as one launch per layer (each reads its own layer's pages,
+    # about 1/80 of the K/V, so nothing carries over from one launch to the next)
+    layer_reps = []
+    for _ in range(4):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for l in range(args.decode_layers):
+            sp.decode(dplan, l, q_dec[l], db["table"], db["k_pool"], db["v_pool"], scale,
+                      o_dec[l], lse_dec[l], workspace=db["workspace"])
+        e1.record(stream)
+        layer_reps.append((e0, e1))
+    torch.cuda.synchronize()
+    dec_layer_ms = float(np.median([a.elapsed_time(b) for a, b in layer_reps[1:]]))
+
     ceil = measure_ceilings(torch, dev, stream, log)
 
     pre_ms_layer = float(np.mean(dur["prefill"]))
@@ -346,6 +360,13 @@ def main():
             "reps": args.decode_reps,
             "kv_bytes": decode_bytes,
             "ms_in_steps": [round(x, 4) for x in dur["decode"]],
+            "per_layer_launches": {
+                "launches": args.decode_layers,
+                "ms_all_layers": round(dec_layer_ms, 4),
+                "ms_per_layer": round(dec_layer_ms / args.decode_layers, 4),
+                "gbs": round(decode_bytes / (dec_layer_ms * 1e-3) / 1e9, 1),
+                "frac_of_hbm_peak": round(decode_bytes / (dec_layer_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            },
         },
         "roofline": {
             "kernel": "prefill_kernel",

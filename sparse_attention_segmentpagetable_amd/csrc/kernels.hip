@@ -182,8 +182,11 @@ __global__ __launch_bounds__(256) void append_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// decode, split-K. One wave per work item (unit, slots [lo, hi)), all of which
-// the decode row sees. Per 32-key step, with v_mfma_f32_16x16x32_bf16:
+// decode, split-K. One wave per part of a work item (unit, slots [lo, hi)), all
+// of which the decode row sees: an item's 32-slot steps are dealt to 2^sub_log2
+// consecutive parts (one part unless a launch has too few items to fill the
+// chip), each writing its own partial. Per 32-key step, with
+// v_mfma_f32_16x16x32_bf16:
 //   S^T[16 keys][16 cols] = K[keys][D] . Q^T[D][cols]   (cols = the G query heads)
 //   O^T[16 dims][16 cols] += V^T[dims][32 keys] . P^T[32 keys][cols]
 // The key order inside an S^T tile is permuted so that the 8 keys a lane holds
@@ -193,33 +196,45 @@ __global__ __launch_bounds__(256) void append_kernel(
 template <int D>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
     const int32_t* __restrict__ tab, int32_t off_units, int32_t off_pages, int32_t off_dec,
-    int32_t item_b, int32_t item_e, const uint16_t* __restrict__ q, int64_t q_layer_stride,
-    const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, float* __restrict__ ws,
-    int32_t G, int32_t Hq, int32_t P, int32_t log2P, float c) {
+    int32_t item_b, int32_t item_e, int32_t sub_log2, const uint16_t* __restrict__ q,
+    int64_t q_layer_stride, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
+    float* __restrict__ ws, int32_t G, int32_t Hq, int32_t P, int32_t log2P, float c) {
   constexpr int KS = D / 32;  // k-steps of the QK^T contraction
   constexpr int DT = D / 16;  // 16-row tiles of O^T
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int32_t it = item_b + (int32_t)blockIdx.x * 4 + wave;
+  const int32_t wid = (int32_t)blockIdx.x * 4 + wave;
+  const int32_t it = item_b + (wid >> sub_log2), part = wid & ((1 << sub_log2) - 1);
   if (it >= item_e) return;
   const int32_t* item = tab + off_dec + kDecItemInts * it;
   // slots [lo, hi) minus the gap [gap_lo, gap_hi): the zero tail of a sink page
   // between a local head's sink segment and its window segment
-  const int32_t u = item[0], lo = item[1], hi = item[2], gap_lo = item[3];
+  const int32_t u = item[0], gap_lo = item[3];
+  int32_t lo = item[1], hi = item[2];
   const int32_t* ur = tab + off_units + kUnitInts * u;
   const int32_t b = ur[U_B], l = ur[U_L], h = ur[U_H];
   const int32_t* pages = tab + off_pages + ur[U_PAGEOFF];
   const int n = lane & 15, g = lane >> 4;
   const int64_t PD = (int64_t)P * D;
-  const int32_t lo8 = lo & ~7;
-
   const int32_t gap_hi = gap_lo > 0 ? ((gap_lo + P - 1) >> log2P) << log2P : 0;
+  // this part's steps: the item's steps of 32 slots from lo & ~7, dealt in equal runs
+  int32_t s_first = lo & ~7;
+  {
+    const int32_t nst = (hi - s_first + 31) >> 5;
+    const int32_t per = (nst + (1 << sub_log2) - 1) >> sub_log2;
+    const int32_t st0 = min(part * per, nst), st1 = min(st0 + per, nst);
+    hi = min(hi, s_first + 32 * st1);
+    s_first += 32 * st0;
+    lo = max(lo, s_first);
+    while (s_first >= gap_lo && s_first + 32 <= gap_hi) s_first += 32;  // whole step in the gap
+  }
+  const int32_t lo8 = s_first;
 
   // a window of the item's page ids, one per lane; each step reads the ids it
   // needs with readlane into scalar registers, and the window moves on when a
   // step would leave it
   const int32_t pg_last = (hi - 1) >> log2P;
   int32_t pg_first = lo8 >> log2P;
-  int32_t pid_lane = pg_first + lane <= pg_last ? pages[pg_first + lane] : 0;
+  int32_t pid_lane = lo8 < hi && pg_first + lane <= pg_last ? pages[pg_first + lane] : 0;
 
   bf16x8 qf[KS];
   {
@@ -303,15 +318,17 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
       }
     mx = wave_max_xor(mx, 16);
     mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(m, mx * c);  // every step holds a visible key: finite
-    const float alpha = fast_exp2(m - m_new);
+    const float m_new = fmaxf(m, mx * c);
+    // a part's step can hold no key of the part: then every p and alpha are 0
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
     float p[8];
     float ps = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[4 * t + i] = fast_exp2(fmaf(st[t][i], c, -m_new));
+        p[4 * t + i] = fast_exp2(fmaf(st[t][i], c, -m_use));
         ps += p[4 * t + i];
       }
     lsum = lsum * alpha + ps;
@@ -336,6 +353,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     return s;
   };
   // two-deep register pipeline: the next step's operands are in flight while a step computes
+  // (a part without keys runs one step that loads nothing and leaves m, l, O as they are)
   int32_t s0 = lo8;
   load_step(s0, kbuf[0], vbuf[0]);
   for (;;) {
@@ -352,8 +370,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
-  if (n < G) {
-    float* w = ws + ((int64_t)(it - item_b) * G + n) * kWsStride<D>;
+  if (n < G) {  // a part without keys writes m = -inf, l = 0, O = 0
+    float* w = ws + ((((int64_t)(it - item_b) << sub_log2) + part) * G + n) * kWsStride<D>;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       *reinterpret_cast<f32x4*>(w + 16 * dt + 4 * g) = acc[dt];  // dims 16dt + 4g + i
@@ -373,8 +391,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 template <int D, int WPP>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const int32_t* __restrict__ tab, int32_t off_units, int32_t off_decunits, int32_t unit_b,
-    int32_t unit_e, int32_t item_b, const float* __restrict__ ws, int32_t G, int32_t Hq,
-    int32_t B, uint16_t* __restrict__ o, float* __restrict__ lse, int32_t all_layers) {
+    int32_t unit_e, int32_t item_b, int32_t sub_log2, const float* __restrict__ ws, int32_t G,
+    int32_t Hq, int32_t B, uint16_t* __restrict__ o, float* __restrict__ lse, int32_t all_layers) {
   constexpr int LPI = D / 4;        // lanes per item
   constexpr int IPW = 64 / LPI;     // items per wave at a time
   constexpr int NS = IPW * WPP;     // items per pair at a time
@@ -386,10 +404,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   if (u >= unit_e) return;          // uniform over the waves of a pair
   const int32_t* ur = tab + off_units + kUnitInts * u;
   const int32_t b = ur[U_B], l = ur[U_L], h = ur[U_H];
-  const int32_t ib = tab[off_decunits + 2 * u], ie = tab[off_decunits + 2 * u + 1];
+  // the unit's partial records: 2^sub_log2 per item
+  const int32_t ib = (tab[off_decunits + 2 * u] - item_b) << sub_log2;
+  const int32_t ie = (tab[off_decunits + 2 * u + 1] - item_b) << sub_log2;
   const int64_t row = (all_layers ? (int64_t)l * B * Hq : 0) + (int64_t)b * Hq + h * G + j;
   // record of (item it, query column j): D floats of O, then m (log2 units) and l
-  const float* rec0 = ws + ((int64_t)(ib - item_b) * G + j) * kWsStride<D>;
+  const float* rec0 = ws + ((int64_t)ib * G + j) * kWsStride<D>;
   const int64_t rstride = (int64_t)G * kWsStride<D>;
   // the unit's max over its items, one item per lane (every wave of the pair alike)
   float m = -INFINITY;
@@ -1433,9 +1453,21 @@ SEGPAGED_API int segpaged_decode(const segpaged_plan* pl, int32_t layer, const v
   if (layer < -1 || layer >= pl->L) return SEGPAGED_ESTATE;
   const Span sp = span_of(pl, layer);
   const int64_t nitems = sp.dec_e - sp.dec_b;
-  const int64_t need = nitems * (int64_t)pl->G * (pl->D + 4) * 4;
+  const int64_t rec_bytes = (int64_t)pl->G * (pl->D + 4) * 4;  // one partial (G columns)
+  const int64_t need = nitems * rec_bytes;
   if (need > 0 && (!workspace || !aligned16(workspace))) return SEGPAGED_EINVAL;
   if (workspace_bytes < need) return SEGPAGED_ENOSPACE;
+  // Parts per item: a launch with too few items to fill the chip (one layer of a
+  // plan whose split was sized for all layers) deals each item's steps to up to
+  // 16 waves, while a part keeps >= 256 keys and the workspace holds the partials.
+  int sub_log2 = 0;
+  {
+    const int64_t keys = layer < 0 ? pl->total.decode_tokens : pl->stats[layer].decode_tokens;
+    const int64_t recs = workspace_bytes / rec_bytes;
+    while (sub_log2 < kDecMaxPartsLog2 && (nitems << sub_log2) < kDecFillWaves &&
+           (nitems << (sub_log2 + 1)) <= recs && keys / (nitems << (sub_log2 + 1)) >= 256)
+      ++sub_log2;
+  }
   const int64_t nunits = sp.unit_e - sp.unit_b;
   if (nunits == 0) return SEGPAGED_OK;
   hipStream_t st = (hipStream_t)stream;
@@ -1446,31 +1478,32 @@ SEGPAGED_API int segpaged_decode(const segpaged_plan* pl, int32_t layer, const v
   auto* vpp = (const uint16_t*)v_pool;
   auto* ws = (float*)workspace;
   if (nitems > 0) {
-    const dim3 grid((unsigned)((nitems + 3) / 4)), block(256);
+    const dim3 grid((unsigned)(((nitems << sub_log2) + 3) / 4)), block(256);
     if (pl->D == 128)
       hipLaunchKernelGGL(decode_partial_kernel<128>, grid, block, 0, st, d_table,
                          (int32_t)pl->off_units, (int32_t)pl->off_pages, (int32_t)pl->off_dec,
-                         (int32_t)sp.dec_b, (int32_t)sp.dec_e, qq, qstride, kpp, vpp, ws, pl->G,
-                         pl->Hq, pl->P, pl->log2P, c);
+                         (int32_t)sp.dec_b, (int32_t)sp.dec_e, sub_log2, qq, qstride, kpp, vpp,
+                         ws, pl->G, pl->Hq, pl->P, pl->log2P, c);
     else
       hipLaunchKernelGGL(decode_partial_kernel<64>, grid, block, 0, st, d_table,
                          (int32_t)pl->off_units, (int32_t)pl->off_pages, (int32_t)pl->off_dec,
-                         (int32_t)sp.dec_b, (int32_t)sp.dec_e, qq, qstride, kpp, vpp, ws, pl->G,
-                         pl->Hq, pl->P, pl->log2P, c);
+                         (int32_t)sp.dec_b, (int32_t)sp.dec_e, sub_log2, qq, qstride, kpp, vpp,
+                         ws, pl->G, pl->Hq, pl->P, pl->log2P, c);
     int rc = check_launch();
     if (rc) return rc;
   }
   // Four waves per pair when some unit has many items and the pairs alone leave
   // the chip short of waves (under 64 per CU); otherwise four pairs per workgroup.
   const int64_t pairs = nunits * pl->G;
-  const int wpp = sp.max_unit_items > 16 && pairs < 64 * 256 ? 4 : 1;
+  const int wpp = (sp.max_unit_items << sub_log2) > 16 && pairs < 64 * 256 ? 4 : 1;
   const int64_t per_wg = 4 / wpp;
   const dim3 grid((unsigned)((pairs + per_wg - 1) / per_wg)), block(256);
   auto* oo = (uint16_t*)o;
 #define SEGPAGED_LAUNCH_COMBINE(DD, WW)                                                          \
   hipLaunchKernelGGL((decode_combine_kernel<DD, WW>), grid, block, 0, st, d_table,               \
                      (int32_t)pl->off_units, (int32_t)pl->off_decunits, (int32_t)sp.unit_b,     \
-                     (int32_t)sp.unit_e, (int32_t)sp.dec_b, ws, pl->G, pl->Hq, pl->B, oo, lse,  \
+                     (int32_t)sp.unit_e, (int32_t)sp.dec_b, sub_log2, ws, pl->G, pl->Hq, pl->B, \
+                     oo, lse,                                                                   \
                      (int32_t)(layer < 0))
   if (pl->D == 128) {
     if (wpp == 4) SEGPAGED_LAUNCH_COMBINE(128, 4); else SEGPAGED_LAUNCH_COMBINE(128, 1);

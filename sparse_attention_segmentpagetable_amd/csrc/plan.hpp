@@ -29,6 +29,8 @@ constexpr int kPrefillRows = 256; // query rows per prefill tile: G heads x (256
 constexpr int kBlockN = 32;       // keys per prefill block
 constexpr int kMaxGroup = 16;     // Q heads per KV head the decode kernel supports
 constexpr int kCtrInts = 16;      // prefill work counter line per layer (+1 for all layers)
+constexpr int kDecMaxPartsLog2 = 4;     // a decode item is dealt to at most 16 waves
+constexpr int64_t kDecFillWaves = 4096; // decode waves a launch aims for (16 per compute unit)
 
 struct LayerRange {
   int64_t unit_b, unit_e;   // units

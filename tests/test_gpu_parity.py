@@ -361,3 +361,60 @@ def test_decode_long_items_small_pages():
     ref, ref_lse = OA.attention(dspec, 0, qb, kb, vb)
     parity(o, ref, "decode long items P=16")
     lse_parity(lse, ref_lse, "decode long items P=16")
+
+
+def _parts_log2(nitems, keys, recs):
+    """Waves per decode item the library picks for a launch (a copy of its rule, so
+    the test can check that it runs the path it means to)."""
+    s = 0
+    while s < 4 and (nitems << s) < 4096 and (nitems << (s + 1)) <= recs and \
+            keys // (nitems << (s + 1)) >= 256:
+        s += 1
+    return s
+
+
+@pytest.mark.parametrize("ps", [16, 64])
+def test_decode_item_parts(ps):
+    """One layer of a two-layer plan with 4096-key items, launched alone with room
+    for more partials: each item is dealt to several waves (parts). Layer 0's local
+    head keeps sink 4 + window 60, one short item over the sink page and two window
+    pages, so with 4 parts one part starts in the sink page's zero tail and holds no
+    key (page 64), or gets no step at all (page 16). The same layers from the
+    all-layer call with the minimal workspace run one wave per item."""
+    kind = [W.GLOBAL, W.LOCAL, W.LOCAL, W.RETRIEVAL]
+    lens = [9000, 4400]
+    retr = W.seeded_retrieval_sets(lens, kind, 2, 2, 5, 0.2)
+    spec = W.decode_form(W.Spec(name="parts", num_layers=2, num_q_heads=8, num_kv_heads=2,
+                                head_dim=128, page_size=ps, seq_len=lens,
+                                first_query_pos=[0, 0], kind=kind, sink=[0, 4, 7, 0],
+                                window=[1, 60, 3000, 1], retrieval=retr, seed=21))
+    plan = sp.Plan(spec, decode_split_tokens=4096)
+    bufs = plan.allocate(DEV)
+    kvs = [W.kv_bits(spec, l) for l in range(2)]
+    sp.build(plan, -1, to_dev(np.stack([k for k, _ in kvs])), to_dev(np.stack([v for _, v in kvs])),
+             bufs["table"], bufs["k_pool"], bufs["v_pool"])
+    qs = [W.q_bits(spec, l) for l in range(2)]
+    scale = 1 / np.sqrt(128)
+    q_all = to_dev(np.stack(qs))
+    o_all = torch.empty_like(q_all)
+    lse_all = torch.empty(q_all.shape[:3], dtype=torch.float32, device=DEV)
+    sp.decode(plan, -1, q_all, bufs["table"], bufs["k_pool"], bufs["v_pool"], scale, o_all,
+              lse_all, workspace=bufs["workspace"])
+    big_ws = torch.empty(16 * bufs["workspace"].numel() + 4096, dtype=bufs["workspace"].dtype,
+                         device=DEV)
+    rec = spec.num_q_heads // spec.num_kv_heads * (128 + 4) * 4
+    for l in range(2):
+        st = plan.stats(l)
+        assert _parts_log2(st["decode_items"], st["decode_tokens"],
+                           big_ws.numel() * big_ws.element_size() // rec) == (2 if l == 0 else 3)
+        q = to_dev(qs[l])
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=DEV)
+        sp.decode(plan, l, q, bufs["table"], bufs["k_pool"], bufs["v_pool"], scale, o, lse,
+                  workspace=big_ws)
+        torch.cuda.synchronize()
+        ref, ref_lse = OA.attention(spec, l, qs[l], *kvs[l], scale=scale)
+        parity(to_f64(o), ref, f"decode parts L{l}")
+        lse_parity(lse.cpu().numpy(), ref_lse, f"decode parts L{l}")
+        parity(to_f64(o_all[l]), ref, f"decode one wave per item L{l}")
+        assert np.max(np.abs(to_f64(o) - to_f64(o_all[l]))) <= 2 ** -7  # fp32 merge order only
