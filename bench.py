@@ -306,6 +306,7 @@ def main():
     torch.cuda.synchronize()
     dec_layer_ms = float(np.median([a.elapsed_time(b) for a, b in layer_reps[1:]]))
 
+    xfer = page_transfer(torch, sp, dplan, db, dspec, stream, log)
     ceil = measure_ceilings(torch, dev, stream, log)
 
     pre_ms_layer = float(np.mean(dur["prefill"]))
@@ -367,6 +368,7 @@ def main():
                 "gbs": round(decode_bytes / (dec_layer_ms * 1e-3) / 1e9, 1),
                 "frac_of_hbm_peak": round(decode_bytes / (dec_layer_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             },
+            "page_transfer": xfer,
         },
         "roofline": {
             "kernel": "prefill_kernel",
@@ -408,6 +410,53 @@ def main():
         torch.cuda.empty_cache()
         out.update(extra_configs(torch, W, sp, dev, stream, log))
     print(json.dumps(out), flush=True)
+
+
+def page_transfer(torch, sp, plan, bufs, spec, stream, log):
+    """The decode cache moved as page streams (all layers in one call each way):
+    what a prefill machine would send a decode machine, against the dense K/V of
+    the same tokens. Export and import each read and write the stream's bytes."""
+    n = sp.stream_elems(plan, -1)
+    ks = torch.empty(n, dtype=torch.bfloat16, device=bufs["k_pool"].device)
+    vs = torch.empty_like(ks)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ts]))
+
+    ex_ms = timed(lambda: sp.export_pages(plan, -1, bufs["table"], bufs["k_pool"], bufs["v_pool"],
+                                          ks, vs))
+    im_ms = timed(lambda: sp.import_pages(plan, -1, ks, vs, bufs["table"], bufs["k_pool"],
+                                          bufs["v_pool"]))
+    stream_bytes = 2 * n * 2
+    st = plan.stats(-1)
+    retained = st["retained_tokens"] * 2 * spec.head_dim * 2
+    dense = 2 * spec.num_layers * spec.num_kv_heads * spec.head_dim * 2 * sum(spec.seq_len)
+    del ks, vs
+    torch.cuda.empty_cache()
+    log(f"page transfer: {stream_bytes / 1e9:.2f} GB stream (dense {dense / 1e9:.1f} GB, "
+        f"{dense / stream_bytes:.2f}x less), export {ex_ms:.2f} ms, import {im_ms:.2f} ms")
+    return {
+        "workload": "the llama70b-shaped decode cache (all layers) as K and V page streams",
+        "stream_bytes": stream_bytes,
+        "retained_kv_bytes": retained,
+        "dense_kv_bytes": dense,
+        "dense_over_stream": round(dense / stream_bytes, 3),
+        "export_ms": round(ex_ms, 3),
+        "import_ms": round(im_ms, 3),
+        "export_hbm_gbs": round(2 * stream_bytes / (ex_ms * 1e-3) / 1e9, 1),
+        "import_hbm_gbs": round(2 * stream_bytes / (im_ms * 1e-3) / 1e9, 1),
+    }
 
 
 def measure_ceilings(torch, dev, stream, log):

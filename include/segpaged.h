@@ -13,7 +13,8 @@
  *         mask-free fused varlen kernel and the dense+mask equivalence check;
  *         section 5: layout must be built once at KV-write time.
  *   [SUM] RedKnot summary (m.youleyou.com/wenzhang/3087667.html) -- head-class
- *         sparsification; SegPagedAttention as storage + execution substrate.
+ *         sparsification; SegPagedAttention as storage + execution substrate;
+ *         system gains (KV bytes moved between prefill and decode machines).
  *   [KV]  KV-cache guide (zhangjiuzhi.com/?p=3078) -- section 4.3 block tables,
  *         section 5.3 GQA grouping, section 10.2 online softmax.
  *
@@ -262,6 +263,29 @@ SEGPAGED_API int segpaged_select_topp(const segpaged_plan* plan, int32_t layer, 
                                       const void* k_dense, const int32_t* d_table, float scale,
                                       float p, int32_t* out_pos, int32_t* out_cnt, void* workspace,
                                       int64_t workspace_bytes, void* stream);
+
+/* The pages of `layer` (every layer when -1) as one contiguous stream per tensor,
+ * for moving a cache to another device or process: prefill and decode on separate
+ * machines move KV between them, and a SegPaged cache moves only what each head
+ * keeps [SUM: KV transfer bytes in the disaggregated setting]. The stream holds the
+ * table's pages of that range in table order, each in the pool page layout of
+ * segpaged_build: stats(layer).pages * P * D bf16 per tensor (tail slots included).
+ *   d_table  device table image uploaded by segpaged_build or segpaged_import_pages
+ *   k_out, v_out  device bf16 streams (written); pools are only read
+ * The stream depends on the plan's units and segments, not on its page ids. */
+SEGPAGED_API int segpaged_export_pages(const segpaged_plan* plan, int32_t layer,
+                                       const int32_t* d_table, const void* k_pool,
+                                       const void* v_pool, void* k_out, void* v_out,
+                                       void* stream);
+
+/* The inverse: upload the table slice of `layer` (as segpaged_build does), then write
+ * the streamed pages into this plan's pages. The plan must come from the same spec as
+ * the exporting plan up to free list and pool capacity, so its units, segments and
+ * page counts match; its page ids may differ. Pages of other layers are untouched.
+ *   k_in, v_in  device bf16 streams of stats(layer).pages * P * D elements each */
+SEGPAGED_API int segpaged_import_pages(const segpaged_plan* plan, int32_t layer,
+                                       const void* k_in, const void* v_in, int32_t* d_table,
+                                       void* k_pool, void* v_pool, void* stream);
 
 /* Split-K decode [RT section 4; KV section 10.2]: the query at position N_b - 1 of
  * each sequence attends to every key it can see. Work items are (unit, key

@@ -221,6 +221,35 @@ def pool(spec: Spec, layer: int, k_bits: np.ndarray, v_bits: np.ndarray,
     return kp, vp, written
 
 
+def transfer_stream(spec: Spec, layer: int, k_bits: np.ndarray, v_bits: np.ndarray
+                    ) -> Tuple[np.ndarray, np.ndarray]:
+    """The pages of one layer as a transfer stream (K uint16 [pages, D/8, P, 8],
+    V uint16 [pages, P/8, D, 8]): units in table order, their segments in order,
+    each segment's pages in order, every page in the pool layout with zero tail
+    slots. Only what each head keeps is moved (RedKnot summary, system gains: KV
+    bytes moved between prefill and decode machines); the stream does not depend
+    on page ids. k_bits/v_bits: that layer's dense K/V [T_total, Hkv, D]."""
+    P, D = spec.page_size, spec.head_dim
+    kvo = spec.kv_row_offsets()
+    ks, vs = [], []
+    for (u, b, l, h) in units(spec):
+        if l != layer:
+            continue
+        for seg in unit_segments(spec, b, l, h):
+            pos = segment_positions(seg)
+            for p0 in range(0, len(pos), P):
+                rows = kvo[b] + pos[p0:p0 + P]
+                kt = np.zeros((P, D), dtype=np.uint16)
+                vt = np.zeros((P, D), dtype=np.uint16)
+                kt[:len(rows)] = k_bits[rows, h]
+                vt[:len(rows)] = v_bits[rows, h]
+                ks.append(kt.reshape(P, D // 8, 8).transpose(1, 0, 2))
+                vs.append(vt.reshape(P // 8, 8, D).transpose(0, 2, 1))
+    if not ks:
+        return (np.zeros((0, D // 8, P, 8), np.uint16), np.zeros((0, P // 8, D, 8), np.uint16))
+    return np.stack(ks), np.stack(vs)
+
+
 def kv_len_total(spec: Spec, layers=None) -> int:
     """Retained tokens summed over all units (of the given layers)."""
     tot = 0

@@ -7,8 +7,9 @@ pages. The compute path is libsegpaged.so (HIP, gfx950); this package is its
 ctypes binding.
 """
 from .segpaged import (DENSE, GLOBAL, LIB_PATH, LOCAL, RETRIEVAL, Plan, SegPagedError,
-                       Sizes, Stats, append, build, decode, library, prefill,
-                       select_topp)
+                       Sizes, Stats, append, build, decode, export_pages, import_pages,
+                       library, prefill, select_topp, stream_elems)
 
-__all__ = ["Plan", "build", "append", "prefill", "decode", "select_topp", "library", "SegPagedError", "Sizes", "Stats",
+__all__ = ["Plan", "build", "append", "prefill", "decode", "select_topp", "export_pages",
+           "import_pages", "stream_elems", "library", "SegPagedError", "Sizes", "Stats",
            "GLOBAL", "LOCAL", "RETRIEVAL", "DENSE", "LIB_PATH"]

@@ -2,9 +2,12 @@
 // entry points that launch them.
 //
 //   build_kernel           build_segpaged_cache: dense K/V rows -> per-head pages
-//   decode_partial_kernel  split-K decode: one wave per (unit, key range) item
-//   decode_combine_kernel  log-sum-exp merge of the items of each unit
+//   append_kernel          new tokens' K/V into their slots (growth plans)
+//   decode_partial_kernel  split-K decode: one wave per (unit, key range) item part
+//   decode_combine_kernel  log-sum-exp merge of the partials of each unit
 //   prefill_kernel         GQA flash-style prefill over each head's own pages
+//   page_copy_kernel       a layer's pages as one contiguous stream and back (moving
+//                          a cache between devices or processes)
 //
 // Method: SegPagedAttention runtime explainer, section 3 (per-(layer, head,
 // segment) page table and pool; local heads keep only sink + recent tokens) and
@@ -1242,6 +1245,29 @@ __global__ __launch_bounds__(512) void prefill_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// page transfer: the pages of a range of table slots as one contiguous stream
+// (table order, each page in the pool layout), or back into a pool under the page
+// ids of a table. Grid-stride over 16-byte chunks; blockIdx.y picks K or V.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void page_copy_kernel(
+    const int32_t* __restrict__ tab, int32_t off_pages, int32_t page_b, int64_t npages,
+    int32_t log2c, const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src,
+    uint16_t* __restrict__ k_dst, uint16_t* __restrict__ v_dst, int32_t to_stream) {
+  const uint16_t* src = blockIdx.y ? v_src : k_src;
+  uint16_t* dst = blockIdx.y ? v_dst : k_dst;
+  const int64_t nchunks = npages << log2c, cmask = ((int64_t)1 << log2c) - 1;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunks;
+       c += (int64_t)gridDim.x * 256) {
+    const int64_t pid = tab[off_pages + page_b + (c >> log2c)];
+    const int64_t pc = (pid << log2c) + (c & cmask);  // the chunk in the pool
+    if (to_stream)
+      st16(dst + c * 8, ld16(src + pc * 8));
+    else
+      st16(dst + pc * 8, ld16(src + c * 8));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host helpers
 // ---------------------------------------------------------------------------
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -1287,6 +1313,49 @@ int upload(const segpaged_plan* pl, int32_t* d_table, int64_t off, int64_t count
   return e == hipSuccess ? SEGPAGED_OK : SEGPAGED_EHIP;
 }
 
+// The table slice of `layer` into d_table (everything when layer = -1): what
+// segpaged_build and segpaged_import_pages upload before writing pages.
+int upload_layer_table(const segpaged_plan* pl, int32_t layer, int32_t* d_table,
+                       hipStream_t st) {
+  if (layer < 0) return upload(pl, d_table, 0, pl->total_ints, st);
+  const Span sp = span_of(pl, layer);
+  const int64_t U = kUnitInts;
+  int rc;
+  if ((rc = upload(pl, d_table, 0, pl->off_units, st))) return rc;
+  if ((rc = upload(pl, d_table, pl->off_units + U * sp.unit_b, U * (sp.unit_e - sp.unit_b), st)))
+    return rc;
+  if ((rc = upload(pl, d_table, pl->off_pages + sp.page_b, sp.page_e - sp.page_b, st))) return rc;
+  if ((rc = upload(pl, d_table, pl->off_retr + sp.retr_b, sp.retr_e - sp.retr_b, st))) return rc;
+  if ((rc = upload(pl, d_table, pl->off_decunits + 2 * sp.unit_b, 2 * (sp.unit_e - sp.unit_b),
+                   st)))
+    return rc;
+  if ((rc = upload(pl, d_table, pl->off_dec + kDecItemInts * sp.dec_b,
+                   kDecItemInts * (sp.dec_e - sp.dec_b), st)))
+    return rc;
+  if ((rc = upload(pl, d_table, pl->off_pre + kPreItemInts * sp.pre_b,
+                   kPreItemInts * (sp.pre_e - sp.pre_b), st)))
+    return rc;
+  // zeroed prefill work counters of this layer and of all-layer calls
+  if ((rc = upload(pl, d_table, pl->off_ctr + kCtrInts * layer, kCtrInts, st))) return rc;
+  return upload(pl, d_table, pl->off_ctr + kCtrInts * pl->L, kCtrInts, st);
+}
+
+// Pages [page_b, page_e) of the table between a pool and a contiguous stream.
+int launch_page_copy(const segpaged_plan* pl, const Span& sp, const int32_t* d_table,
+                     const void* k_src, const void* v_src, void* k_dst, void* v_dst,
+                     int32_t to_stream, hipStream_t st) {
+  const int64_t npages = sp.page_e - sp.page_b;
+  if (npages == 0) return SEGPAGED_OK;
+  const int32_t log2c = pl->log2P + __builtin_ctz((unsigned)pl->D) - 3;  // 16-byte chunks per page
+  const int64_t nchunks = npages << log2c;
+  const int64_t cus = std::max(device_cus(), 1);
+  const dim3 grid((unsigned)std::min<int64_t>((nchunks + 255) / 256, cus * 64), 2), block(256);
+  hipLaunchKernelGGL(page_copy_kernel, grid, block, 0, st, d_table, (int32_t)pl->off_pages,
+                     (int32_t)sp.page_b, npages, log2c, (const uint16_t*)k_src,
+                     (const uint16_t*)v_src, (uint16_t*)k_dst, (uint16_t*)v_dst, to_stream);
+  return check_launch();
+}
+
 }  // namespace
 
 extern "C" {
@@ -1301,30 +1370,8 @@ SEGPAGED_API int segpaged_build(const segpaged_plan* pl, int32_t layer, const vo
   if (layer < -1 || layer >= pl->L) return SEGPAGED_ESTATE;
   hipStream_t st = (hipStream_t)stream;
   const Span sp = span_of(pl, layer);
-  int rc;
-  if (layer < 0) {
-    rc = upload(pl, d_table, 0, pl->total_ints, st);
-    if (rc) return rc;
-  } else {
-    const int64_t U = kUnitInts;
-    if ((rc = upload(pl, d_table, 0, pl->off_units, st))) return rc;
-    if ((rc = upload(pl, d_table, pl->off_units + U * sp.unit_b, U * (sp.unit_e - sp.unit_b), st)))
-      return rc;
-    if ((rc = upload(pl, d_table, pl->off_pages + sp.page_b, sp.page_e - sp.page_b, st))) return rc;
-    if ((rc = upload(pl, d_table, pl->off_retr + sp.retr_b, sp.retr_e - sp.retr_b, st))) return rc;
-    if ((rc = upload(pl, d_table, pl->off_decunits + 2 * sp.unit_b, 2 * (sp.unit_e - sp.unit_b),
-                     st)))
-      return rc;
-    if ((rc = upload(pl, d_table, pl->off_dec + kDecItemInts * sp.dec_b,
-                     kDecItemInts * (sp.dec_e - sp.dec_b), st)))
-      return rc;
-    if ((rc = upload(pl, d_table, pl->off_pre + kPreItemInts * sp.pre_b,
-                     kPreItemInts * (sp.pre_e - sp.pre_b), st)))
-      return rc;
-    // zeroed prefill work counters of this layer and of all-layer calls
-    if ((rc = upload(pl, d_table, pl->off_ctr + kCtrInts * layer, kCtrInts, st))) return rc;
-    if ((rc = upload(pl, d_table, pl->off_ctr + kCtrInts * pl->L, kCtrInts, st))) return rc;
-  }
+  const int rc = upload_layer_table(pl, layer, d_table, st);
+  if (rc) return rc;
   const int64_t npages = sp.page_e - sp.page_b;
   if (npages == 0) return SEGPAGED_OK;
   const int64_t dstride = layer < 0 ? pl->kv_rows * pl->Hkv * pl->D : 0;
@@ -1344,6 +1391,33 @@ SEGPAGED_API int segpaged_build(const segpaged_plan* pl, int32_t layer, const vo
                        (int32_t)sp.unit_b, (int32_t)sp.unit_e, (int32_t)sp.page_b, pl->Hkv, pl->P,
                        pl->log2P, kd, vd, dstride, kpp, vpp);
   return check_launch();
+}
+
+SEGPAGED_API int segpaged_export_pages(const segpaged_plan* pl, int32_t layer,
+                                       const int32_t* d_table, const void* k_pool,
+                                       const void* v_pool, void* k_out, void* v_out,
+                                       void* stream) {
+  if (!pl || !d_table || !k_pool || !v_pool || !k_out || !v_out) return SEGPAGED_EINVAL;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_out) || !aligned16(v_out) ||
+      !aligned4(d_table))
+    return SEGPAGED_EINVAL;
+  if (layer < -1 || layer >= pl->L) return SEGPAGED_ESTATE;
+  return launch_page_copy(pl, span_of(pl, layer), d_table, k_pool, v_pool, k_out, v_out, 1,
+                          (hipStream_t)stream);
+}
+
+SEGPAGED_API int segpaged_import_pages(const segpaged_plan* pl, int32_t layer, const void* k_in,
+                                       const void* v_in, int32_t* d_table, void* k_pool,
+                                       void* v_pool, void* stream) {
+  if (!pl || !k_in || !v_in || !d_table || !k_pool || !v_pool) return SEGPAGED_EINVAL;
+  if (!aligned16(k_in) || !aligned16(v_in) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned4(d_table))
+    return SEGPAGED_EINVAL;
+  if (layer < -1 || layer >= pl->L) return SEGPAGED_ESTATE;
+  hipStream_t st = (hipStream_t)stream;
+  const int rc = upload_layer_table(pl, layer, d_table, st);
+  if (rc) return rc;
+  return launch_page_copy(pl, span_of(pl, layer), d_table, k_in, v_in, k_pool, v_pool, 0, st);
 }
 
 SEGPAGED_API int segpaged_append(segpaged_plan* pl, int32_t layer, const void* k_new,

@@ -78,6 +78,8 @@ def _lib():
         lib.segpaged_plan_table_host.argtypes = [vp, _i32p, ctypes.c_int64]
         lib.segpaged_plan_stats.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(Stats)]
         lib.segpaged_build.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
+        lib.segpaged_export_pages.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
+        lib.segpaged_import_pages.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
         lib.segpaged_plan_append.argtypes = [vp, _i32p]
         lib.segpaged_select_topp.argtypes = [vp, ctypes.c_int32, vp, vp, vp, ctypes.c_float,
                                              ctypes.c_float, vp, vp, vp, ctypes.c_int64, vp]
@@ -266,6 +268,50 @@ def build(plan: Plan, layer: int, k_dense, v_dense, table, k_pool, v_pool, strea
     _check(_lib().segpaged_build(plan.handle, layer, _ptr(k_dense, "k"), _ptr(v_dense, "v"),
                                  _ptr(table, "table"), _ptr(k_pool, "kp"), _ptr(v_pool, "vp"),
                                  _stream(stream)), "segpaged_build")
+
+
+def stream_elems(plan: Plan, layer: int) -> int:
+    """bf16 elements per tensor of the page stream of `layer` (all layers when -1)."""
+    return plan.stats(layer)["pages"] * plan.page_size * plan.head_dim
+
+
+def export_pages(plan: Plan, layer: int, table, k_pool, v_pool, k_out, v_out, stream=None):
+    """segpaged_export_pages: the pages of `layer` as one stream per tensor."""
+    import torch
+    z = plan.sizes
+    n = stream_elems(plan, layer)
+    _ptr(table, "table", torch.int32)
+    _need(table, z.table_int32s, "table")
+    for t, nm in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        _ptr(t, nm, torch.bfloat16)
+        _need(t, z.pool_bytes // 2, nm)
+    for t, nm in ((k_out, "k_out"), (v_out, "v_out")):
+        _ptr(t, nm, torch.bfloat16)
+        _need(t, n, nm)
+    _check(_lib().segpaged_export_pages(plan.handle, layer, _ptr(table, "table"),
+                                        _ptr(k_pool, "kp"), _ptr(v_pool, "vp"),
+                                        _ptr(k_out, "ko"), _ptr(v_out, "vo"), _stream(stream)),
+           "segpaged_export_pages")
+
+
+def import_pages(plan: Plan, layer: int, k_in, v_in, table, k_pool, v_pool, stream=None):
+    """segpaged_import_pages: upload the table slice of `layer`, then write the
+    streamed pages into this plan's pages."""
+    import torch
+    z = plan.sizes
+    n = stream_elems(plan, layer)
+    for t, nm in ((k_in, "k_in"), (v_in, "v_in")):
+        _ptr(t, nm, torch.bfloat16)
+        _need(t, n, nm)
+    _ptr(table, "table", torch.int32)
+    _need(table, z.table_int32s, "table")
+    for t, nm in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        _ptr(t, nm, torch.bfloat16)
+        _need(t, z.pool_bytes // 2, nm)
+    _check(_lib().segpaged_import_pages(plan.handle, layer, _ptr(k_in, "ki"), _ptr(v_in, "vi"),
+                                        _ptr(table, "table"), _ptr(k_pool, "kp"),
+                                        _ptr(v_pool, "vp"), _stream(stream)),
+           "segpaged_import_pages")
 
 
 def prefill(plan: Plan, layer: int, q, table, k_pool, v_pool, scale: float, o, lse=None,

@@ -141,6 +141,50 @@ def test_table_structure_and_free_list():
     assert list(retr) == [1, 2, 30, 31, 32, 3, 17, 0, 1, 2, 3, 4, 5, 6, 7, 8, 40, 41]
 
 
+def test_transfer_stream_elements_and_pool_pages():
+    """The transfer stream, element by element from the page-layout formulas of the
+    pool (K (slot, d) at [d // 8][slot][d % 8], V at [slot // 8][d][slot % 8]), and
+    page by page equal to the pool pages its table lists for the layer, in order."""
+    free = W.seeded_free_list(120, seed=5)
+    spec = _spec_mixed(free, 120)
+    t = L.table(spec)
+    P, D = spec.page_size, spec.head_dim
+    kvo = spec.kv_row_offsets()
+    page_b = 0
+    for layer in range(3):
+        kb, vb = W.kv_bits(spec, layer)
+        ks, vs = L.transfer_stream(spec, layer, kb, vb)
+        # expected pages from the retained positions of each unit, in table order
+        j = 0
+        for b in range(spec.num_seqs):
+            for h in range(spec.num_kv_heads):
+                c = layer * spec.num_kv_heads + h
+                retr = spec.retrieval.get((b, layer, h)) if spec.retrieval else None
+                for seg in L.retained_segments(spec.kind[c], spec.sink[c], spec.window[c],
+                                               spec.seq_len[b], spec.first_query_pos[b], retr):
+                    pos = (list(range(seg[0], seg[0] + seg[1])) if seg[0] != "gathered"
+                           else [int(x) for x in seg[1]])
+                    npg = -(-len(pos) // P)
+                    for slot in range(npg * P):
+                        for d in range(D):
+                            if slot < len(pos):
+                                ek = kb[kvo[b] + pos[slot], h, d]
+                                ev = vb[kvo[b] + pos[slot], h, d]
+                            else:
+                                ek = ev = 0
+                            jj, sl = j + slot // P, slot % P
+                            assert ks[jj, d // 8, sl, d % 8] == ek
+                            assert vs[jj, sl // 8, d, sl % 8] == ev
+                    j += npg
+        assert j == len(ks) == len(vs)
+        # the same pages, found through the table's page ids
+        kp, vp, _ = L.pool(spec, layer, kb, vb, 120)
+        ids = t[int(t[13]) + page_b:int(t[13]) + page_b + j]
+        assert np.array_equal(ks, kp[ids]) and np.array_equal(vs, vp[ids])
+        page_b += j
+    assert page_b == int(t[9])
+
+
 def test_pool_round_trip_and_loops_agree():
     free = W.seeded_free_list(120, seed=3)
     spec = _spec_mixed(free, 120)
