@@ -80,7 +80,7 @@ def summarize_pmc(fetch_dir, write_dir):
     import re
 
     def load(d, counter):
-        per = {}
+        per, grids = {}, {}
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
                 if r["Counter_Name"] != counter:
@@ -91,6 +91,12 @@ def summarize_pmc(fetch_dir, write_dir):
                 key = m.group(1) if m else ("copy" if "neg_kernel" in nm else None)
                 if key:
                     per.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
+                    grids.setdefault(key, []).append(int(r["Grid_Size"]))
+        # decode: the all-layer call (the largest grid), not the one-layer launches
+        for key in ("decode_partial_kernel", "decode_combine_kernel"):
+            if key in per:
+                g = max(grids[key])
+                per[key] = [v for v, gg in zip(per[key], grids[key]) if gg == g]
         return per
     fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
     f_scale = COPY_BYTES / (sum(fetch["copy"]) / len(fetch["copy"]))
@@ -134,9 +140,13 @@ def summarize_mfma(pmc_dir):
             d = per.setdefault((m.group(1), r["Dispatch_Id"]), {})
             d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
             d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+            d["grid"] = int(r["Grid_Size"])
     out = {"kernels_sha256_16": kernels_hash(), "per_kernel": {}}
     for k in ("prefill_kernel", "decode_partial_kernel"):
         rows = [v for (kk, _), v in per.items() if kk == k and "GRBM_GUI_ACTIVE" in v]
+        if rows and k == "decode_partial_kernel":  # the all-layer call: the largest grid
+            g = max(v["grid"] for v in rows)
+            rows = [v for v in rows if v["grid"] == g]
         if not rows:
             continue
         busy = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"] for v in rows)
