@@ -28,7 +28,8 @@
  *     (NULL = the null stream) on the current HIP device.
  *   - Asynchronous kernel faults surface at the caller's next synchronisation.
  *   - bf16 tensors are raw IEEE bfloat16 bits, row-major, 16-byte aligned.
- *   - A plan is immutable after creation; concurrent calls that share a plan are
+ *   - A plan changes only in segpaged_plan_append (growth plans); every other call
+ *     takes it read-only, and concurrent read-only calls that share a plan are
  *     safe. A plan must outlive all work enqueued with it.
  */
 #ifndef SEGPAGED_H

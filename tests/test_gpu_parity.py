@@ -373,8 +373,8 @@ def _parts_log2(nitems, keys, recs):
     return s
 
 
-@pytest.mark.parametrize("ps", [16, 64])
-def test_decode_item_parts(ps):
+@pytest.mark.parametrize("ps,hd", [(16, 128), (64, 128), (32, 64)])
+def test_decode_item_parts(ps, hd):
     """One layer of a two-layer plan with 4096-key items, launched alone with room
     for more partials: each item is dealt to several waves (parts). Layer 0's local
     head keeps sink 4 + window 60, one short item over the sink page and two window
@@ -385,7 +385,7 @@ def test_decode_item_parts(ps):
     lens = [9000, 4400]
     retr = W.seeded_retrieval_sets(lens, kind, 2, 2, 5, 0.2)
     spec = W.decode_form(W.Spec(name="parts", num_layers=2, num_q_heads=8, num_kv_heads=2,
-                                head_dim=128, page_size=ps, seq_len=lens,
+                                head_dim=hd, page_size=ps, seq_len=lens,
                                 first_query_pos=[0, 0], kind=kind, sink=[0, 4, 7, 0],
                                 window=[1, 60, 3000, 1], retrieval=retr, seed=21))
     plan = sp.Plan(spec, decode_split_tokens=4096)
@@ -394,7 +394,7 @@ def test_decode_item_parts(ps):
     sp.build(plan, -1, to_dev(np.stack([k for k, _ in kvs])), to_dev(np.stack([v for _, v in kvs])),
              bufs["table"], bufs["k_pool"], bufs["v_pool"])
     qs = [W.q_bits(spec, l) for l in range(2)]
-    scale = 1 / np.sqrt(128)
+    scale = 1 / np.sqrt(hd)
     q_all = to_dev(np.stack(qs))
     o_all = torch.empty_like(q_all)
     lse_all = torch.empty(q_all.shape[:3], dtype=torch.float32, device=DEV)
@@ -402,7 +402,7 @@ def test_decode_item_parts(ps):
               lse_all, workspace=bufs["workspace"])
     big_ws = torch.empty(16 * bufs["workspace"].numel() + 4096, dtype=bufs["workspace"].dtype,
                          device=DEV)
-    rec = spec.num_q_heads // spec.num_kv_heads * (128 + 4) * 4
+    rec = spec.num_q_heads // spec.num_kv_heads * (hd + 4) * 4
     for l in range(2):
         st = plan.stats(l)
         assert _parts_log2(st["decode_items"], st["decode_tokens"],

@@ -18,28 +18,28 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _spec(ps, free=None, cap=0):
+def _spec(ps, free=None, cap=0, hd=128):
     """Three layers of mixed classes in decode form: sink pages with zero tails,
     two-segment local heads, gathered retrieval sets, ragged lengths."""
     kind = [W.GLOBAL, W.LOCAL, W.RETRIEVAL, W.LOCAL, W.LOCAL, W.GLOBAL]
     lens = [1500, 333, 2100]
     retr = W.seeded_retrieval_sets(lens, kind, 3, 2, 17, 0.1)
-    s = W.Spec(name="moved", num_layers=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
+    s = W.Spec(name="moved", num_layers=3, num_q_heads=8, num_kv_heads=2, head_dim=hd,
                page_size=ps, seq_len=lens, first_query_pos=[0, 0, 0], kind=kind,
                sink=[0, 4, 0, 7, 0, 0], window=[1, 200, 1, 90, 1000, 1], retrieval=retr,
                free_list=free, capacity_pages=cap, seed=31)
     return W.decode_form(s)
 
 
-@pytest.mark.parametrize("ps", [16, 64])
-def test_export_then_import_into_another_plan(ps):
-    sender = _spec(ps)
+@pytest.mark.parametrize("ps,hd", [(16, 128), (64, 128), (128, 64)])
+def test_export_then_import_into_another_plan(ps, hd):
+    sender = _spec(ps, hd=hd)
     send = sp.Plan(sender)
     sb = send.allocate(DEV)
     kvs = [W.kv_bits(sender, l) for l in range(3)]
     sp.build(send, -1, to_dev(np.stack([k for k, _ in kvs])), to_dev(np.stack([v for _, v in kvs])),
              sb["table"], sb["k_pool"], sb["v_pool"])
-    P, D = ps, 128
+    P, D = ps, hd
 
     # the stream of each layer, and of all layers in one call
     streams = []
@@ -83,7 +83,7 @@ def test_export_then_import_into_another_plan(ps):
     assert not kp[~written].any() and not vp[~written].any()  # no other page touched
 
     # the moved cache serves a decode on the receiver
-    scale = 1 / np.sqrt(128)
+    scale = 1 / np.sqrt(hd)
     for l in range(3):
         qb = W.q_bits(receiver, l)
         q = to_dev(qb)
