@@ -415,6 +415,8 @@ def main():
             out["dense_mask"] = {"error": f"{type(e).__name__}: {e}"[:300]}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(torch, W, pspec, qs[0], ks[0], vs[0], args, log)
+        out["cpu_baseline"]["decode"] = cpu_baseline_decode(torch, W, dspec, dplan, q_dec, dev,
+                                                            args, log)
     if not args.no_extra:
         del pb, db, qs, ks, vs, o_pre, lse_pre, q_dec, o_dec, lse_dec
         torch.cuda.empty_cache()
@@ -996,6 +998,37 @@ def cpu_baseline(torch, W, pspec, q0, k0, v0, args, log):
             "sample": (f"{done_rows} query rows of layer 0 at seeded positions, all "
                        f"{pspec.num_q_heads} Q heads, full {N}-token context; scaled to "
                        f"{args.prefill_layers} layers x {pspec.num_q_heads} heads per token"),
+            "seconds": round(spent, 2)}
+
+
+def cpu_baseline_decode(torch, W, dspec, dplan, q_dec, dev, args, log):
+    """The oracle on the decode workload: the decode row of one (sequence, layer) at a
+    time, against that sequence's whole dense K/V, until about a third of the
+    prefill baseline's time has passed. Rate = K/V bytes of the keys the row sees
+    (bf16) per second."""
+    from oracle import attention as OA
+    B, n, L = dspec.num_seqs, dspec.seq_len[0], dspec.num_layers
+    Hkv, D = dspec.num_kv_heads, dspec.head_dim
+    rng = np.random.default_rng([dspec.seed, 78])
+    done, spent, nbytes = 0, 0.0, 0
+    while spent < args.cpu_seconds / 3:
+        l, b = int(rng.integers(0, L)), int(rng.integers(0, B))
+        kd = W.randn_bf16_device((B * n, Hkv, D), dspec.seed, W.TAG_K, l, dev)
+        vd = W.randn_bf16_device((B * n, Hkv, D), dspec.seed, W.TAG_V, l, dev)
+        kb = kd[b * n:(b + 1) * n].view(torch.int16).cpu().numpy().view(np.uint16)
+        vb = vd[b * n:(b + 1) * n].view(torch.int16).cpu().numpy().view(np.uint16)
+        qr = q_dec[l, b:b + 1].view(torch.int16).cpu().numpy().view(np.uint16)
+        del kd, vd
+        t0 = time.perf_counter()
+        OA.attention_rows(dspec, l, b, [n - 1], qr, kb, vb)
+        spent += time.perf_counter() - t0
+        nbytes += dplan.stats(l)["decode_tokens"] // B * 2 * D * 2
+        done += 1
+    gbs = nbytes / spent / 1e9
+    log(f"oracle decode: {done} (sequence, layer) rows in {spent:.1f} s -> {gbs:.3f} GB/s")
+    return {"value": round(gbs, 4), "unit": "GB/s", "kind": "oracle",
+            "sample": (f"the decode row of {done} seeded (sequence, layer) pairs of the "
+                       f"{L}-layer decode workload, each against its {n}-token dense K/V"),
             "seconds": round(spent, 2)}
 
 
