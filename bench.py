@@ -195,8 +195,8 @@ def main():
         summarize_mfma(args.summarize_mfma)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(units shard by KV head with no exchange; see the design notes).", file=sys.stderr)
+        print("bench.py runs on one GPU only: there is no multi-GPU path (the units would "
+              "shard by KV head with no exchange between GPUs).", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -46,7 +46,7 @@ extern "C" {
 typedef enum {
   SEGPAGED_OK = 0,
   SEGPAGED_EINVAL = -1,        /* invalid argument (null/misaligned pointer, bad spec value) */
-  SEGPAGED_EUNSUPPORTED = -2,  /* valid but not supported by this build (head_dim, page size, group) */
+  SEGPAGED_EUNSUPPORTED = -2,  /* valid but not supported by the library (head_dim, page size, group) */
   SEGPAGED_ENOSPACE = -3,      /* pool capacity, free list, table or workspace too small */
   SEGPAGED_EHIP = -4,          /* a HIP runtime call or kernel launch failed */
   SEGPAGED_ESTATE = -5         /* call does not fit the plan (e.g. layer out of range) */
