@@ -150,8 +150,8 @@ def seeded_free_list(capacity: int, seed: int) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
-# the five workloads (shapes as in the task's configuration list) plus knobs
-# that shrink them for parity tests
+# the five workloads (tiny, Mistral-7B-shaped layer, Llama-3.3-70B-shaped decode,
+# long prefill, mixed-length decode) plus knobs that shrink them for parity tests
 # ----------------------------------------------------------------------------
 
 def tiny(form: str = "prefill", n: int = 512) -> Spec:
