@@ -7,8 +7,9 @@
 // mass-ordered prefix (larger first, equal masses by position) reaching p of the
 // total, returned as sorted positions.
 //
-//   select_scores_kernel  scores of 256 keys x G heads per workgroup (fp32, log2
-//                         units), with each block's max and exp-sum per head
+//   select_scores_kernel  scores of 256 keys x G heads per workgroup (bf16 MFMA,
+//                         fp32, log2 units), with each block's max and exp-sum
+//                         per head
 //   select_topp_kernel    one workgroup per pair: the masses, then a radix
 //                         select on their bits (8 bits per pass, larger first)
 //                         with each bin's mass summed alongside in fixed point,
@@ -28,6 +29,8 @@ using namespace segpaged;
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSelKeys = 256;  // keys per scoring workgroup
 constexpr int kSelThreads = 256;
 constexpr float kLog2eSel = 1.4426950408889634f;
@@ -46,9 +49,11 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Scores of 256 keys for the G query heads of (b, h): a wave reads 4 key rows per
-// load, 16 lanes per row (16 bytes each, coalesced), and the 16 partial dot
-// products of a row meet by lane shuffles. Writes s[g] = c * q_g . k_j (log2
+// Scores of 256 keys for the G query heads of (b, h) with v_mfma_f32_16x16x32_bf16:
+// S[16 keys][16 cols] = K[keys][32 dims] . Q^T[32 dims][cols], the G query heads as
+// columns (zero past G). A wave takes 64 keys, 16 per MFMA tile; lane (n, g) loads
+// 8 dims (16 bytes) of key n of a tile straight from the dense K rows and holds
+// the scores of keys 4g .. 4g + 3 for head n. Writes s[g] = c * q_g . k_j (log2
 // units) and, per block and head, the max and the sum of exp2(s - max).
 template <int D>
 __global__ __launch_bounds__(kSelThreads) void select_scores_kernel(
@@ -56,8 +61,7 @@ __global__ __launch_bounds__(kSelThreads) void select_scores_kernel(
     int32_t Hkv, int32_t G, int32_t Hq, int32_t T, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kd, float c, float* __restrict__ ws_s,
     float* __restrict__ ws_part, int32_t nblk) {
-  constexpr int LPR = D / 8;       // lanes per key row (16 bytes each)
-  constexpr int RPW = 64 / LPR;    // rows per wave load
+  constexpr int KS = D / 32;  // 32-dim steps of the contraction
   const int b = blockIdx.y / Hkv, h = blockIdx.y % Hkv, blk = blockIdx.x;
   const int32_t* ur = tab + off_units + kUnitInts * ((layer * B + b) * Hkv + h);
   if (ur[U_KIND] != SEGPAGED_RETRIEVAL) return;
@@ -67,38 +71,34 @@ __global__ __launch_bounds__(kSelThreads) void select_scores_kernel(
   __shared__ float ssc[kSelKeys][kMaxGroup];
   __shared__ float red[kMaxGroup][4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int sub = lane % LPR, rr = lane / LPR;
-  // this lane's 8 dims of every query head
-  float qv[kMaxGroup][8];
+  const int n = lane & 15, g = lane >> 4;
+  // Q^T operand: head n (zero past G), dims 32 ks + 8 g .. + 7
+  bf16x8 qf[KS];
 #pragma unroll
-  for (int g = 0; g < kMaxGroup; ++g) {
-    if (g < G) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * Hq + h * G + g) * D + sub * 8);
-      qv[g][0] = bf16_lo(w.x); qv[g][1] = bf16_hi(w.x); qv[g][2] = bf16_lo(w.y);
-      qv[g][3] = bf16_hi(w.y); qv[g][4] = bf16_lo(w.z); qv[g][5] = bf16_hi(w.z);
-      qv[g][6] = bf16_lo(w.w); qv[g][7] = bf16_hi(w.w);
-    }
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (n < G) w = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * Hq + h * G + n) * D + ks * 32 + g * 8);
+    qf[ks] = __builtin_bit_cast(bf16x8, w);
   }
-  // wave w scores keys [64 w, 64 w + 64) of the block, RPW rows per step
-  for (int r0 = 0; r0 < 64; r0 += RPW) {
-    const int kb = wave * 64 + r0 + rr;  // key within the block
-    const int32_t j = blk * kSelKeys + kb;
-    float kv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (j < N) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(kd + ((int64_t)(kvo + j) * Hkv + h) * D + sub * 8);
-      kv[0] = bf16_lo(w.x); kv[1] = bf16_hi(w.x); kv[2] = bf16_lo(w.y); kv[3] = bf16_hi(w.y);
-      kv[4] = bf16_lo(w.z); kv[5] = bf16_hi(w.z); kv[6] = bf16_lo(w.w); kv[7] = bf16_hi(w.w);
-    }
+  // K operands of the wave's 4 tiles of 16 keys, every load in flight at once
+  u32x4 kv[4][KS];
 #pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g) {
-      if (g < G) {
-        float d = 0.f;
+  for (int t = 0; t < 4; ++t) {
+    const int32_t j = blk * kSelKeys + wave * 64 + t * 16 + n;
+    const uint16_t* row = kd + ((int64_t)(kvo + min(j, N - 1)) * Hkv + h) * D + g * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(kv[e], qv[g][e], d);
+    for (int ks = 0; ks < KS; ++ks) kv[t][ks] = *reinterpret_cast<const u32x4*>(row + ks * 32);
+  }
 #pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1) d += __shfl_xor(d, off, 64);
-        if (sub == 0) ssc[kb][g] = d * c;
-      }
+  for (int t = 0; t < 4; ++t) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv[t][ks]), qf[ks],
+                                                    acc, 0, 0, 0);
+    if (n < G) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ssc[wave * 64 + t * 16 + 4 * g + i][n] = acc[i] * c;
     }
   }
   __syncthreads();
@@ -159,24 +159,6 @@ __device__ unsigned long long wave_sum_u64(unsigned long long v) {
 }
 
 // fixed-order reductions over the workgroup
-__device__ float block_max_top(float v, float* red) {
-  v = wave_max(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float t = red[0];
-  for (int w = 1; w < kTopWaves; ++w) t = fmaxf(t, red[w]);
-  return t;
-}
-__device__ float block_sum_top(float v, float* red) {
-  v = wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float t = 0.f;
-  for (int w = 0; w < kTopWaves; ++w) t += red[w];
-  return t;
-}
 __device__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long* red) {
   v = wave_sum_u64(v);
   __syncthreads();
@@ -221,43 +203,91 @@ __global__ __launch_bounds__(kTopThreads) void select_topp_kernel(
     if (tid == 0) out_cnt[b * Hkv + h] = 0;
     return;
   }
-  __shared__ float sM[kLdsKeys];
+  // masses of up to kLdsKeys keys, one pad word per 32 so that a thread's run of
+  // consecutive keys (the final pass) meets other threads' runs in other banks
+  __shared__ float sM[kLdsKeys + kLdsKeys / 32];
   __shared__ unsigned int hc[256];
   __shared__ unsigned long long hs[256];
-  __shared__ float sm[kMaxGroup], sl[kMaxGroup], redf[kTopWaves];
+  __shared__ float sm[kMaxGroup], sl[kMaxGroup], redg[kTopWaves][kMaxGroup];
   __shared__ unsigned long long redu[kTopWaves];
   __shared__ int wtot[kTopWaves];
   __shared__ int s_chosen;
   __shared__ unsigned long long s_acc;
   const bool in_lds = N <= kLdsKeys;
   float* Mg = ws_m + (int64_t)h * T + kvo;
-  // normalisers of the G heads over all N keys
+  auto mass_at = [&](int32_t j) { return in_lds ? sM[j + (j >> 5)] : Mg[j]; };
+  const int lane = tid & 63, wave = tid >> 6;
+  // normalisers of the G heads over all N keys, every head at once: each thread
+  // over its share of the block partials, then the waves in a fixed order
   const int nb = (N + kSelKeys - 1) / kSelKeys;
   const float* part = ws_part + ((int64_t)h * B + b) * nblk * G * 2;
-  for (int g = 0; g < G; ++g) {
-    float m = -INFINITY;
-    for (int k = tid; k < nb; k += kTopThreads) m = fmaxf(m, part[((int64_t)k * G + g) * 2]);
-    const float mx = block_max_top(m, redf);
-    float l = 0.f;
+  {
+    float v[kMaxGroup];
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) v[g] = -INFINITY;
     for (int k = tid; k < nb; k += kTopThreads)
-      l += part[((int64_t)k * G + g) * 2 + 1] * exp2f(part[((int64_t)k * G + g) * 2] - mx);
-    const float ls = block_sum_top(l, redf);
-    if (tid == 0) { sm[g] = mx; sl[g] = 1.f / ls; }
+#pragma unroll
+      for (int g = 0; g < kMaxGroup; ++g)
+        if (g < G) v[g] = fmaxf(v[g], part[((int64_t)k * G + g) * 2]);
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) {
+      if (g < G) {
+        v[g] = wave_max(v[g]);
+        if (lane == 0) redg[wave][g] = v[g];
+      }
+    }
+    __syncthreads();
+    if (tid < G) {
+      float t = redg[0][tid];
+      for (int w = 1; w < kTopWaves; ++w) t = fmaxf(t, redg[w][tid]);
+      sm[tid] = t;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) v[g] = 0.f;
+    for (int k = tid; k < nb; k += kTopThreads)
+#pragma unroll
+      for (int g = 0; g < kMaxGroup; ++g)
+        if (g < G)
+          v[g] += part[((int64_t)k * G + g) * 2 + 1] * exp2f(part[((int64_t)k * G + g) * 2] - sm[g]);
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) {
+      if (g < G) {
+        v[g] = wave_sum(v[g]);
+        if (lane == 0) redg[wave][g] = v[g];
+      }
+    }
+    __syncthreads();
+    if (tid < G) {
+      float t = 0.f;
+      for (int w = 0; w < kTopWaves; ++w) t += redg[w][tid];
+      sl[tid] = 1.f / t;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   // masses, and their total in fixed point
   const float* S = ws_s + ((int64_t)h * T + kvo) * G;
   const float inv_g = 1.f / (float)G;
   unsigned long long tfx = 0;
   for (int32_t j = tid; j < N; j += kTopThreads) {
     float m = 0.f;
-    for (int g = 0; g < G; ++g) m += exp2f(S[(int64_t)j * G + g] - sm[g]) * sl[g];
+    const float* sj = S + (int64_t)j * G;
+    if ((G & 3) == 0) {  // 16-byte loads of the key's G scores
+      for (int g = 0; g < G; g += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(sj + g);
+        m += __builtin_amdgcn_exp2f(x.x - sm[g]) * sl[g];
+        m += __builtin_amdgcn_exp2f(x.y - sm[g + 1]) * sl[g + 1];
+        m += __builtin_amdgcn_exp2f(x.z - sm[g + 2]) * sl[g + 2];
+        m += __builtin_amdgcn_exp2f(x.w - sm[g + 3]) * sl[g + 3];
+      }
+    } else {
+      for (int g = 0; g < G; ++g) m += __builtin_amdgcn_exp2f(sj[g] - sm[g]) * sl[g];
+    }
     m *= inv_g;
-    if (in_lds) sM[j] = m; else Mg[j] = m;
+    if (in_lds) sM[j + (j >> 5)] = m; else Mg[j] = m;
     tfx += to_fx(m);
   }
   const unsigned long long total = block_sum_u64(tfx, redu);
-  const float* M = in_lds ? sM : Mg;
   unsigned long long R = (unsigned long long)((double)p * (double)total);  // still to take
   if (R == 0) R = 1;
   uint32_t prefix = 0, mask = 0;
@@ -266,7 +296,7 @@ __global__ __launch_bounds__(kTopThreads) void select_topp_kernel(
     for (int k = tid; k < 256; k += kTopThreads) { hc[k] = 0; hs[k] = 0; }
     __syncthreads();
     for (int32_t j = tid; j < N; j += kTopThreads) {
-      const float m = M[j];
+      const float m = mass_at(j);
       const uint32_t u = __float_as_uint(m);
       if ((u & mask) != prefix) continue;
       const uint32_t bin = (u >> shift) & 255u;
@@ -304,12 +334,12 @@ __global__ __launch_bounds__(kTopThreads) void select_topp_kernel(
   const int32_t per = (N + kTopThreads - 1) / kTopThreads;
   const int32_t lo = min(N, tid * per), hi = min(N, lo + per);
   int ties = 0;
-  for (int32_t j = lo; j < hi; ++j) ties += __float_as_uint(M[j]) == prefix;
+  for (int32_t j = lo; j < hi; ++j) ties += __float_as_uint(mass_at(j)) == prefix;
   int ties_total;
   const int tie_base = block_scan_top(ties, wtot, ties_total);
   int nsel = 0, tr = tie_base;
   for (int32_t j = lo; j < hi; ++j) {
-    const uint32_t u = __float_as_uint(M[j]);
+    const uint32_t u = __float_as_uint(mass_at(j));
     nsel += u > prefix || (u == prefix && tr < t);
     tr += u == prefix;
   }
@@ -318,7 +348,7 @@ __global__ __launch_bounds__(kTopThreads) void select_topp_kernel(
   int32_t* out = out_pos + (int64_t)h * T + kvo;
   tr = tie_base;
   for (int32_t j = lo; j < hi; ++j) {
-    const uint32_t u = __float_as_uint(M[j]);
+    const uint32_t u = __float_as_uint(mass_at(j));
     if (u > prefix || (u == prefix && tr < t)) out[pos++] = j;
     tr += u == prefix;
   }
