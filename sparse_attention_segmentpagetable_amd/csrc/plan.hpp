@@ -28,6 +28,7 @@ constexpr int kPreItemInts = 2;   // unit, first query position of the tile
 constexpr int kPrefillRows = 256; // query rows per prefill tile: G heads x (256 / G) positions
 constexpr int kBlockN = 32;       // keys per prefill block
 constexpr int kMaxGroup = 16;     // Q heads per KV head the decode kernel supports
+constexpr int kSelChunk = 2048;   // keys per workgroup of the top-p masses and first radix pass
 constexpr int kCtrInts = 16;      // prefill work counter line per layer (+1 for all layers)
 constexpr int kDecMaxPartsLog2 = 4;     // a decode item is dealt to at most 16 waves
 constexpr int64_t kDecFillWaves = 4096; // decode waves a launch aims for (16 per compute unit)

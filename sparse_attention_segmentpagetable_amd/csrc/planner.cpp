@@ -553,8 +553,12 @@ SEGPAGED_API int segpaged_plan_sizes(const segpaged_plan* pl, segpaged_sizes* z)
       n_max = std::max(n_max, n);
     }
     const int64_t nblk = std::max<int64_t>(1, (n_max + 255) / 256);
-    z->select_workspace_bytes =
-        4 * (pl->Hkv * t_max * (pl->G + 1) + pl->Hkv * (int64_t)pl->B * nblk * pl->G * 2);
+    const int64_t nchunk = std::max<int64_t>(1, (n_max + kSelChunk - 1) / kSelChunk);
+    const int64_t floats = pl->Hkv * t_max * (pl->G + 1) + pl->Hkv * (int64_t)pl->B * nblk * pl->G * 2;
+    // then, 16-byte aligned, the per-chunk histograms: 64-bit mass sums (256 bins and
+    // the chunk total) and 32-bit counts
+    z->select_workspace_bytes = (4 * floats + 15) / 16 * 16 +
+                                pl->Hkv * (int64_t)pl->B * nchunk * (257 * 8 + 256 * 4);
   }
   return SEGPAGED_OK;
 }

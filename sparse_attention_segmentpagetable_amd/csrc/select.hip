@@ -10,10 +10,13 @@
 //   select_scores_kernel  scores of 256 keys x G heads per workgroup (bf16 MFMA,
 //                         fp32, log2 units), with each block's max and exp-sum
 //                         per head
-//   select_topp_kernel    one workgroup per pair: the masses, then a radix
-//                         select on their bits (8 bits per pass, larger first)
-//                         with each bin's mass summed alongside in fixed point,
-//                         then the positions taken in order by a block scan
+//   select_mass_kernel    per chunk of 2048 keys of a pair: the pair's
+//                         normalisers, the masses, and the histogram of their
+//                         top 8 bits with each bin's mass in fixed point
+//   select_topp_kernel    one workgroup per pair: the first radix pass from the
+//                         chunk histograms, three more passes (8 bits each,
+//                         larger values first) over the masses in LDS, then the
+//                         positions taken in order by a block scan
 // Every sum is taken in a fixed order or in exact integer arithmetic, so the set
 // is the same on every call.
 #include <hip/hip_runtime.h>
@@ -139,11 +142,11 @@ __global__ __launch_bounds__(kSelThreads) void select_scores_kernel(
 }
 
 // Top-p over the keys of (b, h), one workgroup of kTopThreads per pair: the
-// pair's normalisers from the block partials, the masses (kept in LDS up to
-// kLdsKeys keys, else in the workspace), then a radix select on the masses'
-// bits, 8 bits per pass, larger values first. Each bin's mass is summed in
-// fixed point (mass * 2^40, 64-bit integer adds in LDS), so the sums are exact
-// and the same on every call.
+// masses come from the workspace (kept in LDS up to kLdsKeys keys), the first
+// radix pass from the merged chunk histograms, then three more passes on the
+// masses' bits, 8 bits per pass, larger values first. Each bin's mass is summed
+// in fixed point (mass * 2^40, 64-bit integer adds), so the sums are exact and
+// the same on every call.
 constexpr int kTopThreads = 1024;
 constexpr int kTopWaves = kTopThreads / 64;
 constexpr int kLdsKeys = 32768;
@@ -158,15 +161,51 @@ __device__ unsigned long long wave_sum_u64(unsigned long long v) {
   return v;
 }
 
-// fixed-order reductions over the workgroup
-__device__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long* red) {
-  v = wave_sum_u64(v);
+// Radix-select step over 256 bins (counts hc, fixed-point masses hs), taken from
+// the largest bin down: the chosen bin is the largest k whose bins k..255 hold a
+// mass of at least R (that bin holds mass, so it is not empty); when all of them
+// hold less (candidates below the fixed-point step) it is the lowest non-empty
+// bin. acc is the mass of the bins above the chosen one. Threads 0..255 take one
+// bin each, in reverse so that a prefix scan gives the sums from the top.
+struct BinPick {
+  unsigned long long wsum[4];
+  int kstar, low, chosen;
+  unsigned long long acc;
+};
+__device__ void choose_bin(const unsigned int* hc, const unsigned long long* hs,
+                           unsigned long long R, BinPick& bp) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = 255 - tid;
+  unsigned long long v = 0, incl = 0;
+  if (tid == 0) {
+    bp.kstar = -1;
+    bp.low = 256;
+  }
+  if (tid < 256) {
+    v = hs[k];
+    incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned long long y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) bp.wsum[wave] = incl;
+  }
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  if (tid < 256) {
+    for (int w = 0; w < wave; ++w) incl += bp.wsum[w];  // mass of bins k..255
+    const unsigned long long ge = __ballot(incl >= R);  // holds for k <= kstar
+    const unsigned long long ne = __ballot(hc[k] != 0u);
+    if (lane == 0 && ge) atomicMax(&bp.kstar, 255 - (wave * 64 + __ffsll((long long)ge) - 1));
+    if (lane == 0 && ne) atomicMin(&bp.low, 255 - (wave * 64 + 63 - __clzll((long long)ne)));
+  }
   __syncthreads();
-  unsigned long long t = 0;
-  for (int w = 0; w < kTopWaves; ++w) t += red[w];
-  return t;
+  const int chosen = bp.kstar >= 0 ? bp.kstar : bp.low;
+  if (tid < 256 && k == chosen) {
+    bp.chosen = chosen;
+    bp.acc = incl - v;
+  }
+  __syncthreads();
 }
 // exclusive prefix sum in thread order
 __device__ int block_scan_top(int v, int* wtot, int& total) {
@@ -189,11 +228,149 @@ __device__ int block_scan_top(int v, int* wtot, int& total) {
   return base + x - v;
 }
 
-__global__ __launch_bounds__(kTopThreads) void select_topp_kernel(
+// The G normalisers of a pair from the block partials of the scores kernel, with
+// the threads of one workgroup of NT (fixed order: each thread over its share of
+// the partials, then the waves in order), into sm (max, log2 units) and sl (1/sum).
+template <int NT>
+__device__ void pair_normalisers(const float* part, int nb, int G, float* sm, float* sl,
+                                 float (*redg)[kMaxGroup]) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float v[kMaxGroup];
+#pragma unroll
+  for (int g = 0; g < kMaxGroup; ++g) v[g] = -INFINITY;
+  for (int k = tid; k < nb; k += NT)
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g)
+      if (g < G) v[g] = fmaxf(v[g], part[((int64_t)k * G + g) * 2]);
+#pragma unroll
+  for (int g = 0; g < kMaxGroup; ++g) {
+    if (g < G) {
+      v[g] = wave_max(v[g]);
+      if (lane == 0) redg[wave][g] = v[g];
+    }
+  }
+  __syncthreads();
+  if (tid < G) {
+    float t = redg[0][tid];
+    for (int w = 1; w < NW; ++w) t = fmaxf(t, redg[w][tid]);
+    sm[tid] = t;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < kMaxGroup; ++g) v[g] = 0.f;
+  for (int k = tid; k < nb; k += NT)
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g)
+      if (g < G)
+        v[g] += part[((int64_t)k * G + g) * 2 + 1] * exp2f(part[((int64_t)k * G + g) * 2] - sm[g]);
+#pragma unroll
+  for (int g = 0; g < kMaxGroup; ++g) {
+    if (g < G) {
+      v[g] = wave_sum(v[g]);
+      if (lane == 0) redg[wave][g] = v[g];
+    }
+  }
+  __syncthreads();
+  if (tid < G) {
+    float t = 0.f;
+    for (int w = 0; w < NW; ++w) t += redg[w][tid];
+    sl[tid] = 1.f / t;
+  }
+  __syncthreads();
+}
+
+// Masses of keys [chunk * kSelChunk, +kSelChunk) of a pair (mean over the G heads
+// of each head's softmax weight), into ws_m, and the chunk's histogram of the
+// masses' top 8 bits: counts, and mass sums in fixed point (mass * 2^40) with the
+// chunk's total in bin 256.
+constexpr int kMassThreads = 256;
+__global__ __launch_bounds__(kMassThreads) void select_mass_kernel(
     const int32_t* __restrict__ tab, int32_t off_seqs, int32_t off_units, int32_t layer, int32_t B,
     int32_t Hkv, int32_t G, int32_t T, const float* __restrict__ ws_s,
-    const float* __restrict__ ws_part, int32_t nblk, float* __restrict__ ws_m, float p,
-    int32_t* __restrict__ out_pos, int32_t* __restrict__ out_cnt) {
+    const float* __restrict__ ws_part, int32_t nblk, float* __restrict__ ws_m,
+    unsigned long long* __restrict__ hsum, unsigned int* __restrict__ hcnt, int32_t nchunk) {
+  const int b = blockIdx.y / Hkv, h = blockIdx.y % Hkv, ch = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t* ur = tab + off_units + kUnitInts * ((layer * B + b) * Hkv + h);
+  const int32_t N = tab[off_seqs + kSeqInts * b + S_N];
+  const int32_t kvo = tab[off_seqs + kSeqInts * b + S_KVOFF];
+  if (ur[U_KIND] != SEGPAGED_RETRIEVAL || ch * kSelChunk >= N) return;  // uniform
+  __shared__ float sm[kMaxGroup], sl[kMaxGroup], redg[kMassThreads / 64][kMaxGroup];
+  __shared__ unsigned int hc[256];
+  __shared__ unsigned long long hs[257];
+  __shared__ unsigned long long redu[kMassThreads / 64];
+  for (int k = tid; k < 256; k += kMassThreads) { hc[k] = 0; hs[k] = 0; }
+  const int nb = (N + kSelKeys - 1) / kSelKeys;
+  pair_normalisers<kMassThreads>(ws_part + ((int64_t)h * B + b) * nblk * G * 2, nb, G, sm, sl,
+                                 redg);
+  const float* S = ws_s + ((int64_t)h * T + kvo) * G;
+  float* Mg = ws_m + (int64_t)h * T + kvo;
+  const float inv_g = 1.f / (float)G;
+  unsigned long long tfx = 0;
+  constexpr int kPer = kSelChunk / kMassThreads;  // keys per thread, all loads in flight
+  const int32_t j0 = ch * kSelChunk + tid;
+  float m[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) m[u] = 0.f;
+  if ((G & 3) == 0) {  // 16-byte loads of a key's G scores
+    for (int g = 0; g < G; g += 4) {
+      float4 x[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int32_t j = min(j0 + u * kMassThreads, N - 1);
+        x[u] = *reinterpret_cast<const float4*>(S + (int64_t)j * G + g);
+      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        m[u] += __builtin_amdgcn_exp2f(x[u].x - sm[g]) * sl[g];
+        m[u] += __builtin_amdgcn_exp2f(x[u].y - sm[g + 1]) * sl[g + 1];
+        m[u] += __builtin_amdgcn_exp2f(x[u].z - sm[g + 2]) * sl[g + 2];
+        m[u] += __builtin_amdgcn_exp2f(x[u].w - sm[g + 3]) * sl[g + 3];
+      }
+    }
+  } else {
+    for (int g = 0; g < G; ++g) {
+      float x[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) x[u] = S[(int64_t)min(j0 + u * kMassThreads, N - 1) * G + g];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) m[u] += __builtin_amdgcn_exp2f(x[u] - sm[g]) * sl[g];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int32_t j = j0 + u * kMassThreads;
+    if (j < N) {
+      const float mu = m[u] * inv_g;
+      Mg[j] = mu;
+      const unsigned long long fx = to_fx(mu);
+      tfx += fx;
+      const uint32_t bin = __float_as_uint(mu) >> 24;
+      atomicAdd(&hc[bin], 1u);
+      atomicAdd(&hs[bin], fx);
+    }
+  }
+  tfx = wave_sum_u64(tfx);
+  if ((tid & 63) == 0) redu[tid >> 6] = tfx;
+  __syncthreads();
+  const int64_t rec = ((int64_t)h * B + b) * nchunk + ch;
+  for (int k = tid; k < 256; k += kMassThreads) {
+    hsum[rec * 257 + k] = hs[k];
+    hcnt[rec * 256 + k] = hc[k];
+  }
+  if (tid == 0) {
+    unsigned long long t = 0;
+    for (int w = 0; w < kMassThreads / 64; ++w) t += redu[w];
+    hsum[rec * 257 + 256] = t;
+  }
+}
+
+__global__ __launch_bounds__(kTopThreads) void select_topp_kernel(
+    const int32_t* __restrict__ tab, int32_t off_seqs, int32_t off_units, int32_t layer, int32_t B,
+    int32_t Hkv, int32_t T, const float* __restrict__ ws_m,
+    const unsigned long long* __restrict__ hsum, const unsigned int* __restrict__ hcnt,
+    int32_t nchunk, float p, int32_t* __restrict__ out_pos, int32_t* __restrict__ out_cnt) {
   const int b = blockIdx.x / Hkv, h = blockIdx.x % Hkv;
   const int tid = threadIdx.x;
   const int32_t* ur = tab + off_units + kUnitInts * ((layer * B + b) * Hkv + h);
@@ -207,124 +384,76 @@ __global__ __launch_bounds__(kTopThreads) void select_topp_kernel(
   // consecutive keys (the final pass) meets other threads' runs in other banks
   __shared__ float sM[kLdsKeys + kLdsKeys / 32];
   __shared__ unsigned int hc[256];
-  __shared__ unsigned long long hs[256];
-  __shared__ float sm[kMaxGroup], sl[kMaxGroup], redg[kTopWaves][kMaxGroup];
-  __shared__ unsigned long long redu[kTopWaves];
+  __shared__ unsigned long long hs[257];
   __shared__ int wtot[kTopWaves];
-  __shared__ int s_chosen;
-  __shared__ unsigned long long s_acc;
+  __shared__ BinPick bp;
   const bool in_lds = N <= kLdsKeys;
-  float* Mg = ws_m + (int64_t)h * T + kvo;
+  const float* Mg = ws_m + (int64_t)h * T + kvo;
   auto mass_at = [&](int32_t j) { return in_lds ? sM[j + (j >> 5)] : Mg[j]; };
-  const int lane = tid & 63, wave = tid >> 6;
-  // normalisers of the G heads over all N keys, every head at once: each thread
-  // over its share of the block partials, then the waves in a fixed order
-  const int nb = (N + kSelKeys - 1) / kSelKeys;
-  const float* part = ws_part + ((int64_t)h * B + b) * nblk * G * 2;
-  {
-    float v[kMaxGroup];
+  // the first radix pass and the total from the chunk histograms (integer sums)
+  const int nch = (N + kSelChunk - 1) / kSelChunk;
+  const int64_t rec0 = ((int64_t)h * B + b) * nchunk;
+  if (tid < 257) {  // chunks 8 at a time, their loads in flight together
+    unsigned long long t = 0;
+    unsigned int c = 0;
+    for (int q0 = 0; q0 < nch; q0 += 8) {
+      unsigned long long a[8];
+      unsigned int n8[8];
 #pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g) v[g] = -INFINITY;
-    for (int k = tid; k < nb; k += kTopThreads)
-#pragma unroll
-      for (int g = 0; g < kMaxGroup; ++g)
-        if (g < G) v[g] = fmaxf(v[g], part[((int64_t)k * G + g) * 2]);
-#pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g) {
-      if (g < G) {
-        v[g] = wave_max(v[g]);
-        if (lane == 0) redg[wave][g] = v[g];
+      for (int u = 0; u < 8; ++u) {
+        const int64_t r = rec0 + min(q0 + u, nch - 1);
+        a[u] = hsum[r * 257 + tid];
+        n8[u] = hcnt[r * 256 + min(tid, 255)];
       }
-    }
-    __syncthreads();
-    if (tid < G) {
-      float t = redg[0][tid];
-      for (int w = 1; w < kTopWaves; ++w) t = fmaxf(t, redg[w][tid]);
-      sm[tid] = t;
-    }
-    __syncthreads();
 #pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g) v[g] = 0.f;
-    for (int k = tid; k < nb; k += kTopThreads)
-#pragma unroll
-      for (int g = 0; g < kMaxGroup; ++g)
-        if (g < G)
-          v[g] += part[((int64_t)k * G + g) * 2 + 1] * exp2f(part[((int64_t)k * G + g) * 2] - sm[g]);
-#pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g) {
-      if (g < G) {
-        v[g] = wave_sum(v[g]);
-        if (lane == 0) redg[wave][g] = v[g];
-      }
+      for (int u = 0; u < 8; ++u)
+        if (q0 + u < nch) { t += a[u]; c += n8[u]; }
     }
-    __syncthreads();
-    if (tid < G) {
-      float t = 0.f;
-      for (int w = 0; w < kTopWaves; ++w) t += redg[w][tid];
-      sl[tid] = 1.f / t;
-    }
-    __syncthreads();
+    hs[tid] = t;
+    if (tid < 256) hc[tid] = c;
   }
-  // masses, and their total in fixed point
-  const float* S = ws_s + ((int64_t)h * T + kvo) * G;
-  const float inv_g = 1.f / (float)G;
-  unsigned long long tfx = 0;
-  for (int32_t j = tid; j < N; j += kTopThreads) {
-    float m = 0.f;
-    const float* sj = S + (int64_t)j * G;
-    if ((G & 3) == 0) {  // 16-byte loads of the key's G scores
-      for (int g = 0; g < G; g += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(sj + g);
-        m += __builtin_amdgcn_exp2f(x.x - sm[g]) * sl[g];
-        m += __builtin_amdgcn_exp2f(x.y - sm[g + 1]) * sl[g + 1];
-        m += __builtin_amdgcn_exp2f(x.z - sm[g + 2]) * sl[g + 2];
-        m += __builtin_amdgcn_exp2f(x.w - sm[g + 3]) * sl[g + 3];
+  if (in_lds) {  // 8 loads in flight per thread
+    for (int32_t jb = 0; jb < N; jb += 8 * kTopThreads) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = Mg[min(jb + u * kTopThreads + tid, N - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int32_t j = jb + u * kTopThreads + tid;
+        if (j < N) sM[j + (j >> 5)] = v[u];
       }
-    } else {
-      for (int g = 0; g < G; ++g) m += __builtin_amdgcn_exp2f(sj[g] - sm[g]) * sl[g];
     }
-    m *= inv_g;
-    if (in_lds) sM[j + (j >> 5)] = m; else Mg[j] = m;
-    tfx += to_fx(m);
   }
-  const unsigned long long total = block_sum_u64(tfx, redu);
+  __syncthreads();
+  const unsigned long long total = hs[256];
   unsigned long long R = (unsigned long long)((double)p * (double)total);  // still to take
   if (R == 0) R = 1;
   uint32_t prefix = 0, mask = 0;
   unsigned int c_eq = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int k = tid; k < 256; k += kTopThreads) { hc[k] = 0; hs[k] = 0; }
-    __syncthreads();
-    for (int32_t j = tid; j < N; j += kTopThreads) {
-      const float m = mass_at(j);
-      const uint32_t u = __float_as_uint(m);
-      if ((u & mask) != prefix) continue;
-      const uint32_t bin = (u >> shift) & 255u;
-      atomicAdd(&hc[bin], 1u);
-      atomicAdd(&hs[bin], to_fx(m));
-    }
-    __syncthreads();
-    if (tid == 0) {  // the bin holding the last value taken, from the largest bin down
-      unsigned long long acc = 0;
-      int chosen = -1, lowest = -1;
-      for (int k = 255; k >= 0; --k) {
-        if (hc[k] == 0) continue;
-        lowest = k;
-        if (acc + hs[k] >= R) { chosen = k; break; }
-        acc += hs[k];
+    if (shift < 24) {  // the first pass's histogram came from the chunks
+      for (int k = tid; k < 256; k += kTopThreads) { hc[k] = 0; hs[k] = 0; }
+      __syncthreads();
+      for (int32_t jb = 0; jb < N; jb += 4 * kTopThreads) {
+        uint32_t u[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) u[x] = __float_as_uint(mass_at(min(jb + x * kTopThreads + tid, N - 1)));
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          if (jb + x * kTopThreads + tid < N && (u[x] & mask) == prefix) {
+            const uint32_t bin = (u[x] >> shift) & 255u;
+            atomicAdd(&hc[bin], 1u);
+            atomicAdd(&hs[bin], to_fx(__uint_as_float(u[x])));
+          }
+        }
       }
-      if (chosen < 0) {  // every candidate (masses below the fixed-point step)
-        chosen = lowest;
-        acc -= hs[lowest];
-      }
-      s_chosen = chosen;
-      s_acc = acc;
+      __syncthreads();
     }
-    __syncthreads();
-    R -= s_acc;
-    prefix |= (uint32_t)s_chosen << shift;
+    choose_bin(hc, hs, R, bp);
+    R -= bp.acc;
+    prefix |= (uint32_t)bp.chosen << shift;
     mask |= 255u << shift;
-    c_eq = hc[s_chosen];
+    c_eq = hc[bp.chosen];
     __syncthreads();
   }
   // keys of mass above the threshold, then the first t (by position) equal to it
@@ -333,10 +462,13 @@ __global__ __launch_bounds__(kTopThreads) void select_topp_kernel(
   if (tau_fx > 0) t = (int)min((unsigned long long)c_eq, max(1ull, (R + tau_fx - 1) / tau_fx));
   const int32_t per = (N + kTopThreads - 1) / kTopThreads;
   const int32_t lo = min(N, tid * per), hi = min(N, lo + per);
-  int ties = 0;
-  for (int32_t j = lo; j < hi; ++j) ties += __float_as_uint(mass_at(j)) == prefix;
-  int ties_total;
-  const int tie_base = block_scan_top(ties, wtot, ties_total);
+  int tie_base = 0;
+  if (t < (int)c_eq) {  // only the first t ties by position are taken: count them first
+    int ties = 0;
+    for (int32_t j = lo; j < hi; ++j) ties += __float_as_uint(mass_at(j)) == prefix;
+    int ties_total;
+    tie_base = block_scan_top(ties, wtot, ties_total);
+  }
   int nsel = 0, tr = tie_base;
   for (int32_t j = lo; j < hi; ++j) {
     const uint32_t u = __float_as_uint(mass_at(j));
@@ -379,11 +511,15 @@ SEGPAGED_API int segpaged_select_topp(const segpaged_plan* pl, int32_t layer, co
     nmax = std::max<int64_t>(nmax, pl->buf[pl->off_seqs + kSeqInts * b + S_N]);
   const int64_t nblk = std::max<int64_t>(1, (nmax + kSelKeys - 1) / kSelKeys);
   const int64_t s_floats = Hkv * T * G, m_floats = Hkv * T, part_floats = Hkv * B * nblk * G * 2;
-  const int64_t need = 4 * (s_floats + m_floats + part_floats);
+  const int64_t nchunk = std::max<int64_t>(1, (nmax + kSelChunk - 1) / kSelChunk);
+  const int64_t hist_off = (4 * (s_floats + m_floats + part_floats) + 15) / 16 * 16;
+  const int64_t need = hist_off + Hkv * B * nchunk * (257 * 8 + 256 * 4);
   if (workspace_bytes < need) return SEGPAGED_ENOSPACE;
   float* ws_s = (float*)workspace;
   float* ws_m = ws_s + s_floats;
   float* ws_part = ws_m + m_floats;
+  unsigned long long* hsum = (unsigned long long*)((char*)workspace + hist_off);
+  unsigned int* hcnt = (unsigned int*)(hsum + Hkv * B * nchunk * 257);
   hipStream_t st = (hipStream_t)stream;
   const float c = scale * kLog2eSel;
   const dim3 g1((unsigned)nblk, (unsigned)(B * Hkv)), blk(kSelThreads);
@@ -398,10 +534,15 @@ SEGPAGED_API int segpaged_select_topp(const segpaged_plan* pl, int32_t layer, co
                        (int32_t)T, (const uint16_t*)q, (const uint16_t*)k_dense, c, ws_s, ws_part,
                        (int32_t)nblk);
   if (hipGetLastError() != hipSuccess) return SEGPAGED_EHIP;
+  hipLaunchKernelGGL(select_mass_kernel, dim3((unsigned)nchunk, (unsigned)(B * Hkv)),
+                     dim3(kMassThreads), 0, st, d_table, (int32_t)pl->off_seqs,
+                     (int32_t)pl->off_units, layer, (int32_t)B, (int32_t)Hkv, (int32_t)G,
+                     (int32_t)T, ws_s, ws_part, (int32_t)nblk, ws_m, hsum, hcnt, (int32_t)nchunk);
+  if (hipGetLastError() != hipSuccess) return SEGPAGED_EHIP;
   hipLaunchKernelGGL(select_topp_kernel, dim3((unsigned)(B * Hkv)), dim3(kTopThreads), 0, st,
                      d_table, (int32_t)pl->off_seqs, (int32_t)pl->off_units, layer, (int32_t)B,
-                     (int32_t)Hkv, (int32_t)G, (int32_t)T, ws_s, ws_part, (int32_t)nblk, ws_m, p,
-                     out_pos, out_cnt);
+                     (int32_t)Hkv, (int32_t)T, ws_m, hsum, hcnt, (int32_t)nchunk, p, out_pos,
+                     out_cnt);
   return hipGetLastError() == hipSuccess ? SEGPAGED_OK : SEGPAGED_EHIP;
 }
 
