@@ -53,7 +53,9 @@ def _run(spec, layer, qb, kb, p):
 
 
 CASES = [("d128-g4", 128, 8, (700, 1029, 64)), ("d64-g16", 64, 32, (3000, 1, 257)),
-         ("d128-g8-long", 128, 16, (40000, 32768, 32769))]  # masses past the LDS limit
+         ("d128-g8-long", 128, 16, (40000, 32768, 32769)),  # masses past the LDS limit
+         # group sizes that are not a multiple of 4, lengths at the 2048-key chunk edges
+         ("d128-g3-chunks", 128, 6, (2048, 2049, 4095)), ("d64-g1", 64, 2, (6000, 1, 2))]
 
 
 @pytest.mark.parametrize("name,hd,hq,n", CASES, ids=[c[0] for c in CASES])
