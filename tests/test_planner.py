@@ -234,3 +234,39 @@ def test_probe_library_exports_its_header_symbols():
     assert lib.segpaged_probe_hbm_read(fake, 24, 1, 8, fake, None) == -1
     assert lib.segpaged_probe_hbm_read(fake, 16, 0, 8, fake, None) == -1
     assert lib.segpaged_probe_hbm_read(fake, 16, 1, 5, fake, None) == -1
+
+
+def test_select_and_transfer_validation_without_gpu():
+    """segpaged_select_topp and the page-stream calls reject bad arguments before
+    touching the GPU: null or misaligned buffers (EINVAL), scale or p out of range
+    (EINVAL), a layer out of range (ESTATE), a workspace one byte short (ENOSPACE)."""
+    lib = sp.library()
+    vp, f32 = ctypes.c_void_p, ctypes.c_float
+    fake = vp(1 << 20)
+    kind = [W.RETRIEVAL, W.LOCAL, W.GLOBAL, W.RETRIEVAL]
+    spec = W.Spec(name="sel", num_layers=2, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                  page_size=64, seq_len=[300, 70], first_query_pos=[0, 0], kind=kind,
+                  sink=[0, 4, 0, 0], window=[1, 20, 1, 1],
+                  retrieval={(b, l, h): np.zeros(0, np.int32) for b in range(2) for l in range(2)
+                             for h in range(2) if kind[l * 2 + h] == W.RETRIEVAL}, seed=3)
+    plan = sp.Plan(W.decode_form(spec))
+    need = plan.sizes.select_workspace_bytes
+
+    def sel(layer=0, q=fake, scale=0.1, p=0.9, ws=fake, nbytes=need):
+        return lib.segpaged_select_topp(plan.handle, layer, q, fake, fake, f32(scale), f32(p),
+                                        fake, fake, ws, nbytes, None)
+
+    assert sel(q=None) == -1
+    assert sel(q=vp((1 << 20) + 8)) == -1        # Q not 16-byte aligned
+    assert sel(ws=None) == -1
+    for p in (0.0, -0.5, 1.01, float("nan")):
+        assert sel(p=p) == -1, p
+    for scale in (0.0, -1.0, float("inf"), float("nan")):
+        assert sel(scale=scale) == -1, scale
+    assert sel(layer=2) == -5 and sel(layer=-1) == -5
+    assert sel(nbytes=need - 1) == -3
+    for fn in (lib.segpaged_export_pages, lib.segpaged_import_pages):
+        assert fn(plan.handle, 0, None, fake, fake, fake, fake, fake, None) == -1
+        assert fn(plan.handle, 0, fake, vp((1 << 20) + 4), fake, fake, fake, fake, None) == -1
+        assert fn(plan.handle, 2, fake, fake, fake, fake, fake, fake, None) == -5
+        assert fn(plan.handle, -2, fake, fake, fake, fake, fake, fake, None) == -5
