@@ -71,8 +71,8 @@ __global__ __launch_bounds__(kSelThreads) void select_scores_kernel(
   const int32_t N = tab[off_seqs + kSeqInts * b + S_N];
   const int32_t kvo = tab[off_seqs + kSeqInts * b + S_KVOFF];
   if (blk * kSelKeys >= N) return;  // uniform over the workgroup
-  __shared__ float ssc[kSelKeys][kMaxGroup];
-  __shared__ float red[kMaxGroup][4];
+  __shared__ float ssc[kSelKeys][kMaxGroup + 1];  // padded: a thread's row in its own bank
+  __shared__ float red[kMaxGroup][4][2];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
   // Q^T operand: head n (zero past G), dims 32 ks + 8 g .. + 7
@@ -105,39 +105,35 @@ __global__ __launch_bounds__(kSelThreads) void select_scores_kernel(
     }
   }
   __syncthreads();
-  // thread t: key t of the block
+  // thread t: key t of the block. Per head, each wave's max and exp-sum in one
+  // pass, then the four waves merged in order by thread g < G.
   const int32_t j = blk * kSelKeys + (int32_t)threadIdx.x;
   const bool ok = j < N;
   float* srow = ws_s + ((int64_t)h * T + kvo + j) * G;
 #pragma unroll
   for (int g = 0; g < kMaxGroup; ++g) {
     if (g < G) {
-      const float sv = ssc[threadIdx.x][g];
+      const float sv = ok ? ssc[threadIdx.x][g] : -INFINITY;
       if (ok) srow[g] = sv;
-      const float m = wave_max(ok ? sv : -INFINITY);
-      if (lane == 0) red[g][wave] = m;
-    }
-  }
-  __syncthreads();
-  float mb[kMaxGroup];
-#pragma unroll
-  for (int g = 0; g < kMaxGroup; ++g)
-    mb[g] = g < G ? fmaxf(fmaxf(red[g][0], red[g][1]), fmaxf(red[g][2], red[g][3])) : 0.f;
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < kMaxGroup; ++g) {
-    if (g < G) {
-      const float e = ok ? exp2f(ssc[threadIdx.x][g] - mb[g]) : 0.f;
-      const float l = wave_sum(e);
-      if (lane == 0) red[g][wave] = l;
+      const float m = wave_max(sv);  // -inf only for a wave past the last key
+      const float l = wave_sum(ok ? exp2f(sv - (m == -INFINITY ? 0.f : m)) : 0.f);
+      if (lane == 0) {
+        red[g][wave][0] = m;
+        red[g][wave][1] = l;
+      }
     }
   }
   __syncthreads();
   if ((int)threadIdx.x < G) {
     const int g = threadIdx.x;
+    float mb = red[g][0][0];
+    for (int w = 1; w < 4; ++w) mb = fmaxf(mb, red[g][w][0]);
+    float lb = 0.f;
+    for (int w = 0; w < 4; ++w)
+      if (red[g][w][0] != -INFINITY) lb += red[g][w][1] * exp2f(red[g][w][0] - mb);
     float* part = ws_part + (((int64_t)h * B + b) * nblk + blk) * G * 2 + 2 * g;
-    part[0] = mb[g];
-    part[1] = (red[g][0] + red[g][1]) + (red[g][2] + red[g][3]);
+    part[0] = mb;
+    part[1] = lb;
   }
 }
 
