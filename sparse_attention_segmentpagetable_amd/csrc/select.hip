@@ -293,10 +293,13 @@ __global__ __launch_bounds__(kMassThreads) void select_mass_kernel(
   const int32_t kvo = tab[off_seqs + kSeqInts * b + S_KVOFF];
   if (ur[U_KIND] != SEGPAGED_RETRIEVAL || ch * kSelChunk >= N) return;  // uniform
   __shared__ float sm[kMaxGroup], sl[kMaxGroup], redg[kMassThreads / 64][kMaxGroup];
-  __shared__ unsigned int hc[256];
-  __shared__ unsigned long long hs[257];
+  // a bin's count (at most kSelChunk < 2^12) in bits 52..63 and its fixed-point mass
+  // (below 2^52: the chunk's masses sum to at most about 1, i.e. 2^40) below: one
+  // atomic per key
+  static_assert(kSelChunk < (1 << 12), "bin counts take 12 bits");
+  __shared__ unsigned long long hp[256];
   __shared__ unsigned long long redu[kMassThreads / 64];
-  for (int k = tid; k < 256; k += kMassThreads) { hc[k] = 0; hs[k] = 0; }
+  for (int k = tid; k < 256; k += kMassThreads) hp[k] = 0;
   const int nb = (N + kSelKeys - 1) / kSelKeys;
   pair_normalisers<kMassThreads>(ws_part + ((int64_t)h * B + b) * nblk * G * 2, nb, G, sm, sl,
                                  redg);
@@ -343,8 +346,7 @@ __global__ __launch_bounds__(kMassThreads) void select_mass_kernel(
       const unsigned long long fx = to_fx(mu);
       tfx += fx;
       const uint32_t bin = __float_as_uint(mu) >> 24;
-      atomicAdd(&hc[bin], 1u);
-      atomicAdd(&hs[bin], fx);
+      atomicAdd(&hp[bin], (1ull << 52) + fx);
     }
   }
   tfx = wave_sum_u64(tfx);
@@ -352,8 +354,8 @@ __global__ __launch_bounds__(kMassThreads) void select_mass_kernel(
   __syncthreads();
   const int64_t rec = ((int64_t)h * B + b) * nchunk + ch;
   for (int k = tid; k < 256; k += kMassThreads) {
-    hsum[rec * 257 + k] = hs[k];
-    hcnt[rec * 256 + k] = hc[k];
+    hsum[rec * 257 + k] = hp[k] & ((1ull << 52) - 1);
+    hcnt[rec * 256 + k] = (unsigned int)(hp[k] >> 52);
   }
   if (tid == 0) {
     unsigned long long t = 0;
