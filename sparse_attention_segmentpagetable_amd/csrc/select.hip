@@ -224,54 +224,59 @@ __device__ int block_scan_top(int v, int* wtot, int& total) {
   return base + x - v;
 }
 
+// (m, l) <- the merge of two (max, exp-sum) pairs in log2 units; empty is (-inf, 0)
+__device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
+  const float mx = fmaxf(m, m2);
+  if (mx != -INFINITY) l = l * exp2f(m - mx) + l2 * exp2f(m2 - mx);
+  m = mx;
+}
+
 // The G normalisers of a pair from the block partials of the scores kernel, with
-// the threads of one workgroup of NT (fixed order: each thread over its share of
-// the partials, then the waves in order), into sm (max, log2 units) and sl (1/sum).
+// the threads of one workgroup of NT, into sm (max, log2 units) and sl (1/sum).
+// One pass: each thread merges its share of the partials (all G heads' loads in
+// flight at once), then a fixed xor tree in each wave and the waves in order.
 template <int NT>
 __device__ void pair_normalisers(const float* part, int nb, int G, float* sm, float* sl,
-                                 float (*redg)[kMaxGroup]) {
+                                 float (*redm)[kMaxGroup], float (*redl)[kMaxGroup]) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float v[kMaxGroup];
+  float m[kMaxGroup], l[kMaxGroup];
 #pragma unroll
-  for (int g = 0; g < kMaxGroup; ++g) v[g] = -INFINITY;
-  for (int k = tid; k < nb; k += NT)
+  for (int g = 0; g < kMaxGroup; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+  }
+  for (int k = tid; k < nb; k += NT) {
+    float pm[kMaxGroup], pv[kMaxGroup];
 #pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g)
-      if (g < G) v[g] = fmaxf(v[g], part[((int64_t)k * G + g) * 2]);
+    for (int g = 0; g < kMaxGroup; ++g) {  // heads past G re-read head G - 1, unused
+      const int64_t e = ((int64_t)k * G + min(g, G - 1)) * 2;
+      pm[g] = part[e];
+      pv[g] = part[e + 1];
+    }
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) merge_ml(m[g], l[g], pm[g], pv[g]);
+  }
 #pragma unroll
   for (int g = 0; g < kMaxGroup; ++g) {
     if (g < G) {
-      v[g] = wave_max(v[g]);
-      if (lane == 0) redg[wave][g] = v[g];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const float m2 = __shfl_xor(m[g], off, 64), l2 = __shfl_xor(l[g], off, 64);
+        merge_ml(m[g], l[g], m2, l2);
+      }
+      if (lane == 0) {
+        redm[wave][g] = m[g];
+        redl[wave][g] = l[g];
+      }
     }
   }
   __syncthreads();
   if (tid < G) {
-    float t = redg[0][tid];
-    for (int w = 1; w < NW; ++w) t = fmaxf(t, redg[w][tid]);
-    sm[tid] = t;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < kMaxGroup; ++g) v[g] = 0.f;
-  for (int k = tid; k < nb; k += NT)
-#pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g)
-      if (g < G)
-        v[g] += part[((int64_t)k * G + g) * 2 + 1] * exp2f(part[((int64_t)k * G + g) * 2] - sm[g]);
-#pragma unroll
-  for (int g = 0; g < kMaxGroup; ++g) {
-    if (g < G) {
-      v[g] = wave_sum(v[g]);
-      if (lane == 0) redg[wave][g] = v[g];
-    }
-  }
-  __syncthreads();
-  if (tid < G) {
-    float t = 0.f;
-    for (int w = 0; w < NW; ++w) t += redg[w][tid];
-    sl[tid] = 1.f / t;
+    float mt = redm[0][tid], lt = redl[0][tid];
+    for (int w = 1; w < NW; ++w) merge_ml(mt, lt, redm[w][tid], redl[w][tid]);
+    sm[tid] = mt;
+    sl[tid] = 1.f / lt;
   }
   __syncthreads();
 }
@@ -292,7 +297,8 @@ __global__ __launch_bounds__(kMassThreads) void select_mass_kernel(
   const int32_t N = tab[off_seqs + kSeqInts * b + S_N];
   const int32_t kvo = tab[off_seqs + kSeqInts * b + S_KVOFF];
   if (ur[U_KIND] != SEGPAGED_RETRIEVAL || ch * kSelChunk >= N) return;  // uniform
-  __shared__ float sm[kMaxGroup], sl[kMaxGroup], redg[kMassThreads / 64][kMaxGroup];
+  __shared__ float sm[kMaxGroup], sl[kMaxGroup];
+  __shared__ float redm[kMassThreads / 64][kMaxGroup], redl[kMassThreads / 64][kMaxGroup];
   // a bin's count (at most kSelChunk < 2^12) in bits 52..63 and its fixed-point mass
   // (below 2^52: the chunk's masses sum to at most about 1, i.e. 2^40) below: one
   // atomic per key
@@ -300,32 +306,43 @@ __global__ __launch_bounds__(kMassThreads) void select_mass_kernel(
   __shared__ unsigned long long hp[256];
   __shared__ unsigned long long redu[kMassThreads / 64];
   for (int k = tid; k < 256; k += kMassThreads) hp[k] = 0;
-  const int nb = (N + kSelKeys - 1) / kSelKeys;
-  pair_normalisers<kMassThreads>(ws_part + ((int64_t)h * B + b) * nblk * G * 2, nb, G, sm, sl,
-                                 redg);
   const float* S = ws_s + ((int64_t)h * T + kvo) * G;
   float* Mg = ws_m + (int64_t)h * T + kvo;
   const float inv_g = 1.f / (float)G;
   unsigned long long tfx = 0;
   constexpr int kPer = kSelChunk / kMassThreads;  // keys per thread, all loads in flight
   const int32_t j0 = ch * kSelChunk + tid;
+  // G a multiple of 4: the thread's scores (16-byte loads) are requested before the
+  // normalisers, so their latency passes under those reductions
+  const bool vec = (G & 3) == 0;
+  float4 xs[kMaxGroup / 4][kPer];
+  if (vec) {
+#pragma unroll
+    for (int gq = 0; gq < kMaxGroup / 4; ++gq)
+      if (4 * gq < G)
+#pragma unroll
+        for (int u = 0; u < kPer; ++u)
+          xs[gq][u] = *reinterpret_cast<const float4*>(
+              S + (int64_t)min(j0 + u * kMassThreads, N - 1) * G + 4 * gq);
+  }
+  const int nb = (N + kSelKeys - 1) / kSelKeys;
+  pair_normalisers<kMassThreads>(ws_part + ((int64_t)h * B + b) * nblk * G * 2, nb, G, sm, sl,
+                                 redm, redl);
   float m[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) m[u] = 0.f;
-  if ((G & 3) == 0) {  // 16-byte loads of a key's G scores
-    for (int g = 0; g < G; g += 4) {
-      float4 x[kPer];
+  if (vec) {
 #pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int32_t j = min(j0 + u * kMassThreads, N - 1);
-        x[u] = *reinterpret_cast<const float4*>(S + (int64_t)j * G + g);
-      }
+    for (int gq = 0; gq < kMaxGroup / 4; ++gq) {
+      if (4 * gq < G) {
+        const int g = 4 * gq;
 #pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        m[u] += __builtin_amdgcn_exp2f(x[u].x - sm[g]) * sl[g];
-        m[u] += __builtin_amdgcn_exp2f(x[u].y - sm[g + 1]) * sl[g + 1];
-        m[u] += __builtin_amdgcn_exp2f(x[u].z - sm[g + 2]) * sl[g + 2];
-        m[u] += __builtin_amdgcn_exp2f(x[u].w - sm[g + 3]) * sl[g + 3];
+        for (int u = 0; u < kPer; ++u) {
+          m[u] += __builtin_amdgcn_exp2f(xs[gq][u].x - sm[g]) * sl[g];
+          m[u] += __builtin_amdgcn_exp2f(xs[gq][u].y - sm[g + 1]) * sl[g + 1];
+          m[u] += __builtin_amdgcn_exp2f(xs[gq][u].z - sm[g + 2]) * sl[g + 2];
+          m[u] += __builtin_amdgcn_exp2f(xs[gq][u].w - sm[g + 3]) * sl[g + 3];
+        }
       }
     }
   } else {
