@@ -15,8 +15,9 @@
 //                         top 8 bits with each bin's mass in fixed point
 //   select_topp_kernel    one workgroup per pair: the first radix pass from the
 //                         chunk histograms, three more passes (8 bits each,
-//                         larger values first) over the masses in LDS, then the
-//                         positions taken in order by a block scan
+//                         larger values first) over the masses held in
+//                         registers, then the positions taken in order by a
+//                         block scan
 // Every sum is taken in a fixed order or in exact integer arithmetic, so the set
 // is the same on every call.
 #include <hip/hip_runtime.h>
@@ -138,14 +139,15 @@ __global__ __launch_bounds__(kSelThreads) void select_scores_kernel(
 }
 
 // Top-p over the keys of (b, h), one workgroup of kTopThreads per pair: the
-// masses come from the workspace (kept in LDS up to kLdsKeys keys), the first
-// radix pass from the merged chunk histograms, then three more passes on the
-// masses' bits, 8 bits per pass, larger values first. Each bin's mass is summed
+// masses come from the workspace (held in registers, row-major over the threads,
+// up to kTopThreads * kRegKeys keys), the first radix pass from the
+// merged chunk histograms, then three more passes on the masses' bits, 8 bits per
+// pass, larger values first. Each bin's mass is summed
 // in fixed point (mass * 2^40, 64-bit integer adds), so the sums are exact and
 // the same on every call.
 constexpr int kTopThreads = 1024;
 constexpr int kTopWaves = kTopThreads / 64;
-constexpr int kLdsKeys = 32768;
+constexpr int kRegKeys = 32;  // keys per thread whose mass bits stay in registers
 
 __device__ __forceinline__ unsigned long long to_fx(float m) {
   return (unsigned long long)(m * 1099511627776.0f);  // exact scaling, truncated
@@ -395,16 +397,24 @@ __global__ __launch_bounds__(kTopThreads) void select_topp_kernel(
     if (tid == 0) out_cnt[b * Hkv + h] = 0;
     return;
   }
-  // masses of up to kLdsKeys keys, one pad word per 32 so that a thread's run of
-  // consecutive keys (the final pass) meets other threads' runs in other banks
-  __shared__ float sM[kLdsKeys + kLdsKeys / 32];
   __shared__ unsigned int hc[256];
   __shared__ unsigned long long hs[257];
   __shared__ int wtot[kTopWaves];
   __shared__ BinPick bp;
-  const bool in_lds = N <= kLdsKeys;
+  __shared__ int rc[kRegKeys * kTopWaves];  // per (row, wave): counts, then their prefix
   const float* Mg = ws_m + (int64_t)h * T + kvo;
-  auto mass_at = [&](int32_t j) { return in_lds ? sM[j + (j >> 5)] : Mg[j]; };
+  const int lane = tid & 63, wave = tid >> 6;
+  // Up to kTopThreads * kRegKeys keys, thread t holds the mass bits of keys
+  // i * kTopThreads + t (row i) in registers for every pass (coalesced loads);
+  // beyond that each thread takes a run of consecutive keys from the workspace.
+  const bool in_reg = N <= kTopThreads * kRegKeys;
+  uint32_t mu[kRegKeys];
+  if (in_reg) {
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i)
+      mu[i] = __float_as_uint(Mg[min(i * kTopThreads + tid, N - 1)]);  // past N: unused
+  }
+  auto valid = [&](int i) { return i * kTopThreads + tid < N; };
   // the first radix pass and the total from the chunk histograms (integer sums)
   const int nch = (N + kSelChunk - 1) / kSelChunk;
   const int64_t rec0 = ((int64_t)h * B + b) * nchunk;
@@ -427,18 +437,6 @@ __global__ __launch_bounds__(kTopThreads) void select_topp_kernel(
     hs[tid] = t;
     if (tid < 256) hc[tid] = c;
   }
-  if (in_lds) {  // 8 loads in flight per thread
-    for (int32_t jb = 0; jb < N; jb += 8 * kTopThreads) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = Mg[min(jb + u * kTopThreads + tid, N - 1)];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int32_t j = jb + u * kTopThreads + tid;
-        if (j < N) sM[j + (j >> 5)] = v[u];
-      }
-    }
-  }
   __syncthreads();
   const unsigned long long total = hs[256];
   unsigned long long R = (unsigned long long)((double)p * (double)total);  // still to take
@@ -449,17 +447,25 @@ __global__ __launch_bounds__(kTopThreads) void select_topp_kernel(
     if (shift < 24) {  // the first pass's histogram came from the chunks
       for (int k = tid; k < 256; k += kTopThreads) { hc[k] = 0; hs[k] = 0; }
       __syncthreads();
-      for (int32_t jb = 0; jb < N; jb += 4 * kTopThreads) {
-        uint32_t u[4];
+      auto count = [&](uint32_t u) {
+        if ((u & mask) == prefix) {
+          const uint32_t bin = (u >> shift) & 255u;
+          atomicAdd(&hc[bin], 1u);
+          atomicAdd(&hs[bin], to_fx(__uint_as_float(u)));
+        }
+      };
+      if (in_reg) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) u[x] = __float_as_uint(mass_at(min(jb + x * kTopThreads + tid, N - 1)));
+        for (int i = 0; i < kRegKeys; ++i)
+          if (valid(i)) count(mu[i]);
+      } else {
+        for (int32_t jb = 0; jb < N; jb += 4 * kTopThreads) {
+          uint32_t u[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          if (jb + x * kTopThreads + tid < N && (u[x] & mask) == prefix) {
-            const uint32_t bin = (u[x] >> shift) & 255u;
-            atomicAdd(&hc[bin], 1u);
-            atomicAdd(&hs[bin], to_fx(__uint_as_float(u[x])));
-          }
+          for (int x = 0; x < 4; ++x) u[x] = __float_as_uint(Mg[min(jb + x * kTopThreads + tid, N - 1)]);
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            if (jb + x * kTopThreads + tid < N) count(u[x]);
         }
       }
       __syncthreads();
@@ -475,30 +481,77 @@ __global__ __launch_bounds__(kTopThreads) void select_topp_kernel(
   const unsigned long long tau_fx = to_fx(__uint_as_float(prefix));
   int t = (int)c_eq;
   if (tau_fx > 0) t = (int)min((unsigned long long)c_eq, max(1ull, (R + tau_fx - 1) / tau_fx));
+  const bool all_ties = t >= (int)c_eq;  // uniform
+  int32_t* out = out_pos + (int64_t)h * T + kvo;
+  if (in_reg) {
+    // Position order is row-major over (row i, lane t): a key's rank among the
+    // flagged keys is the flagged count of the (row, wave) pairs before its own
+    // plus its lanes below it in the wave's ballot.
+    auto rank_base = [&](auto flag, int& total_out) {
+#pragma unroll
+      for (int i = 0; i < kRegKeys; ++i) {
+        const unsigned long long bal = __ballot(flag(i));
+        if (lane == 0) rc[i * kTopWaves + wave] = __popcll(bal);
+      }
+      __syncthreads();
+      const int v = tid < kRegKeys * kTopWaves ? rc[tid] : 0;
+      const int base = block_scan_top(v, wtot, total_out);
+      __syncthreads();  // every count read before the prefixes overwrite them
+      if (tid < kRegKeys * kTopWaves) rc[tid] = base;
+      __syncthreads();
+    };
+    auto below = [&](unsigned long long bal) {
+      return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    };
+    bool sel[kRegKeys];
+    if (all_ties) {
+#pragma unroll
+      for (int i = 0; i < kRegKeys; ++i) sel[i] = valid(i) && mu[i] >= prefix;
+    } else {  // the ties' ranks by position decide which of them are taken
+      int ties_total;
+      auto tie = [&](int i) { return valid(i) && mu[i] == prefix; };
+      rank_base(tie, ties_total);
+#pragma unroll
+      for (int i = 0; i < kRegKeys; ++i) {
+        const bool ti = tie(i);
+        const int rank = rc[i * kTopWaves + wave] + below(__ballot(ti));
+        sel[i] = valid(i) && (mu[i] > prefix || (ti && rank < t));
+      }
+      __syncthreads();  // ranks read before the selection counts overwrite them
+    }
+    int nsel_total;
+    rank_base([&](int i) { return sel[i]; }, nsel_total);
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i) {
+      const unsigned long long bal = __ballot(sel[i]);
+      if (sel[i]) out[rc[i * kTopWaves + wave] + below(bal)] = i * kTopThreads + tid;
+    }
+    if (tid == 0) out_cnt[b * Hkv + h] = nsel_total;
+    return;
+  }
+  // runs of consecutive keys per thread, masses from the workspace
   const int32_t per = (N + kTopThreads - 1) / kTopThreads;
   const int32_t lo = min(N, tid * per), hi = min(N, lo + per);
   int tie_base = 0;
-  if (t < (int)c_eq) {  // only the first t ties by position are taken: count them first
+  if (!all_ties) {  // only the first t ties by position are taken: count them first
     int ties = 0;
-    for (int32_t j = lo; j < hi; ++j) ties += __float_as_uint(mass_at(j)) == prefix;
+    for (int32_t j = lo; j < hi; ++j) ties += __float_as_uint(Mg[j]) == prefix;
     int ties_total;
     tie_base = block_scan_top(ties, wtot, ties_total);
   }
   int nsel = 0, tr = tie_base;
-  for (int32_t j = lo; j < hi; ++j) {
-    const uint32_t u = __float_as_uint(mass_at(j));
-    nsel += u > prefix || (u == prefix && tr < t);
+  auto take = [&](uint32_t u) {  // in position order within the run
+    const bool s_ = u > prefix || (u == prefix && tr < t);
     tr += u == prefix;
-  }
+    return s_;
+  };
+  for (int32_t j = lo; j < hi; ++j) nsel += take(__float_as_uint(Mg[j]));
   int nsel_total;
   int pos = block_scan_top(nsel, wtot, nsel_total);
-  int32_t* out = out_pos + (int64_t)h * T + kvo;
   tr = tie_base;
-  for (int32_t j = lo; j < hi; ++j) {
-    const uint32_t u = __float_as_uint(mass_at(j));
-    if (u > prefix || (u == prefix && tr < t)) out[pos++] = j;
-    tr += u == prefix;
-  }
+  for (int32_t j = lo; j < hi; ++j)
+    if (take(__float_as_uint(Mg[j]))) out[pos++] = j;
   if (tid == 0) out_cnt[b * Hkv + h] = nsel_total;
 }
 
