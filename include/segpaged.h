@@ -26,6 +26,8 @@
  *     a stream. Device buffers (pools, table, Q, O, LSE, workspace, dense K/V)
  *     are owned by the caller. `stream` is a hipStream_t passed as void*
  *     (NULL = the null stream) on the current HIP device.
+ *   - k_pool and v_pool may be NULL when the plan has no pages (pool_bytes = 0:
+ *     no head keeps a token), and a page stream of zero elements may be NULL.
  *   - Asynchronous kernel faults surface at the caller's next synchronisation.
  *   - bf16 tensors are raw IEEE bfloat16 bits, row-major, 16-byte aligned.
  *   - A plan changes only in segpaged_plan_append (growth plans); every other call

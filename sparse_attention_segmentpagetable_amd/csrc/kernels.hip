@@ -1295,6 +1295,11 @@ struct Span {
   int64_t max_unit_items;
 };
 
+// The pools may be NULL when the plan has no pages (no head keeps a token).
+bool pools_ok(const segpaged_plan* pl, const void* k_pool, const void* v_pool) {
+  return (k_pool && v_pool) || pl->pool_pages == 0;
+}
+
 Span span_of(const segpaged_plan* pl, int32_t layer) {
   if (layer >= 0) {
     const LayerRange& r = pl->layers[layer];
@@ -1345,7 +1350,8 @@ int launch_page_copy(const segpaged_plan* pl, const Span& sp, const int32_t* d_t
                      const void* k_src, const void* v_src, void* k_dst, void* v_dst,
                      int32_t to_stream, hipStream_t st) {
   const int64_t npages = sp.page_e - sp.page_b;
-  if (npages == 0) return SEGPAGED_OK;
+  if (npages == 0) return SEGPAGED_OK;  // empty streams may be NULL
+  if (!k_src || !v_src || !k_dst || !v_dst) return SEGPAGED_EINVAL;
   const int32_t log2c = pl->log2P + __builtin_ctz((unsigned)pl->D) - 3;  // 16-byte chunks per page
   const int64_t nchunks = npages << log2c;
   const int64_t cus = std::max(device_cus(), 1);
@@ -1363,7 +1369,8 @@ extern "C" {
 SEGPAGED_API int segpaged_build(const segpaged_plan* pl, int32_t layer, const void* k_dense,
                                 const void* v_dense, int32_t* d_table, void* k_pool,
                                 void* v_pool, void* stream) {
-  if (!pl || !k_dense || !v_dense || !d_table || !k_pool || !v_pool) return SEGPAGED_EINVAL;
+  if (!pl || !k_dense || !v_dense || !d_table || !pools_ok(pl, k_pool, v_pool))
+    return SEGPAGED_EINVAL;
   if (!aligned16(k_dense) || !aligned16(v_dense) || !aligned16(k_pool) || !aligned16(v_pool) ||
       !aligned4(d_table))
     return SEGPAGED_EINVAL;
@@ -1397,33 +1404,36 @@ SEGPAGED_API int segpaged_export_pages(const segpaged_plan* pl, int32_t layer,
                                        const int32_t* d_table, const void* k_pool,
                                        const void* v_pool, void* k_out, void* v_out,
                                        void* stream) {
-  if (!pl || !d_table || !k_pool || !v_pool || !k_out || !v_out) return SEGPAGED_EINVAL;
+  if (!pl || !d_table || !pools_ok(pl, k_pool, v_pool)) return SEGPAGED_EINVAL;
   if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_out) || !aligned16(v_out) ||
       !aligned4(d_table))
     return SEGPAGED_EINVAL;
   if (layer < -1 || layer >= pl->L) return SEGPAGED_ESTATE;
-  return launch_page_copy(pl, span_of(pl, layer), d_table, k_pool, v_pool, k_out, v_out, 1,
-                          (hipStream_t)stream);
+  const Span sp = span_of(pl, layer);
+  if (sp.page_e > sp.page_b && (!k_out || !v_out)) return SEGPAGED_EINVAL;
+  return launch_page_copy(pl, sp, d_table, k_pool, v_pool, k_out, v_out, 1, (hipStream_t)stream);
 }
 
 SEGPAGED_API int segpaged_import_pages(const segpaged_plan* pl, int32_t layer, const void* k_in,
                                        const void* v_in, int32_t* d_table, void* k_pool,
                                        void* v_pool, void* stream) {
-  if (!pl || !k_in || !v_in || !d_table || !k_pool || !v_pool) return SEGPAGED_EINVAL;
+  if (!pl || !d_table || !pools_ok(pl, k_pool, v_pool)) return SEGPAGED_EINVAL;
   if (!aligned16(k_in) || !aligned16(v_in) || !aligned16(k_pool) || !aligned16(v_pool) ||
       !aligned4(d_table))
     return SEGPAGED_EINVAL;
   if (layer < -1 || layer >= pl->L) return SEGPAGED_ESTATE;
+  const Span sp = span_of(pl, layer);
+  if (sp.page_e > sp.page_b && (!k_in || !v_in)) return SEGPAGED_EINVAL;
   hipStream_t st = (hipStream_t)stream;
   const int rc = upload_layer_table(pl, layer, d_table, st);
   if (rc) return rc;
-  return launch_page_copy(pl, span_of(pl, layer), d_table, k_in, v_in, k_pool, v_pool, 0, st);
+  return launch_page_copy(pl, sp, d_table, k_in, v_in, k_pool, v_pool, 0, st);
 }
 
 SEGPAGED_API int segpaged_append(segpaged_plan* pl, int32_t layer, const void* k_new,
                                  const void* v_new, int32_t* d_table, void* k_pool, void* v_pool,
                                  void* stream) {
-  if (!pl || !d_table || !k_pool || !v_pool) return SEGPAGED_EINVAL;
+  if (!pl || !d_table || !pools_ok(pl, k_pool, v_pool)) return SEGPAGED_EINVAL;
   if (pl->append_cap <= 0) return SEGPAGED_ESTATE;
   if (layer < -1 || layer >= pl->L) return SEGPAGED_ESTATE;
   const int64_t B = pl->B, Hkv = pl->Hkv;
@@ -1475,7 +1485,7 @@ SEGPAGED_API int segpaged_prefill(const segpaged_plan* pl, int32_t layer, const 
                                   int64_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
-  if (!pl || !q || !d_table || !k_pool || !v_pool || !o) return SEGPAGED_EINVAL;
+  if (!pl || !q || !d_table || !pools_ok(pl, k_pool, v_pool) || !o) return SEGPAGED_EINVAL;
   if (!aligned16(q) || !aligned16(o) || !aligned16(k_pool) || !aligned16(v_pool) ||
       !aligned4(d_table) || (lse && !aligned4(lse)))
     return SEGPAGED_EINVAL;
@@ -1519,7 +1529,7 @@ SEGPAGED_API int segpaged_decode(const segpaged_plan* pl, int32_t layer, const v
                                  const int32_t* d_table, const void* k_pool, const void* v_pool,
                                  float scale, void* o, float* lse, void* workspace,
                                  int64_t workspace_bytes, void* stream) {
-  if (!pl || !q || !d_table || !k_pool || !v_pool || !o) return SEGPAGED_EINVAL;
+  if (!pl || !q || !d_table || !pools_ok(pl, k_pool, v_pool) || !o) return SEGPAGED_EINVAL;
   if (!aligned16(q) || !aligned16(o) || !aligned16(k_pool) || !aligned16(v_pool) ||
       !aligned4(d_table) || (lse && !aligned4(lse)))
     return SEGPAGED_EINVAL;
@@ -1538,7 +1548,7 @@ SEGPAGED_API int segpaged_decode(const segpaged_plan* pl, int32_t layer, const v
   {
     const int64_t keys = layer < 0 ? pl->total.decode_tokens : pl->stats[layer].decode_tokens;
     const int64_t recs = workspace_bytes / rec_bytes;
-    while (sub_log2 < kDecMaxPartsLog2 && (nitems << sub_log2) < kDecFillWaves &&
+    while (nitems > 0 && sub_log2 < kDecMaxPartsLog2 && (nitems << sub_log2) < kDecFillWaves &&
            (nitems << (sub_log2 + 1)) <= recs && keys / (nitems << (sub_log2 + 1)) >= 256)
       ++sub_log2;
   }

@@ -58,42 +58,47 @@ CASES = [("d128-g4", 128, 8, (700, 1029, 64)), ("d64-g16", 64, 32, (3000, 1, 257
          ("d128-g3-chunks", 128, 6, (2048, 2049, 4095)), ("d64-g1", 64, 2, (6000, 1, 2))]
 
 
+def check_sets(spec, layer, qb, kb, pos, cnt, p, name):
+    """Every key whose oracle mass is clearly above the oracle's threshold is taken,
+    none clearly below; the set is sorted, reaches p and is minimal."""
+    kvo, G, hd = spec.kv_row_offsets(), spec.group, spec.head_dim
+    for b, nb in enumerate(spec.seq_len):
+        for h in range(spec.num_kv_heads):
+            kind, _, _ = spec.head_class(layer, h)
+            c = int(cnt[b, h])
+            if kind != W.RETRIEVAL or nb == 0:
+                assert c == 0
+                continue
+            got = pos[h, kvo[b]:kvo[b] + c]
+            mass = OS.key_mass(qb[b, h * G:(h + 1) * G], kb[kvo[b]:kvo[b] + nb, h], 1 / np.sqrt(hd))
+            tau = OS.threshold(mass, p)
+            assert c >= 1 and np.all(np.diff(got) > 0) and got[0] >= 0 and got[-1] < nb
+            sel = set(int(x) for x in got)
+            # masses below fp32's resolution of the total (1e-6 of it) are not
+            # ordered reliably: they are in the set or not
+            must = set(np.nonzero(mass > max(tau * (1 + 1e-4), 1e-6))[0].tolist())
+            assert must <= sel, (name, b, h, len(must - sel))
+            assert all(mass[j] >= tau * (1 - 1e-4) for j in sel)
+            tot = mass[got].sum()
+            assert tot >= p - 1e-5, (tot, p)
+            assert tot - mass[got].min() < p + 1e-5 or p == 1.0
+            ref = OS.top_p(mass, p)
+            print(f"[select] {name} p={p} L{layer} b{b} h{h}: {c} keys (oracle {len(ref)})",
+                  flush=True)
+
+
 @pytest.mark.parametrize("name,hd,hq,n", CASES, ids=[c[0] for c in CASES])
 @pytest.mark.parametrize("p", [0.5, 0.9, 0.99, 1.0])
 def test_select_topp_against_oracle(name, hd, hq, n, p):
     spec = _spec(hd, hq, n)
-    kvo, G = spec.kv_row_offsets(), spec.group
     for layer in range(spec.num_layers):
         qb = _scaled_q(spec, layer, 4.0)
         kb, _ = W.kv_bits(spec, layer)
         pos, cnt = _run(spec, layer, qb, kb, p)
         pos2, cnt2 = _run(spec, layer, qb, kb, p)
         assert np.array_equal(cnt, cnt2)  # the same set on every call
-        for b, nb in enumerate(n):
-            for h in range(spec.num_kv_heads):
-                kind, _, _ = spec.head_class(layer, h)
-                c = int(cnt[b, h])
-                if kind != W.RETRIEVAL:
-                    assert c == 0
-                    continue
-                got = pos[h, kvo[b]:kvo[b] + c]
-                assert np.array_equal(got, pos2[h, kvo[b]:kvo[b] + c])
-                mass = OS.key_mass(qb[b, h * G:(h + 1) * G], kb[kvo[b]:kvo[b] + nb, h],
-                                   1 / np.sqrt(hd))
-                tau = OS.threshold(mass, p)
-                assert np.all(np.diff(got) > 0) and got[0] >= 0 and got[-1] < nb
-                sel = set(int(x) for x in got)
-                # masses below fp32's resolution of the total (1e-6 of it) are not
-                # ordered reliably: they are in the set or not
-                must = set(np.nonzero(mass > max(tau * (1 + 1e-4), 1e-6))[0].tolist())
-                assert must <= sel, (name, b, h, len(must - sel))
-                assert all(mass[j] >= tau * (1 - 1e-4) for j in sel)
-                tot = mass[got].sum()
-                assert tot >= p - 1e-5, (tot, p)
-                assert tot - mass[got].min() < p + 1e-5 or p == 1.0
-                ref = OS.top_p(mass, p)
-                print(f"[select] {name} p={p} L{layer} b{b} h{h}: {c} keys (oracle {len(ref)})",
-                      flush=True)
+        assert np.array_equal(pos, pos2)
+        check_sets(spec, layer, qb, kb, pos, cnt, p, name)
 
 
 def test_select_ties_go_by_position():
@@ -135,3 +140,33 @@ def test_selected_sets_drive_a_decode():
     ref, ref_lse = OA.attention(spec, 0, qb, kb, vb, 1 / np.sqrt(128))
     parity(to_f64(o), ref, "decode over selected retrieval sets")
     lse_parity(lse.cpu().numpy(), ref_lse, "decode over selected retrieval sets")
+
+
+def test_plan_without_pages_takes_null_pools():
+    """Retrieval heads with empty sets only: the plan has no pages, the pools are
+    empty (NULL) and build, prefill and decode still run: no row sees a key."""
+    kind = [W.RETRIEVAL, W.RETRIEVAL]
+    retr = {(b, 0, h): np.zeros(0, np.int32) for b in range(2) for h in range(2)}
+    s = W.Spec(name="nopages", num_layers=1, num_q_heads=4, num_kv_heads=2, head_dim=128,
+               page_size=64, seq_len=[300, 5], first_query_pos=[0, 0], kind=kind, sink=[0, 0],
+               window=[1, 1], retrieval=retr, seed=9)
+    scale = 1 / np.sqrt(128)
+    for spec in (s, W.decode_form(s)):
+        plan = sp.Plan(spec)
+        assert plan.sizes.pool_bytes == 0
+        bufs = plan.allocate(DEV)
+        kb, vb = W.kv_bits(spec, 0)
+        sp.build(plan, 0, to_dev(kb), to_dev(vb), bufs["table"], bufs["k_pool"], bufs["v_pool"])
+        qb = W.q_bits(spec, 0)
+        q = to_dev(qb)
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device=DEV)
+        if spec.first_query_pos[0] == 0:
+            sp.prefill(plan, 0, q, bufs["table"], bufs["k_pool"], bufs["v_pool"], scale, o, lse)
+        else:
+            sp.decode(plan, 0, q, bufs["table"], bufs["k_pool"], bufs["v_pool"], scale, o, lse,
+                      workspace=bufs["workspace"])
+        torch.cuda.synchronize()
+        ref, ref_lse = OA.attention(spec, 0, qb, kb, vb, scale=scale)
+        parity(to_f64(o), ref, "no pages")
+        lse_parity(lse.cpu().numpy(), ref_lse, "no pages")

@@ -270,3 +270,22 @@ def test_select_and_transfer_validation_without_gpu():
         assert fn(plan.handle, 0, fake, vp((1 << 20) + 4), fake, fake, fake, fake, None) == -1
         assert fn(plan.handle, 2, fake, fake, fake, fake, fake, fake, None) == -5
         assert fn(plan.handle, -2, fake, fake, fake, fake, fake, fake, None) == -5
+
+
+def test_decode_without_items_returns_a_status():
+    """A decode-form layer where no unit holds a key (retrieval heads with empty
+    sets) has no decode items: choosing the parts per item must not divide by the
+    item count. Without a GPU the call ends in a HIP status, not a crash."""
+    lib = sp.library()
+    kind = [W.RETRIEVAL, W.RETRIEVAL]
+    spec = W.Spec(name="noitems", num_layers=1, num_q_heads=4, num_kv_heads=2, head_dim=128,
+                  page_size=64, seq_len=[300, 5], first_query_pos=[0, 0], kind=kind,
+                  sink=[0, 0], window=[1, 1],
+                  retrieval={(b, 0, h): np.zeros(0, np.int32) for b in range(2) for h in range(2)},
+                  seed=9)
+    plan = sp.Plan(W.decode_form(spec))
+    assert plan.sizes.decode_items == 0 and plan.sizes.pool_bytes == 0
+    fake, f32 = ctypes.c_void_p(1 << 20), ctypes.c_float
+    rc = lib.segpaged_decode(plan.handle, 0, fake, fake, None, None, f32(0.1), fake, None,
+                             None, 0, None)
+    assert rc in (0, -4), rc
