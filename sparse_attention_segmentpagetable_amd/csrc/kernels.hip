@@ -548,16 +548,6 @@ __device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, ui
 }
 // Empty asm that takes a value in registers: the value is computed before this
 // point, so the compiler cannot sink its computation below a later barrier.
-__device__ __forceinline__ void pin_sgpr(int32_t& x) {
-  x = __builtin_amdgcn_readfirstlane(x);  // uniform by construction
-  asm volatile("" : "+s"(x));
-}
-__device__ __forceinline__ void pin_sgpr(const uint16_t*& p) {
-  uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-  uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)p >> 32));
-  asm volatile("" : "+s"(lo), "+s"(hi));
-  p = (const uint16_t*)(((uintptr_t)hi << 32) | lo);
-}
 __device__ __forceinline__ void pin_vgpr(const f32x16& x) { asm volatile("" ::"v"(x)); }
 // Workgroup barrier without the release/acquire fence of __syncthreads (which
 // would wait for every LDS-DMA in flight); the memory clobber keeps LDS reads

@@ -128,8 +128,6 @@ int64_t tile_cost(int kind, int64_t sink, int64_t window, int64_t r0, int64_t r1
   return blocks;
 }
 
-bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
-
 // Sequence rows from lengths and first query positions (dense K/V rows and Q
 // rows are packed in sequence order).
 void write_seq_rows(segpaged_plan* pl, const int32_t* n, const int32_t* q0) {

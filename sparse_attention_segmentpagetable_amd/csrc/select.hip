@@ -39,8 +39,6 @@ constexpr int kSelKeys = 256;  // keys per scoring workgroup
 constexpr int kSelThreads = 256;
 constexpr float kLog2eSel = 1.4426950408889634f;
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
