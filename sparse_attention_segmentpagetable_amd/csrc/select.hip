@@ -226,15 +226,22 @@ __device__ int block_scan_top(int v, int* wtot, int& total) {
 
 // (m, l) <- the merge of two (max, exp-sum) pairs in log2 units; empty is (-inf, 0)
 __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    l = l2;
+    return;
+  }
   const float mx = fmaxf(m, m2);
-  if (mx != -INFINITY) l = l * exp2f(m - mx) + l2 * exp2f(m2 - mx);
+  l = l * exp2f(m - mx) + l2 * exp2f(m2 - mx);
   m = mx;
 }
 
 // The G normalisers of a pair from the block partials of the scores kernel, with
 // the threads of one workgroup of NT, into sm (max, log2 units) and sl (1/sum).
 // One pass: each thread merges its share of the partials (all G heads' loads in
-// flight at once), then a fixed xor tree in each wave and the waves in order.
+// flight at once); in each wave the max by a fixed xor tree, then every lane's sum
+// rescaled to it and added by the same tree; then the waves in order.
 template <int NT>
 __device__ void pair_normalisers(const float* part, int nb, int G, float* sm, float* sl,
                                  float (*redm)[kMaxGroup], float (*redl)[kMaxGroup]) {
@@ -255,19 +262,17 @@ __device__ void pair_normalisers(const float* part, int nb, int G, float* sm, fl
       pv[g] = part[e + 1];
     }
 #pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g) merge_ml(m[g], l[g], pm[g], pv[g]);
+    for (int g = 0; g < kMaxGroup; ++g)
+      if (g < G) merge_ml(m[g], l[g], pm[g], pv[g]);
   }
 #pragma unroll
   for (int g = 0; g < kMaxGroup; ++g) {
     if (g < G) {
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float m2 = __shfl_xor(m[g], off, 64), l2 = __shfl_xor(l[g], off, 64);
-        merge_ml(m[g], l[g], m2, l2);
-      }
+      const float mw = wave_max(m[g]);
+      const float lw = wave_sum(m[g] == -INFINITY ? 0.f : l[g] * exp2f(m[g] - mw));
       if (lane == 0) {
-        redm[wave][g] = m[g];
-        redl[wave][g] = l[g];
+        redm[wave][g] = mw;
+        redl[wave][g] = lw;
       }
     }
   }
