@@ -30,9 +30,10 @@
  *     no head keeps a token), and a page stream of zero elements may be NULL.
  *   - Asynchronous kernel faults surface at the caller's next synchronisation.
  *   - bf16 tensors are raw IEEE bfloat16 bits, row-major, 16-byte aligned.
- *   - A plan changes only in segpaged_plan_append (growth plans); every other call
- *     takes it read-only, and concurrent read-only calls that share a plan are
- *     safe. A plan must outlive all work enqueued with it.
+ *   - A plan's layout changes only in segpaged_plan_append (growth plans); every
+ *     other call reads it (segpaged_prefill also advances an atomic launch
+ *     generation inside it), and concurrent calls that do not append and share a
+ *     plan are safe. A plan must outlive all work enqueued with it.
  */
 #ifndef SEGPAGED_H
 #define SEGPAGED_H
@@ -194,18 +195,26 @@ SEGPAGED_API int segpaged_build(const segpaged_plan* plan, int32_t layer,
  * sequence and every Q head hq (KV head h = hq / G):
  *     O = sum_{j in vis(i)} softmax_j(scale * q_i . k_j) v_j,   LSE = log sum exp
  * reading only the pages of (layer, b, h); blocks no row of a tile can see are
- * never read, and no mask tensor exists.
+ * never read, and no mask tensor exists. Scores and row sums are fp32; the
+ * softmax weights enter the P.V products as bf16, except in tiles whose first
+ * row sees fewer than 128 keys, where each weight enters as two bf16 terms
+ * (hi + lo, ~2^-16 relative): a row with few keys would otherwise carry a
+ * weight's bf16 rounding (up to 2^-8 relative) into O almost undiluted.
  *   q     device bf16 [T_q][Hq][D] (rows q0_b..N_b-1 of each sequence, packed in
  *         sequence order); [L][T_q][Hq][D] when layer = -1
  *   o     device bf16, same shape as q (written)
  *   lse   device fp32 [T_q][Hq] natural-log LSE ([L][T_q][Hq] when layer = -1), or NULL
  *   scale softmax scale, typically 1/sqrt(D)
  *   workspace/workspace_bytes: prefill_workspace_bytes (may be NULL when 0)
- * d_table, k_pool, v_pool must hold what segpaged_build wrote for this layer.
- * Workgroups take the tiles heaviest-first from a work counter in d_table's
- * counter line of this layer (layer = -1: the all-layers line); the call leaves
- * it at zero again. Calls for the same layer on one d_table must therefore not
- * overlap; other calls may.
+ * d_table, k_pool, v_pool must hold what segpaged_build wrote for this layer;
+ * d_table must be 8-byte aligned here (EINVAL otherwise).
+ * Workgroups take the tiles heaviest-first from a 64-bit work counter in d_table's
+ * counter line of this layer (layer = -1: the all-layers line), tagged with a
+ * generation the plan hands out per call: whatever an earlier launch left there
+ * (one that never finished included), the call claims the counter for its own
+ * generation and computes every tile; a finished call leaves (generation, 0),
+ * so a captured graph of the call also replays. Calls for the same layer on one
+ * d_table must not overlap; other calls may.
  * A row whose visible set is empty (RETRIEVAL only) gets O = 0, LSE = -inf. */
 SEGPAGED_API int segpaged_prefill(const segpaged_plan* plan, int32_t layer, const void* q,
                                   int32_t* d_table, const void* k_pool,
@@ -294,7 +303,8 @@ SEGPAGED_API int segpaged_import_pages(const segpaged_plan* plan, int32_t layer,
  * each sequence attends to every key it can see. Work items are (unit, key
  * range) slices; each writes fp32 partials (running max, normaliser, unnormalised
  * output) for the G query heads of its unit into `workspace`, and a combine pass
- * merges them with the log-sum-exp rule into O and LSE.
+ * merges them with the log-sum-exp rule into O and LSE. The softmax weights enter
+ * the P.V products as two bf16 terms each (hi + lo, ~2^-16 relative).
  *   q     device bf16 [B][Hq][D] ([L][B][Hq][D] when layer = -1)
  *   o     device bf16, same shape (written)
  *   lse   device fp32 [B][Hq] ([L][B][Hq]), or NULL

@@ -60,6 +60,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// the two bf16 of a packed word as fp32 (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __builtin_bit_cast(float, w & 0xFFFF0000u);
+}
+// Precise softmax weights: p ~ hi + lo with both terms bf16 (hi = p rounded to
+// nearest even, lo = the remainder rounded), so a product with V that takes both
+// carries p to ~2^-16 relative instead of bf16's 2^-8.
+// Eight weights p[0..7] as packed hi and lo words (element order as pack_bf16x2).
+__device__ __forceinline__ void split_bf16x8(const float* p, u32x4& hi, u32x4& lo) {
+  hi.x = pack_bf16x2(p[0], p[1]);
+  hi.y = pack_bf16x2(p[2], p[3]);
+  hi.z = pack_bf16x2(p[4], p[5]);
+  hi.w = pack_bf16x2(p[6], p[7]);
+  lo.x = pack_bf16x2(p[0] - bf16_lo(hi.x), p[1] - bf16_hi(hi.x));
+  lo.y = pack_bf16x2(p[2] - bf16_lo(hi.y), p[3] - bf16_hi(hi.y));
+  lo.z = pack_bf16x2(p[4] - bf16_lo(hi.z), p[5] - bf16_hi(hi.z));
+  lo.w = pack_bf16x2(p[6] - bf16_lo(hi.w), p[7] - bf16_hi(hi.w));
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
@@ -336,16 +356,17 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
       }
     lsum = lsum * alpha + ps;
     m = m_new;
-    u32x4 pw;
-    pw.x = pack_bf16x2(p[0], p[1]);
-    pw.y = pack_bf16x2(p[2], p[3]);
-    pw.z = pack_bf16x2(p[4], p[5]);
-    pw.w = pack_bf16x2(p[6], p[7]);
-    const bf16x8 pf = as_bf16x8(pw);
+    // the weights as hi + lo bf16 terms, both multiplied into O: O then carries each
+    // weight to ~2^-16 relative, as the fp32 normaliser does (the matrix cores
+    // have time to spare here: the kernel waits on HBM)
+    u32x4 ph, pl;
+    split_bf16x8(p, ph, pl);
+    const bf16x8 pfh = as_bf16x8(ph), pfl = as_bf16x8(pl);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       acc[dt] *= alpha;
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[dt]), pf, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[dt]), pfh, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[dt]), pfl, acc[dt], 0, 0, 0);
     }
   };
 
@@ -616,10 +637,36 @@ __device__ __forceinline__ void segment_runs(int kind, int32_t pos0, int32_t len
   }
 }
 
+// Prefill work counter: one 64-bit word, (launch generation << 32) | next item.
+// Every workgroup fetches items until it gets one past the list, so a launch makes
+// exactly items + workgroups fetches; the last fetch sets the word to (gen, 0),
+// ready for a launch of the same generation (a replayed graph). A word left by a
+// launch of another generation (in any state) is claimed by one workgroup's
+// compare-and-swap, which takes item 0; the other workgroups then count on.
+__device__ __forceinline__ uint32_t prefill_fetch(unsigned long long* ctr, uint32_t gen,
+                                                  uint32_t last) {
+  const uint32_t v = (uint32_t)atomicAdd(ctr, 1ull);
+  if (v == last) atomicExch(ctr, (unsigned long long)gen << 32);
+  return v;
+}
+__device__ __forceinline__ uint32_t prefill_claim(unsigned long long* ctr, uint32_t gen,
+                                                  uint32_t last) {
+  unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // two rounds suffice unless launches on one counter overlap (not allowed)
+  for (int round = 0; round < 64; ++round) {
+    if ((uint32_t)(old >> 32) == gen) return prefill_fetch(ctr, gen, last);
+    const unsigned long long prev = atomicCAS(ctr, old, ((unsigned long long)gen << 32) | 1ull);
+    if (prev == old) return 0;
+    old = prev;
+  }
+  return 0x7FFFFFFFu;  // past any list: this workgroup takes no item
+}
+
 template <int D, bool SMALLP>
 __global__ __launch_bounds__(512) void prefill_kernel(
     const int32_t* __restrict__ tab, int32_t off_seqs, int32_t off_units, int32_t off_pages,
-    int32_t off_retr, int32_t off_pre, int32_t item_b, int32_t item_e, int32_t* __restrict__ ctr,
+    int32_t off_retr, int32_t off_pre, int32_t item_b, int32_t item_e,
+    unsigned long long* __restrict__ ctr, uint32_t gen,
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, float* __restrict__ lse,
     int64_t q_layer_stride, int64_t lse_layer_stride, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vp, int32_t G, int32_t Hq, int32_t P, int32_t log2P, float c) {
@@ -683,22 +730,27 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     l_run = 0.f;                                                                              \
   } while (0)
 
-  // Persistent workgroups take items of the heaviest-first list from a counter
-  // (ctr[0]), so faster compute units take more: the next item is fetched while
-  // the current one runs. ctr[1] counts finished workgroups; the last one resets
-  // both for the next launch.
-  if (tid == 0) sItem[0] = atomicAdd(&ctr[0], 1);
+  // Persistent workgroups take items of the heaviest-first list from the work
+  // counter, so faster compute units take more: the next item is fetched while
+  // the current one runs.
+  const uint32_t nitems = (uint32_t)(item_e - item_b);
+  const uint32_t last_fetch = nitems + gridDim.x - 1;
+  if (tid == 0) sItem[0] = (int32_t)prefill_claim(ctr, gen, last_fetch);
   __syncthreads();
   for (int32_t round = 0;; ++round) {
-  const int32_t it = item_b + __builtin_amdgcn_readfirstlane(sItem[round & 1]);
-  if (it >= item_e) break;
+  const uint32_t it_idx = (uint32_t)__builtin_amdgcn_readfirstlane(sItem[round & 1]);
+  if (it_idx >= nitems) break;
+  const int32_t it = item_b + (int32_t)it_idx;
   int32_t it_next = 0;  // the item after this one (wave 0, lane 0)
   // tile metadata through the constant address space: scalar loads (the table
   // is not written while a kernel runs)
   typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
   const cint_ptr ctab = (cint_ptr)tab;
   const int32_t u = ctab[off_pre + kPreItemInts * it];
-  const int32_t r0 = ctab[off_pre + kPreItemInts * it + 1];
+  const int32_t r0_flag = ctab[off_pre + kPreItemInts * it + 1];
+  // tiles whose rows see few keys: weights carried as hi + lo bf16 terms
+  const bool precise = r0_flag < 0;
+  const int32_t r0 = r0_flag & 0x7FFFFFFF;
   const cint_ptr ur = ctab + off_units + kUnitInts * u;
   const int32_t kind = ur[U_KIND], b = ur[U_B], l = ur[U_L], h = ur[U_H], N = ur[U_N];
   const int32_t q0 = ur[U_Q0], sink = ur[U_SINK], win = ur[U_WIN], nseg = ur[U_NSEG];
@@ -907,6 +959,21 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     }                                                                                         \
   } while (0)
 
+  // the same with the weights as hi + lo bf16 terms (PF, PL), whose products with V
+  // carry them to ~2^-16 relative, like the fp32 normaliser l_run
+#define SEGPAGED_EXP_PRECISE(SC, PF, PL)                                                      \
+  do {                                                                                        \
+    float p_[16];                                                                             \
+    _Pragma("unroll") for (int i = 0; i < 16; ++i) p_[i] = fast_exp2(fmaf(SC[i], c, neg_m));  \
+    _Pragma("unroll") for (int i = 0; i < 16; ++i) l_run += p_[i];                            \
+    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                        \
+      u32x4 h_, l_;                                                                           \
+      split_bf16x8(&p_[8 * kk], h_, l_);                                                      \
+      PF[kk] = as_bf16x8(h_);                                                                 \
+      PL[kk] = as_bf16x8(l_);                                                                 \
+    }                                                                                         \
+  } while (0)
+
   // Reference of rows that have none yet (scaled log2 units): the max of the
   // first block with a visible key; afterwards no max is taken. Scores far above
   // the reference show up as a row sum above 2^64 at the end of the tile.
@@ -921,8 +988,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     }                                                                                         \
   } while (0)
 
-  // softmax with per-block rescaling (tiles that overflowed)
-#define SEGPAGED_SOFTMAX_SAFE(BLK, SC, PF)                                                    \
+  // softmax with per-block rescaling and precise weights (tiles whose rows see few
+  // keys, and tiles that overflowed)
+#define SEGPAGED_SOFTMAX_SAFE(BLK, SC, PF, PL)                                                \
   do {                                                                                        \
     SEGPAGED_MASK_BLOCK(BLK, SC);                                                             \
     float mx_ = SC[0];                                                                        \
@@ -937,7 +1005,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       _Pragma("unroll") for (int md = 0; md < MD; ++md) oacc[md] *= alpha;                    \
       neg_m = m_run == -INFINITY ? 0.f : -m_run;                                              \
     }                                                                                         \
-    SEGPAGED_EXP(SC, PF);                                                                     \
+    SEGPAGED_EXP_PRECISE(SC, PF, PL);                                                         \
   } while (0)
 
   // End of a phase: this wave's share of the block the next phase may read has
@@ -1072,7 +1140,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     // the previous tile's O while this tile's Q and first blocks are in flight
     SEGPAGED_EPILOGUE_PREV();
     // the next item; its return is waited for with the blocks below
-    if (tid == 0) it_next = atomicAdd(&ctr[0], 1);
+    if (tid == 0) it_next = (int32_t)prefill_fetch(ctr, gen, last_fetch);
     // Q and blocks 0 and 1 landed: vector loads complete in issue order and the
     // O stores can only lower the count
     WAIT_VM_LGKM0((NBUF - 3) * PER_BLOCK);
@@ -1098,9 +1166,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     // Waves 4-7 run one phase behind waves 0-3 (an idle first phase); waves 0-3
     // idle in the last. After phase t every wave has block t/2 + 2 (so at most
     // NBUF - 4 blocks of its own in flight).
+    // (a precise tile only runs the prologue, for the previous tile's O and the
+    // next item, and leaves its blocks to the loop further below)
     const bool late = wave >= 4;
+    const int32_t nfast = precise ? 0 : nblocks;
     if (late) SEGPAGED_PHASE_END();
-    for (int32_t j = 0; j < nblocks; ++j) {
+    for (int32_t j = 0; j < nfast; ++j) {
       // ---- MFMA phase (its operands were read before the barrier; waiting for
       // them here keeps the scalar loads below from being waited on mid-phase)
       __builtin_amdgcn_s_setprio(1);
@@ -1168,7 +1239,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       if (__builtin_amdgcn_ballot_w64(!(l_tot <= 0x1p64f))) sOverflow = 1;
     }
     __syncthreads();
-    if (sOverflow) {  // uniform
+    if (precise || sOverflow) {  // uniform
+      bf16x8 plo[2];
 #pragma unroll
       for (int md = 0; md < MD; ++md)
 #pragma unroll
@@ -1187,8 +1259,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(
         SEGPAGED_LOAD_K((j + 1) % NBUF, kf);
         SEGPAGED_LOAD_V(j % NBUF, vf);
         SEGPAGED_QK(kf, sn);
-        SEGPAGED_SOFTMAX_SAFE(j, s, pf);
+        SEGPAGED_SOFTMAX_SAFE(j, s, pf, plo);
         SEGPAGED_PV(vf, pf);
+        SEGPAGED_PV(vf, plo);
         s = sn;
         // block j + 2 landed and block j's buffer free before it is refilled
         WAIT_VM_LGKM0((NBUF - 4) * PER_BLOCK);
@@ -1199,7 +1272,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     }
   } else {
     SEGPAGED_EPILOGUE_PREV();
-    if (tid == 0) it_next = atomicAdd(&ctr[0], 1);
+    if (tid == 0) it_next = (int32_t)prefill_fetch(ctr, gen, last_fetch);
   }
 #undef SEGPAGED_PHASE_END
 #undef SEGPAGED_BLOCK_SOURCES
@@ -1228,10 +1301,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   }  // tile loop
   SEGPAGED_EPILOGUE_PREV();
 #undef SEGPAGED_EPILOGUE_PREV
-  if (tid == 0 && atomicAdd(&ctr[1], 1) == (int32_t)gridDim.x - 1) {
-    atomicExch(&ctr[0], 0);
-    atomicExch(&ctr[1], 0);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1262,6 +1331,7 @@ __global__ __launch_bounds__(256) void page_copy_kernel(
 // ---------------------------------------------------------------------------
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+inline bool aligned8(const void* p) { return ((uintptr_t)p & 7u) == 0; }
 
 // Compute units of the current device (cached per device id; 0 on error).
 int device_cus() {
@@ -1330,7 +1400,10 @@ int upload_layer_table(const segpaged_plan* pl, int32_t layer, int32_t* d_table,
   if ((rc = upload(pl, d_table, pl->off_pre + kPreItemInts * sp.pre_b,
                    kPreItemInts * (sp.pre_e - sp.pre_b), st)))
     return rc;
-  // zeroed prefill work counters of this layer and of all-layer calls
+  // the padding before the counter lines, then the zeroed prefill work counters of
+  // this layer and of all-layer calls
+  const int64_t pad_b = pl->off_pre + kPreItemInts * pl->pre_cap;
+  if ((rc = upload(pl, d_table, pad_b, pl->off_ctr - pad_b, st))) return rc;
   if ((rc = upload(pl, d_table, pl->off_ctr + kCtrInts * layer, kCtrInts, st))) return rc;
   return upload(pl, d_table, pl->off_ctr + kCtrInts * pl->L, kCtrInts, st);
 }
@@ -1477,7 +1550,7 @@ SEGPAGED_API int segpaged_prefill(const segpaged_plan* pl, int32_t layer, const 
   (void)workspace_bytes;
   if (!pl || !q || !d_table || !pools_ok(pl, k_pool, v_pool) || !o) return SEGPAGED_EINVAL;
   if (!aligned16(q) || !aligned16(o) || !aligned16(k_pool) || !aligned16(v_pool) ||
-      !aligned4(d_table) || (lse && !aligned4(lse)))
+      !aligned8(d_table) || (lse && !aligned4(lse)))
     return SEGPAGED_EINVAL;
   if (!(scale > 0.f) || !std::isfinite(scale)) return SEGPAGED_EINVAL;
   if (layer < -1 || layer >= pl->L) return SEGPAGED_ESTATE;
@@ -1493,7 +1566,12 @@ SEGPAGED_API int segpaged_prefill(const segpaged_plan* pl, int32_t layer, const 
   const int cus = device_cus();
   if (cus <= 0) return SEGPAGED_EHIP;
   const dim3 grid((unsigned)std::min<int64_t>(nitems, cus)), block(512);
-  int32_t* ctr = d_table + pl->off_ctr + kCtrInts * (layer < 0 ? pl->L : layer);
+  // the work counter of this call's line and a generation no earlier launch on it
+  // used (0 is the uploaded state)
+  const int32_t line = layer < 0 ? pl->L : layer;
+  auto* ctr = reinterpret_cast<unsigned long long*>(d_table + pl->off_ctr + kCtrInts * line);
+  uint32_t gen = pl->pre_gen[line].fetch_add(1) + 1;
+  if (gen == 0) gen = pl->pre_gen[line].fetch_add(1) + 1;
   auto* qq = (const uint16_t*)q;
   auto* oo = (uint16_t*)o;
   auto* kpp = (const uint16_t*)k_pool;
@@ -1502,7 +1580,8 @@ SEGPAGED_API int segpaged_prefill(const segpaged_plan* pl, int32_t layer, const 
   hipLaunchKernelGGL((prefill_kernel<DD, SP>), grid, block, 0, st, d_table,                     \
                      (int32_t)pl->off_seqs, (int32_t)pl->off_units, (int32_t)pl->off_pages,     \
                      (int32_t)pl->off_retr, (int32_t)pl->off_pre, (int32_t)sp.pre_b,            \
-                     (int32_t)sp.pre_e, ctr, qq, oo, lse, qstride, lstride, kpp, vpp, pl->G,     \
+                     (int32_t)sp.pre_e, ctr, gen, qq, oo, lse, qstride, lstride, kpp, vpp,      \
+                     pl->G,                                                                      \
                      pl->Hq,                                                                     \
                      pl->P, pl->log2P, c)
   const bool small_pages = pl->P < kBlockN;  // a 32-key block spans two pages

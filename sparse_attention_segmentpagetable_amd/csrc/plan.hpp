@@ -2,7 +2,9 @@
 // Not part of the public ABI (include/segpaged.h is).
 #pragma once
 
+#include <atomic>
 #include <cstdint>
+#include <memory>
 #include <vector>
 
 #include "segpaged.h"
@@ -24,12 +26,17 @@ enum UnitField {
 
 // Work lists that follow the table in the device image.
 constexpr int kDecItemInts = 4;   // unit, slot_lo, slot_hi, 0
-constexpr int kPreItemInts = 2;   // unit, first query position of the tile
+constexpr int kPreItemInts = 2;   // unit, first query position of the tile | kPrecise
+// Prefill tiles whose first row sees fewer keys than this take the precise path
+// (softmax weights as a sum of two bf16 terms); bit 31 of the item's row marks them.
+constexpr int kPreciseKeys = 128;
+constexpr int32_t kPrecise = (int32_t)0x80000000u;
 constexpr int kPrefillRows = 256; // query rows per prefill tile: G heads x (256 / G) positions
 constexpr int kBlockN = 32;       // keys per prefill block
 constexpr int kMaxGroup = 16;     // Q heads per KV head the decode kernel supports
 constexpr int kSelChunk = 2048;   // keys per workgroup of the top-p masses and first radix pass
-constexpr int kCtrInts = 16;      // prefill work counter line per layer (+1 for all layers)
+constexpr int kCtrInts = 16;      // prefill work counter line per layer (+1 for all layers);
+                                  // its first 8 bytes: (launch generation << 32) | next item
 constexpr int kDecMaxPartsLog2 = 4;     // a decode item is dealt to at most 16 waves
 constexpr int64_t kDecFillWaves = 4096; // decode waves a launch aims for (16 per compute unit)
 
@@ -64,4 +71,6 @@ struct segpaged_plan {
   int64_t off_app = 0;                       // append list: row offsets [B+1], first positions [B]
   bool app_upload = false;                   // image changed since the last segpaged_append
   std::vector<uint8_t> pages_dirty;          // per layer: a page list rotated
+  // prefill launch generation per work counter line (L + 1 lines), see segpaged_prefill
+  std::unique_ptr<std::atomic<uint32_t>[]> pre_gen;
 };

@@ -104,6 +104,14 @@ int decode_ranges(int kind, int64_t sink, int64_t window, int64_t n, const Seg* 
   return cnt;
 }
 
+// Keys query row i of a unit sees (the fewest of a tile's rows: its first).
+int64_t row_keys(int kind, int64_t sink, int64_t window, int64_t i, const int32_t* retr,
+                 int64_t retr_len) {
+  if (kind == SEGPAGED_GLOBAL) return i + 1;
+  if (kind == SEGPAGED_LOCAL) return std::min(i + 1, sink + window);
+  return std::upper_bound(retr, retr + retr_len, (int32_t)i) - retr;
+}
+
 // KV blocks a prefill tile visits (cost model for heaviest-first ordering).
 int64_t tile_cost(int kind, int64_t sink, int64_t window, int64_t r0, int64_t r1,
                   const Seg* segs, int nseg, const int32_t* retr) {
@@ -171,7 +179,7 @@ void make_work_lists(const segpaged_plan* pl, WorkLists& wl) {
     lr.dec_b = wl.n_dec();
     lr.pre_b = wl.n_pre();
     lr.max_unit_items = 0;
-    struct PreTile { int64_t cost, unit, r0; };
+    struct PreTile { int64_t cost, unit, r0; bool precise; };
     std::vector<PreTile> tiles;
     for (int64_t u = l * B * Hkv; u < (l + 1) * B * Hkv; ++u) {
       const int32_t* r = t + pl->off_units + kUnitInts * u;
@@ -227,14 +235,17 @@ void make_work_lists(const segpaged_plan* pl, WorkLists& wl) {
       // prefill tiles
       for (int64_t r0 = q0; r0 < n; r0 += BQ) {
         const int64_t r1 = std::min(n, r0 + BQ);
-        tiles.push_back({tile_cost(eff, sink, win, r0, r1, sg, ns, rpos), u, r0});
+        // a row with few keys carries the rounding of each softmax weight into O
+        // almost undiluted: such tiles run the precise path
+        const bool precise = row_keys(eff, sink, win, r0, rpos, rl) < kPreciseKeys;
+        tiles.push_back({tile_cost(eff, sink, win, r0, r1, sg, ns, rpos), u, r0, precise});
       }
     }
     std::stable_sort(tiles.begin(), tiles.end(),
                      [](const PreTile& a, const PreTile& b) { return a.cost > b.cost; });
     for (const PreTile& tl : tiles) {
       wl.pre.push_back((int32_t)tl.unit);
-      wl.pre.push_back((int32_t)tl.r0);
+      wl.pre.push_back((int32_t)tl.r0 | (tl.precise ? kPrecise : 0));
     }
     lr.dec_e = wl.n_dec();
     lr.pre_e = wl.n_pre();
@@ -514,13 +525,17 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
                      : wl.n_pre();
   pl->off_dec = pl->off_decunits + 2 * U;
   pl->off_pre = pl->off_dec + kDecItemInts * pl->dec_cap;
-  pl->off_ctr = pl->off_pre + kPreItemInts * pl->pre_cap;
+  // counter lines 16-byte aligned in the image (64-bit atomics)
+  pl->off_ctr = (pl->off_pre + kPreItemInts * pl->pre_cap + 3) / 4 * 4;
   pl->off_app = pl->off_ctr + (int64_t)kCtrInts * (L + 1);
   pl->total_ints = pl->off_app + (grow ? 2 * B + 1 : 0);
   if (pl->total_ints > kI32Max) { delete pl; return SEGPAGED_EINVAL; }
   t.resize(pl->total_ints, 0);  // work counters and append list start at zero
   store_work_lists(pl, wl);
   pl->pages_dirty.assign(L, 0);
+  pl->pre_gen.reset(new (std::nothrow) std::atomic<uint32_t>[L + 1]);
+  if (!pl->pre_gen) { delete pl; return SEGPAGED_ENOSPACE; }
+  for (int64_t i = 0; i <= L; ++i) pl->pre_gen[i].store(0);
   *plan_out = pl;
   if (sizes) segpaged_plan_sizes(pl, sizes);
   return SEGPAGED_OK;

@@ -123,6 +123,7 @@ class Plan:
         self.num_seqs, self.num_layers = B, L
         self.num_q_heads, self.num_kv_heads = spec.num_q_heads, Hkv
         self.head_dim, self.page_size = spec.head_dim, spec.page_size
+        self.append_capacity = append_capacity
         keep = {}
         keep["seq_len"] = _arr32(spec.seq_len)
         keep["q0"] = _arr32(spec.first_query_pos)

@@ -10,7 +10,7 @@ import torch
 import workloads as W
 from oracle import attention as OA
 from oracle import layout as OL
-from tests.gpu_util import lse_parity, parity, to_bits, to_dev, to_f64
+from tests.gpu_util import assert_image_equal, counter_lines, lse_parity, parity, to_bits, to_dev, to_f64
 
 sp = pytest.importorskip("sparse_attention_segmentpagetable_amd")
 pytestmark = pytest.mark.gpu
@@ -91,7 +91,7 @@ def test_build_table_and_pool_bit_exact(name, mk):
         assert np.array_equal(kp[written], kp_ref[written]), (name, layer)
         assert np.array_equal(vp[written], vp_ref[written]), (name, layer)
     dev_table = bufs["table"].cpu().numpy()
-    assert np.array_equal(dev_table, plan.table_host())
+    assert_image_equal(dev_table, plan)
     assert np.array_equal(dev_table[:plan.sizes.table_len], OL.table(spec))
 
 
@@ -418,3 +418,41 @@ def test_decode_item_parts(ps, hd):
         lse_parity(lse.cpu().numpy(), ref_lse, f"decode parts L{l}")
         parity(to_f64(o_all[l]), ref, f"decode one wave per item L{l}")
         assert np.max(np.abs(to_f64(o) - to_f64(o_all[l]))) <= 2 ** -7  # fp32 merge order only
+
+
+def test_prefill_work_counter_left_raised():
+    """A work counter that an earlier launch left raised (one that never reached its
+    end, or a launch of another generation) skips no tile: each call claims the
+    counter line with a generation of its own, and leaves (generation, 0)."""
+    spec = _long_mixed("prefill")
+    plan = sp.Plan(spec)
+    bufs = plan.allocate(DEV)
+    kb, vb = W.kv_bits(spec, 0)
+    qb = W.q_bits(spec, 0)
+    sp.build(plan, 0, to_dev(kb), to_dev(vb), bufs["table"], bufs["k_pool"], bufs["v_pool"])
+    ref, ref_lse = OA.attention(spec, 0, qb, kb, vb)
+    q = to_dev(qb)
+    # no growth capacity: the L + 1 counter lines of 16 ints end the image
+    off_ctr = counter_lines(plan)[0]
+    table = bufs["table"]
+    gens = []
+    # (next item, generation) words as a stalled or foreign launch could leave them
+    for lo, hi in [(0, 0), (5, 0), (123456, 7), (0x7FFFFFFF, 1), (3, 0x7FFFFFFF), (0, 0)]:
+        table[off_ctr:off_ctr + 2] = torch.tensor([lo, hi], dtype=torch.int32, device=DEV)
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device=DEV)
+        sp.prefill(plan, 0, q, table, bufs["k_pool"], bufs["v_pool"], 1 / np.sqrt(128), o, lse)
+        torch.cuda.synchronize()
+        parity(to_f64(o), ref, f"prefill after counter ({lo}, {hi})")
+        lse_parity(lse.cpu().numpy(), ref_lse, f"prefill after counter ({lo}, {hi})")
+        word = table[off_ctr:off_ctr + 2].cpu().numpy()
+        assert word[0] == 0 and word[1] not in (0, hi), word
+        gens.append(int(word[1]))
+    # back to back, no reset in between: a new generation each call
+    for _ in range(3):
+        o = torch.full_like(q, float("nan"))
+        sp.prefill(plan, 0, q, table, bufs["k_pool"], bufs["v_pool"], 1 / np.sqrt(128), o)
+        torch.cuda.synchronize()
+        parity(to_f64(o), ref, "prefill back to back")
+        gens.append(int(table[off_ctr + 1].item()))
+    assert len(set(gens)) == len(gens)

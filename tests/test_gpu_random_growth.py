@@ -11,7 +11,7 @@ import torch
 
 import workloads as W
 from oracle import attention as OA
-from tests.gpu_util import lse_parity, parity, to_dev, to_f64
+from tests.gpu_util import assert_image_equal, lse_parity, parity, to_dev, to_f64
 
 sp = pytest.importorskip("sparse_attention_segmentpagetable_amd")
 pytestmark = pytest.mark.gpu
@@ -128,4 +128,4 @@ def test_random_growth(seed):
                 of, lf = to_f64(od), lsed.cpu().numpy()
                 parity(of[rows], ref, f"seed {seed} step {step} decode L{l} n={n}")
                 lse_parity(lf[rows], ref_lse, f"seed {seed} step {step} decode L{l}")
-    assert np.array_equal(bufs["table"].cpu().numpy(), plan.table_host())
+    assert_image_equal(bufs["table"].cpu().numpy(), plan)

@@ -130,10 +130,17 @@ def test_prefill_items_tile_every_row_once(spec):
     bq = 256 // G
     got = {}
     for u, r0 in pre:
-        got.setdefault(int(u), []).append(int(r0))
+        got.setdefault(int(u), []).append(int(r0) & 0x7FFFFFFF)
+    precise = {(int(u), int(r0) & 0x7FFFFFFF): int(r0) < 0 for u, r0 in pre}
     for (u, b, l, h) in OL.units(spec):
         n, q0 = spec.seq_len[b], spec.first_query_pos[b]
         assert sorted(got.get(u, [])) == list(range(q0, n, bq))
+        # bit 31 marks the tiles whose first row sees fewer than 128 keys
+        kind, s, w = spec.head_class(l, h)
+        r = spec.retrieval.get((b, l, h))
+        for r0 in range(q0, n, bq):
+            keys = int(OA.visibility_mask(kind, s, w, r, np.array([r0]), n).sum())
+            assert precise[(u, r0)] == (keys < 128), (u, r0, keys)
     assert len(pre) == plan.sizes.prefill_items
 
 
@@ -289,3 +296,21 @@ def test_decode_without_items_returns_a_status():
     rc = lib.segpaged_decode(plan.handle, 0, fake, fake, None, None, f32(0.1), fake, None,
                              None, 0, None)
     assert rc in (0, -4), rc
+
+
+@pytest.mark.parametrize("spec", list(_specs()), ids=lambda s: f"{s.name}")
+@pytest.mark.parametrize("cap", [0, 7])
+def test_counter_lines_aligned_and_zero(spec, cap):
+    """The L + 1 prefill work-counter lines (16 ints each, the first 8 bytes a 64-bit
+    counter) start 16-byte aligned in the image and are uploaded as zeros: the state
+    a prefill call's generation claim starts from."""
+    if cap and any(n - q0 > 1 for n, q0 in zip(spec.seq_len, spec.first_query_pos)):
+        spec = W.decode_form(spec)
+    plan = sp.Plan(spec, append_capacity=cap)
+    t = plan.table_host()
+    tail = 2 * spec.num_seqs + 1 if cap else 0
+    c1 = len(t) - tail
+    c0 = c1 - 16 * (spec.num_layers + 1)
+    assert c0 % 4 == 0 and np.all(t[c0:c1] == 0)
+    z = plan.sizes
+    assert c0 >= z.table_len + 2 * z.num_units + 4 * z.decode_items + 2 * z.prefill_items
