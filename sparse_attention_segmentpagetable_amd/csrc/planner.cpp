@@ -164,7 +164,7 @@ struct WorkLists {
   int64_t n_pre() const { return (int64_t)pre.size() / kPreItemInts; }
 };
 
-void make_work_lists(const segpaged_plan* pl, WorkLists& wl) {
+void make_work_lists(const segpaged_plan* pl, const int32_t* unit_recs, WorkLists& wl) {
   const int32_t* t = pl->buf.data();
   const int64_t B = pl->B, L = pl->L, Hkv = pl->Hkv, P = pl->P, U = pl->num_units;
   const int64_t split = pl->split, BQ = kPrefillRows / pl->G;
@@ -182,7 +182,7 @@ void make_work_lists(const segpaged_plan* pl, WorkLists& wl) {
     struct PreTile { int64_t cost, unit, r0; bool precise; };
     std::vector<PreTile> tiles;
     for (int64_t u = l * B * Hkv; u < (l + 1) * B * Hkv; ++u) {
-      const int32_t* r = t + pl->off_units + kUnitInts * u;
+      const int32_t* r = unit_recs + kUnitInts * u;
       const int eff = r[U_KIND];
       const int64_t n = r[U_N], q0 = r[U_Q0], sink = r[U_SINK], win = r[U_WIN];
       const int ns = r[U_NSEG];
@@ -519,7 +519,7 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
   // ---- work lists after the table: decode units, decode items, prefill items,
   // then the prefill work counters (and, in append mode, the append list)
   WorkLists wl;
-  make_work_lists(pl, wl);
+  make_work_lists(pl, t.data() + pl->off_units, wl);
   pl->dec_cap = grow ? std::max<int64_t>(dec_cap, wl.n_dec()) : wl.n_dec();
   pl->pre_cap = grow ? std::max<int64_t>(U * ceil_div(chunk, kPrefillRows / G), wl.n_pre())
                      : wl.n_pre();
@@ -589,21 +589,15 @@ SEGPAGED_API int segpaged_plan_append(segpaged_plan* pl, const int32_t* n_new) {
     n_now[b] = n_old[b] + n_new[b];
     q0[b] = std::max(n_now[b] - std::max(n_new[b], 1), 0);
   }
-  write_seq_rows(pl, n_now.data(), q0.data());
-  // append list: where each sequence's new K/V rows start, and their positions
-  int32_t* app = &t[pl->off_app];
-  int64_t row = 0;
-  for (int64_t b = 0; b < B; ++b) {
-    app[b] = (int32_t)row;
-    app[B + 1 + b] = n_old[b];
-    row += n_new[b];
-  }
-  app[B] = (int32_t)row;
-  // unit records; a local head's window keeps positions [p0, N): when that
-  // outgrows its ring of pages, p0 moves on by a page and the page that held
-  // the oldest positions becomes the last one
-  for (int64_t u = 0; u < pl->num_units; ++u) {
-    int32_t* r = &t[pl->off_units + kUnitInts * u];
+  // New unit records and ring moves in temporaries: the plan changes only once the
+  // work lists are known to fit. A local head's window keeps positions [p0, N):
+  // when that outgrows its ring of pages, p0 moves on by a page and the page that
+  // held the oldest positions becomes the last one.
+  const int64_t U = pl->num_units;
+  std::vector<int32_t> units(t.begin() + pl->off_units, t.begin() + pl->off_units + kUnitInts * U);
+  std::vector<int64_t> moves(U, 0);
+  for (int64_t u = 0; u < U; ++u) {
+    int32_t* r = &units[kUnitInts * u];
     const int32_t n = n_now[r[U_B]];
     r[U_N] = n;
     r[U_Q0] = q0[r[U_B]];
@@ -616,12 +610,11 @@ SEGPAGED_API int segpaged_plan_append(segpaged_plan* pl, const int32_t* n_new) {
       const int64_t ring_pages = ceil_div(win + pl->append_chunk - 1, P) + 1;
       int64_t p0 = r[U_S1POS];
       int64_t len1 = std::max<int64_t>(n - p0, 0);
-      int32_t* ring = &t[pl->off_pages + r[U_PAGEOFF] + ceil_div(sink, P)];
-      while (len1 > ring_pages * P) {
-        p0 += P;
-        len1 -= P;
-        std::rotate(ring, ring + 1, ring + ring_pages);
-        pl->pages_dirty[r[U_L]] = 1;
+      if (len1 > ring_pages * P) {
+        const int64_t k = ceil_div(len1 - ring_pages * P, P);
+        p0 += k * P;
+        len1 -= k * P;
+        moves[u] = k;
       }
       r[U_S0LEN] = (int32_t)len0;
       r[U_S1POS] = (int32_t)p0;
@@ -630,8 +623,29 @@ SEGPAGED_API int segpaged_plan_append(segpaged_plan* pl, const int32_t* n_new) {
     }
   }
   WorkLists wl;
-  make_work_lists(pl, wl);
+  make_work_lists(pl, units.data(), wl);
   if (wl.n_dec() > pl->dec_cap || wl.n_pre() > pl->pre_cap) return SEGPAGED_ENOSPACE;
+
+  // commit: sequence rows, the append list (where each sequence's new K/V rows
+  // start, and their positions), unit records, rotated rings, work lists
+  write_seq_rows(pl, n_now.data(), q0.data());
+  int32_t* app = &t[pl->off_app];
+  int64_t row = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    app[b] = (int32_t)row;
+    app[B + 1 + b] = n_old[b];
+    row += n_new[b];
+  }
+  app[B] = (int32_t)row;
+  std::copy(units.begin(), units.end(), t.begin() + pl->off_units);
+  for (int64_t u = 0; u < U; ++u) {
+    if (moves[u] == 0) continue;
+    const int32_t* r = &units[kUnitInts * u];
+    const int64_t ring_pages = ceil_div(r[U_WIN] + pl->append_chunk - 1, P) + 1;
+    int32_t* ring = &t[pl->off_pages + r[U_PAGEOFF] + ceil_div(r[U_SINK], P)];
+    std::rotate(ring, ring + moves[u] % ring_pages, ring + ring_pages);
+    pl->pages_dirty[r[U_L]] = 1;
+  }
   store_work_lists(pl, wl);
   pl->app_upload = true;
   return SEGPAGED_OK;

@@ -14,7 +14,10 @@ from typing import Dict, Optional, Sequence, Tuple
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "lib", "libsegpaged.so")
+# SEGPAGED_LIB names another build of the same C ABI (e.g. the host planner built
+# with address and undefined-behaviour sanitizers); entry points it lacks raise
+# when called
+LIB_PATH = os.environ.get("SEGPAGED_LIB") or os.path.join(_PKG, "lib", "libsegpaged.so")
 
 GLOBAL, LOCAL, RETRIEVAL, DENSE = 0, 1, 2, 3
 STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "ENOSPACE", -4: "EHIP", -5: "ESTATE"}
@@ -70,27 +73,34 @@ def _lib():
             raise RuntimeError(f"{LIB_PATH} is not built (run __graft_entry__.build())")
         lib = ctypes.CDLL(LIB_PATH)
         vp = ctypes.c_void_p
-        lib.segpaged_plan_create.argtypes = [ctypes.POINTER(_Spec), ctypes.POINTER(vp),
-                                             ctypes.POINTER(Sizes)]
-        lib.segpaged_plan_destroy.argtypes = [vp]
-        lib.segpaged_plan_destroy.restype = None
-        lib.segpaged_plan_sizes.argtypes = [vp, ctypes.POINTER(Sizes)]
-        lib.segpaged_plan_table_host.argtypes = [vp, _i32p, ctypes.c_int64]
-        lib.segpaged_plan_stats.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(Stats)]
-        lib.segpaged_build.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
-        lib.segpaged_export_pages.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
-        lib.segpaged_import_pages.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
-        lib.segpaged_plan_append.argtypes = [vp, _i32p]
-        lib.segpaged_select_topp.argtypes = [vp, ctypes.c_int32, vp, vp, vp, ctypes.c_float,
-                                             ctypes.c_float, vp, vp, vp, ctypes.c_int64, vp]
-        lib.segpaged_append.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
-        lib.segpaged_prefill.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_float,
-                                         vp, vp, vp, ctypes.c_int64, vp]
-        lib.segpaged_decode.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_float,
-                                        vp, vp, vp, ctypes.c_int64, vp]
-        lib.segpaged_status_str.argtypes = [ctypes.c_int]
-        lib.segpaged_status_str.restype = ctypes.c_char_p
-        lib.segpaged_version.restype = ctypes.c_int
+        sigs = {
+            "segpaged_plan_create": ([ctypes.POINTER(_Spec), ctypes.POINTER(vp),
+                                      ctypes.POINTER(Sizes)], ctypes.c_int),
+            "segpaged_plan_destroy": ([vp], None),
+            "segpaged_plan_sizes": ([vp, ctypes.POINTER(Sizes)], ctypes.c_int),
+            "segpaged_plan_table_host": ([vp, _i32p, ctypes.c_int64], ctypes.c_int),
+            "segpaged_plan_stats": ([vp, ctypes.c_int32, ctypes.POINTER(Stats)], ctypes.c_int),
+            "segpaged_plan_append": ([vp, _i32p], ctypes.c_int),
+            "segpaged_build": ([vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+            "segpaged_export_pages": ([vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+            "segpaged_import_pages": ([vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+            "segpaged_select_topp": ([vp, ctypes.c_int32, vp, vp, vp, ctypes.c_float,
+                                      ctypes.c_float, vp, vp, vp, ctypes.c_int64, vp],
+                                     ctypes.c_int),
+            "segpaged_append": ([vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+            "segpaged_prefill": ([vp, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_float,
+                                  vp, vp, vp, ctypes.c_int64, vp], ctypes.c_int),
+            "segpaged_decode": ([vp, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_float,
+                                 vp, vp, vp, ctypes.c_int64, vp], ctypes.c_int),
+            "segpaged_status_str": ([ctypes.c_int], ctypes.c_char_p),
+            "segpaged_version": ([], ctypes.c_int),
+        }
+        for name, (args, res) in sigs.items():
+            fn = getattr(lib, name, None)
+            if fn is None:  # a partial build: calling this entry point raises
+                continue
+            fn.argtypes = args
+            fn.restype = res
         _LIB = lib
     return _LIB
 

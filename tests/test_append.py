@@ -182,3 +182,24 @@ def test_sizes_do_not_change_with_appends():
     for k in ("table_int32s", "pool_pages", "pool_bytes", "decode_workspace_bytes", "num_pages"):
         assert z0[k] == z1[k], k
     assert plan.sizes.kv_rows == sum(spec.seq_len) + 77
+
+
+def test_failed_append_leaves_the_plan_unchanged():
+    """An append that fails (a count above the chunk, below zero, or past the planned
+    capacity) changes nothing: image, sizes and work counts are those from before."""
+    spec = _spec()
+    plan = sp.Plan(spec, append_capacity=9, append_chunk=4)
+    plan.append([4, 1, 0, 2])
+    before = (plan.table_host().copy(), plan.sizes.as_dict(), plan.stats(-1))
+    for bad, status in (([5, 0, 0, 0], -1), ([0, -1, 0, 0], -1)):
+        with pytest.raises(sp.SegPagedError) as e:
+            plan.append(bad)
+        assert e.value.status == status
+        assert np.array_equal(plan.table_host(), before[0])
+        assert plan.sizes.as_dict() == before[1] and plan.stats(-1) == before[2]
+    plan.append([4, 4, 4, 4])
+    mid = plan.table_host().copy()
+    with pytest.raises(sp.SegPagedError) as e:
+        plan.append([2, 0, 0, 0])  # 50 + 8 + 2 > 50 + 9
+    assert e.value.status == -3
+    assert np.array_equal(plan.table_host(), mid)

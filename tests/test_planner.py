@@ -13,6 +13,7 @@ import pytest
 import workloads as W
 from oracle import attention as OA
 from oracle import layout as OL
+from tests.random_specs import random_spec
 
 sp = pytest.importorskip("sparse_attention_segmentpagetable_amd")
 
@@ -44,6 +45,8 @@ def _specs():
     yield W.mixed_varlen_decode(seqs=4, num_layers=2, lo=64, hi=5000, window=256)
     s = W.tiny("prefill", n=50)
     yield replace(s, seq_len=[50, 0, 7], first_query_pos=[0, 0, 6])  # empty + ragged sequences
+    for seed in range(100, 132):  # the first half of the GPU tests' random specs
+        yield random_spec(seed)
 
 
 @pytest.mark.parametrize("spec", list(_specs()), ids=lambda s: f"{s.name}")
@@ -304,8 +307,10 @@ def test_counter_lines_aligned_and_zero(spec, cap):
     """The L + 1 prefill work-counter lines (16 ints each, the first 8 bytes a 64-bit
     counter) start 16-byte aligned in the image and are uploaded as zeros: the state
     a prefill call's generation claim starts from."""
-    if cap and any(n - q0 > 1 for n, q0 in zip(spec.seq_len, spec.first_query_pos)):
-        spec = W.decode_form(spec)
+    if cap:  # growth plans reserve more pages than the spec's own free list holds
+        spec = replace(spec, free_list=None, capacity_pages=0)
+        if any(n - q0 > 1 for n, q0 in zip(spec.seq_len, spec.first_query_pos)):
+            spec = W.decode_form(spec)
     plan = sp.Plan(spec, append_capacity=cap)
     t = plan.table_host()
     tail = 2 * spec.num_seqs + 1 if cap else 0
