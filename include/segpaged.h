@@ -320,6 +320,23 @@ SEGPAGED_API int segpaged_decode(const segpaged_plan* plan, int32_t layer, const
                                  float scale, void* o, float* lse, void* workspace,
                                  int64_t workspace_bytes, void* stream);
 
+/* segpaged_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc): the same
+ * computation, with the decode workspace taken from a library-owned device array
+ * of SEGPAGED_NOALLOC_SCRATCH_BYTES, one per GPU, held until the process ends
+ * (looked up on a device at its first call there). Makes no allocation of any kind.
+ * A call whose partials need more than that array returns ENOSPACE before any work
+ * is enqueued (a call over one layer of the Llama-3.3-70B-shaped 8 x 32K decode
+ * needs ~15 MB; the array also decides how many waves share an item, exactly as a
+ * workspace_bytes of that size does). Calls that overlap on one GPU share the array
+ * and race: serialise them (one stream, or events). The array needs no clearing:
+ * every partial a call reads was written by that call. */
+#define SEGPAGED_NOALLOC_SCRATCH_BYTES (32LL << 20)
+SEGPAGED_API int segpaged_decode_noalloc(const segpaged_plan* plan, int32_t layer, const void* q,
+                                         const int32_t* d_table, const void* k_pool,
+                                         const void* v_pool, float scale, void* o, float* lse,
+                                         void* stream);
+
 SEGPAGED_API const char* segpaged_status_str(int status);
 
 /* Library version: major * 10000 + minor * 100 + patch. */

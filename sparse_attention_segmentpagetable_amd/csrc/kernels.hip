@@ -22,6 +22,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "plan.hpp"
 
@@ -1425,6 +1426,28 @@ int launch_page_copy(const segpaged_plan* pl, const Span& sp, const int32_t* d_t
   return check_launch();
 }
 
+// Decode workspace of segpaged_decode_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends. Host code reaches it only through the
+// address hipGetSymbolAddress returns on each device (the array's name is a host
+// stand-in, not a device address).
+__device__ __attribute__((aligned(256))) float scratch[kNoAllocScratchBytes / 4];
+
+// The device address of `scratch` on the current device (looked up once per device).
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SEGPAGED_EHIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SEGPAGED_EHIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return SEGPAGED_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1665,6 +1688,18 @@ SEGPAGED_API int segpaged_decode(const segpaged_plan* pl, int32_t layer, const v
   }
 #undef SEGPAGED_LAUNCH_COMBINE
   return check_launch();
+}
+
+SEGPAGED_API int segpaged_decode_noalloc(const segpaged_plan* pl, int32_t layer, const void* q,
+                                         const int32_t* d_table, const void* k_pool,
+                                         const void* v_pool, float scale, void* o, float* lse,
+                                         void* stream) {
+  if (!pl) return SEGPAGED_EINVAL;
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc) return rc;
+  return segpaged_decode(pl, layer, q, d_table, k_pool, v_pool, scale, o, lse, ws,
+                         kNoAllocScratchBytes, stream);
 }
 
 }  // extern "C"

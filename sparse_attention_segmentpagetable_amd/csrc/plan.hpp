@@ -39,6 +39,7 @@ constexpr int kCtrInts = 16;      // prefill work counter line per layer (+1 for
                                   // its first 8 bytes: (launch generation << 32) | next item
 constexpr int kDecMaxPartsLog2 = 4;     // a decode item is dealt to at most 16 waves
 constexpr int64_t kDecFillWaves = 4096; // decode waves a launch aims for (16 per compute unit)
+constexpr int64_t kNoAllocScratchBytes = SEGPAGED_NOALLOC_SCRATCH_BYTES;  // see segpaged.h
 
 struct LayerRange {
   int64_t unit_b, unit_e;   // units

@@ -92,6 +92,8 @@ def _lib():
                                   vp, vp, vp, ctypes.c_int64, vp], ctypes.c_int),
             "segpaged_decode": ([vp, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_float,
                                  vp, vp, vp, ctypes.c_int64, vp], ctypes.c_int),
+            "segpaged_decode_noalloc": ([vp, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_float,
+                                         vp, vp, vp], ctypes.c_int),
             "segpaged_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "segpaged_version": ([], ctypes.c_int),
         }
@@ -408,3 +410,28 @@ def decode(plan: Plan, layer: int, q, table, k_pool, v_pool, scale: float, o, ls
                                   _ptr(v_pool, "vp", torch.bfloat16), float(scale),
                                   _ptr(o, "o"), _ptr(lse, "lse"), _ptr(workspace, "ws"), wsb,
                                   _stream(stream)), "segpaged_decode")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # SEGPAGED_NOALLOC_SCRATCH_BYTES
+
+
+def decode_noalloc(plan: Plan, layer: int, q, table, k_pool, v_pool, scale: float, o, lse=None,
+                   stream=None):
+    """segpaged_decode_noalloc: segpaged_decode with the workspace in the library's
+    own device array (no allocation); calls on one GPU must not overlap."""
+    import torch
+    nl = plan.num_layers if layer < 0 else 1
+    rows = nl * plan.num_seqs * plan.num_q_heads
+    for t, nm in ((q, "q"), (o, "o")):
+        _ptr(t, nm, torch.bfloat16)
+        _need(t, rows * plan.head_dim, nm)
+    if lse is not None:
+        _ptr(lse, "lse", torch.float32)
+        _need(lse, rows, "lse")
+    _ptr(table, "table", torch.int32)
+    _need(table, plan.sizes.table_int32s, "table")
+    _check(_lib().segpaged_decode_noalloc(plan.handle, layer, _ptr(q, "q"), _ptr(table, "t"),
+                                          _ptr(k_pool, "kp", torch.bfloat16),
+                                          _ptr(v_pool, "vp", torch.bfloat16), float(scale),
+                                          _ptr(o, "o"), _ptr(lse, "lse"), _stream(stream)),
+           "segpaged_decode_noalloc")
