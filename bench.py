@@ -66,6 +66,54 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_decode.json")
 COPY_BYTES = 1 << 30
 
 
+def _to_f64(t):
+    """A device tensor as float64 on the host (bf16 widens exactly)."""
+    return t.double().cpu().numpy()
+
+
+def _cos(a, b):
+    nrm = float(np.linalg.norm(a) * np.linalg.norm(b))
+    return float(np.dot(a.ravel(), b.ravel()) / nrm) if nrm > 0 else float(np.array_equal(a, b))
+
+
+def _acc(got, ref, **extra):
+    """Agreement of two outputs [..., heads, D]: max |difference|, cosine over all
+    elements and the smallest cosine of a single query head (axis -2)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    g2 = np.moveaxis(got, -2, 0).reshape(got.shape[-2], -1)
+    r2 = np.moveaxis(ref, -2, 0).reshape(ref.shape[-2], -1)
+    out = {"max_abs_err": float(np.max(np.abs(got - ref))) if got.size else 0.0,
+           "cos": round(_cos(got, ref), 8),
+           "min_head_cos": round(min(_cos(g2[h], r2[h]) for h in range(len(g2))), 8),
+           "elements": int(got.size)}
+    out.update(extra)
+    return out
+
+
+def _merge_acc(parts):
+    """One record from several _acc records: worst error and smallest cosines."""
+    if not parts:
+        return None
+    return {"max_abs_err": max(p["max_abs_err"] for p in parts),
+            "min_cos": min(p["cos"] for p in parts),
+            "min_head_cos": min(p["min_head_cos"] for p in parts),
+            "elements": sum(p["elements"] for p in parts), "checks": len(parts)}
+
+
+def _kv_tokens(plan, spec, layer=-1):
+    """Keys the cache stores against a dense cache of the same tokens: every layer
+    and KV head keeping all N_b (what the dense-mask path holds)."""
+    st = plan.stats(layer)
+    nl = spec.num_layers if layer < 0 else 1
+    dense = nl * spec.num_kv_heads * sum(spec.seq_len)
+    return {"dense_tokens": int(dense), "stored_tokens": int(st["retained_tokens"]),
+            "stored_frac": round(st["retained_tokens"] / dense, 4),
+            "saving": round(1 - st["retained_tokens"] / dense, 4),
+            "page_slots_frac": round(st["pages"] * spec.page_size / dense, 4),
+            "decode_row_keys_frac": round(st["decode_tokens"] / dense, 4)}
+
+
 def kernels_hash():
     import hashlib
     return hashlib.sha256(open(KERNELS_SRC, "rb").read()).hexdigest()[:16]
@@ -318,6 +366,10 @@ def main():
 
     xfer = page_transfer(torch, sp, dplan, db, dspec, stream, log)
     ceil = measure_ceilings(torch, dev, stream, log)
+    # layer 0 once more, untimed: the output the accuracy checks below compare (the
+    # timed steps leave the last layer's in o_pre)
+    sp.prefill(pplan, 0, qs[0], pb["table"], pb["k_pool"], pb["v_pool"], scale, o_pre, lse_pre)
+    torch.cuda.synchronize()
 
     pre_ms_layer = float(np.mean(dur["prefill"]))
     pre_ms_step = float(np.sum(dur["prefill"])) / args.steps
@@ -361,6 +413,12 @@ def main():
             "algorithmic_flops_per_step": prefill_flops,
             "tflops": round(pre_tflops, 1),
             "build_gbs": round(build_bytes / (bld_ms_step * 1e-3) / 1e9, 1),
+            # the prefill-form cache keeps every key (rows from 0 read it); what the
+            # layout saves here is attention work: visible pairs against causal
+            "kv_tokens": _kv_tokens(pplan, pspec),
+            "attention_pairs_frac_of_causal": round(
+                sum(pspec.group * s["prefill_pairs"] for s in pstats) /
+                (args.prefill_layers * Hq * N * (N + 1) / 2), 4),
         },
         "decode": {
             "value": round(dec_gbs, 1),
@@ -370,6 +428,7 @@ def main():
             "ms_min": round(float(np.min(dec_ms)), 4),
             "reps": args.decode_reps,
             "kv_bytes": decode_bytes,
+            "kv_tokens": _kv_tokens(dplan, dspec),
             "ms_in_steps": [round(x, 4) for x in dur["decode"]],
             "per_layer_launches": {
                 "launches": args.decode_layers,
@@ -410,17 +469,26 @@ def main():
     if not args.no_dense:
         try:
             out["dense_mask"] = dense_mask_baseline(torch, W, pspec, dspec, ks[0], vs[0], qs[0],
-                                                    dev, pre_ms_layer, dec_med, args, log)
+                                                    dev, pre_ms_layer, dec_med, args, log,
+                                                    o_pre, q_dec, o_dec)
         except Exception as e:  # the comparison path is optional context
             out["dense_mask"] = {"error": f"{type(e).__name__}: {e}"[:300]}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(torch, W, pspec, qs[0], ks[0], vs[0], args, log)
+        # the oracle rows timed for the baseline double as the accuracy check of the
+        # timed outputs (prefill: layer 0 rows; decode: the all-layer call's rows)
+        out["cpu_baseline"] = cpu_baseline(torch, W, pspec, qs[0], ks[0], vs[0], args, log,
+                                           o_pre)
+        out["prefill"]["accuracy_vs_oracle"] = out["cpu_baseline"].pop("accuracy")
         out["cpu_baseline"]["decode"] = cpu_baseline_decode(torch, W, dspec, dplan, q_dec, dev,
-                                                            args, log)
+                                                            args, log, o_dec)
+        out["decode"]["accuracy_vs_oracle"] = out["cpu_baseline"]["decode"].pop("accuracy")
     if not args.no_extra:
         del pb, db, qs, ks, vs, o_pre, lse_pre, q_dec, o_dec, lse_dec
         torch.cuda.empty_cache()
-        out.update(extra_configs(torch, W, sp, dev, stream, log))
+        samples = {}
+        out.update(extra_configs(torch, W, sp, dev, stream, log, samples))
+        if not args.no_cpu_baseline:
+            cpu_baseline_extra(W, samples, out, log)
     print(json.dumps(out), flush=True)
 
 
@@ -523,7 +591,20 @@ def measure_ceilings(torch, dev, stream, log):
                       "streaming read)"}
 
 
-def extra_configs(torch, W, sp, dev, stream, log):
+def _bits(t):
+    """bf16 bits of a device tensor as host uint16."""
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _sample(samples, key, spec, layer, b, pos, q_rows, k_seq, v_seq, got):
+    """Keep what the oracle needs to check rows `pos` of sequence b: host bits of
+    their queries and of the sequence's K/V (uint16), and the GPU's output rows."""
+    samples.setdefault(key, []).append((spec, layer, b, np.asarray(pos), q_rows, k_seq, v_seq,
+                                        got))
+
+
+def extra_configs(torch, W, sp, dev, stream, log, samples):
     """The other configurations of the scope table, timed outside the step (not part
     of `value`): the mixed-length decode with retrieval heads (32 sequences of 2K-128K
     tokens, 48 layers, one all-layer call; working set far beyond the caches) and the
@@ -565,6 +646,20 @@ def extra_configs(torch, W, sp, dev, stream, log):
     med, mn = timed(lambda: sp.decode(plan, -1, q, bufs["table"], bufs["k_pool"], bufs["v_pool"],
                                       1.0 / math.sqrt(D), o, lse, workspace=bufs["workspace"]), 10)
     gbs = kv_bytes / (med * 1e-3) / 1e9
+    # oracle check rows: the longest and the shortest sequence, and two seeded ones,
+    # each at a seeded layer (retrieval heads included where the layer has them)
+    rng = np.random.default_rng([spec.seed, 79])
+    kvo = spec.kv_row_offsets()
+    pick = [int(np.argmax(spec.seq_len)), int(np.argmin(spec.seq_len))]
+    pick += [int(x) for x in rng.choice(spec.num_seqs, size=2, replace=False)]
+    for b in pick:
+        l = int(rng.integers(0, L))
+        kd = W.randn_bf16_device((T, Hkv, D), spec.seed, W.TAG_K, l, dev)
+        vd = W.randn_bf16_device((T, Hkv, D), spec.seed, W.TAG_V, l, dev)
+        sl = slice(kvo[b], kvo[b] + spec.seq_len[b])
+        _sample(samples, "decode_mixed", spec, l, b, [spec.seq_len[b] - 1], _bits(q[l, b:b + 1]),
+                _bits(kd[sl]), _bits(vd[sl]), _to_f64(o[l, b:b + 1]))
+        del kd, vd
     res["decode_mixed"] = {
         "workload": (f"{spec.num_seqs} sequences of {min(spec.seq_len)}-{max(spec.seq_len)} tokens, "
                      f"{L} layers x {Hkv} KV heads (12% global, 8% retrieval with 5% index sets, "
@@ -572,6 +667,7 @@ def extra_configs(torch, W, sp, dev, stream, log):
         "value": round(gbs, 1), "unit": "GB/s", "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "ms_median": round(med, 4), "ms_min": round(mn, 4), "kv_bytes": kv_bytes,
         "decode_items": plan.sizes.decode_items,
+        "kv_tokens": _kv_tokens(plan, spec),
     }
     log(f"mixed decode: {med:.3f} ms, {gbs:.0f} GB/s")
     del plan, bufs, q, o, lse
@@ -603,6 +699,20 @@ def extra_configs(torch, W, sp, dev, stream, log):
     dmed, dmn = timed(lambda: sp.decode(dplan, 0, qd, db["table"], db["k_pool"], db["v_pool"],
                                         1.0 / math.sqrt(D), od, workspace=db["workspace"]), 50)
     dbytes = dplan.stats(0)["decode_tokens"] * 2 * D * 2
+    # oracle check rows: per sequence the sink, window and page edges, the last row
+    # and 22 seeded rows of the prefill; every decode row
+    rng = np.random.default_rng([spec.seed, 80])
+    n = spec.seq_len[0]
+    for b in range(spec.num_seqs):
+        pos = sorted(set([0, 3, 4, 63, 64, 1023, 1024, 1027, 1028, n - 1] +
+                         [int(x) for x in rng.choice(n, size=22, replace=False)]))
+        rows = torch.as_tensor([b * n + p for p in pos], device=dev)
+        _sample(samples, "mistral_prefill", spec, 0, b, pos, _bits(q[rows]),
+                _bits(k[b * n:(b + 1) * n]), _bits(v[b * n:(b + 1) * n]), _to_f64(o[rows]))
+        nd, kv0 = dspec.seq_len[b], dspec.kv_row_offsets()[b]
+        kvd = slice(kv0, kv0 + nd)
+        _sample(samples, "mistral_decode", dspec, 0, b, [nd - 1], _bits(qd[b:b + 1]),
+                _bits(kd[kvd]), _bits(vd[kvd]), _to_f64(od[b:b + 1]))
     res["mistral_layer"] = {
         "workload": "4 x 8192 tokens, 32 Q / 8 KV heads, D 128, page 64, KV head 0 global, 1-7 local (sink 4, window 1024)",
         "prefill_tflops": round(flops / (pmed * 1e-3) / 1e12, 1),
@@ -612,17 +722,79 @@ def extra_configs(torch, W, sp, dev, stream, log):
         "build_ms": round(bmed, 4),
         "decode_ms": round(dmed, 4), "decode_kv_bytes": dbytes,
         "decode_gbs_cache_resident": round(dbytes / (dmed * 1e-3) / 1e9, 1),
+        "prefill_kv_tokens": _kv_tokens(plan, spec),
+        "decode_kv_tokens": _kv_tokens(dplan, dspec),
     }
     log(f"mistral layer: prefill {pmed:.3f} ms ({flops / (pmed * 1e-3) / 1e12:.0f} TF/s), "
         f"decode {dmed * 1e3:.1f} us")
     del plan, bufs, k, v, q, o, dplan, db
     torch.cuda.empty_cache()
+    res["tiny"] = tiny_config(torch, W, sp, dev, timed, log, samples)
     res["long_prefill_decode_form_build"] = decode_form_build(torch, W, sp, dev, timed, log)
     res["decode_context_sweep"] = decode_context_sweep(torch, W, sp, dev, timed, log)
     res["decode_loop_append"] = decode_loop_append(torch, W, sp, dev, stream, log)
     res["chunked_prefill"] = chunked_prefill(torch, W, sp, dev, stream, log)
     res["retrieval_selection"] = retrieval_selection(torch, W, sp, dev, timed, log)
     return res
+
+
+def tiny_config(torch, W, sp, dev, timed, log, samples):
+    """The tiny workload (1 layer, 8 Q / 4 KV heads, D 64, page 16, 512 tokens):
+    causal prefill of all rows and the decode step at 513 tokens; launch-bound,
+    timed for context and kept whole for the oracle check."""
+    res = {}
+    for form in ("prefill", "decode"):
+        spec = W.tiny(form)
+        plan = sp.Plan(spec)
+        bufs = plan.allocate(dev)
+        kb, vb = W.kv_bits(spec, 0)
+        qb = W.q_bits(spec, 0)
+        dv = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        sp.build(plan, 0, dv(kb), dv(vb), bufs["table"], bufs["k_pool"], bufs["v_pool"])
+        q = dv(qb)
+        o = torch.empty_like(q)
+        scale = 1.0 / math.sqrt(spec.head_dim)
+        if form == "prefill":
+            fn = lambda: sp.prefill(plan, 0, q, bufs["table"], bufs["k_pool"], bufs["v_pool"],
+                                    scale, o)
+        else:
+            fn = lambda: sp.decode(plan, 0, q, bufs["table"], bufs["k_pool"], bufs["v_pool"],
+                                   scale, o, workspace=bufs["workspace"])
+        med, mn = timed(fn, 50)
+        n = spec.seq_len[0]
+        _sample(samples, f"tiny_{form}", spec, 0, 0, list(range(spec.first_query_pos[0], n)), qb,
+                kb, vb, _to_f64(o))
+        res[form] = {"ms_median": round(med, 4), "ms_min": round(mn, 4),
+                     "kv_tokens": _kv_tokens(plan, spec)}
+        del plan, bufs, q, o
+    log(f"tiny: prefill {res['prefill']['ms_median'] * 1e3:.1f} us, decode "
+        f"{res['decode']['ms_median'] * 1e3:.1f} us")
+    return res
+
+
+def cpu_baseline_extra(W, samples, out, log):
+    """The oracle on the rows kept from the other workloads' timed outputs: the
+    equivalence check of the runtime explainer (cosine, and max |O - O_ref|)
+    against the fp64 definition, per workload."""
+    from oracle import attention as OA
+    where = {"tiny_prefill": ("tiny", "prefill"), "tiny_decode": ("tiny", "decode"),
+             "mistral_prefill": ("mistral_layer", "prefill_accuracy_vs_oracle"),
+             "mistral_decode": ("mistral_layer", "decode_accuracy_vs_oracle"),
+             "decode_mixed": ("decode_mixed", "accuracy_vs_oracle")}
+    for key, rows in samples.items():
+        t0 = time.perf_counter()
+        acc = []
+        for spec, layer, b, pos, qb, kb, vb, got in rows:
+            ref, _ = OA.attention_rows(spec, layer, b, pos, qb, kb, vb)
+            acc.append(_acc(got, ref))
+        rec = dict(_merge_acc(acc), rows=int(sum(len(r[3]) for r in rows)),
+                   oracle_seconds=round(time.perf_counter() - t0, 2))
+        top, field = where[key]
+        if key.startswith("tiny_"):
+            out[top][field]["accuracy_vs_oracle"] = rec
+        else:
+            out[top][field] = rec
+        log(f"oracle check {key}: max|err| {rec['max_abs_err']:.3e} min cos {rec['min_cos']:.8f}")
 
 
 def retrieval_selection(torch, W, sp, dev, timed, log):
@@ -711,12 +883,15 @@ def chunked_prefill(torch, W, sp, dev, stream, log):
         f"append {app_ms / L:.3f} ms/layer, pool {plan.sizes.pool_bytes / 1e6:.0f} MB vs "
         f"{one_shot_pool / 1e6:.0f} MB one-shot")
     pool = plan.sizes.pool_bytes
+    dense_bytes = L * N * Hkv * D * 2
     del plan, bufs, k, v, q, o
     torch.cuda.empty_cache()
     return {"workload": f"long-prefill {N} tokens x {L} layers in {N // chunk} chunks of {chunk}",
             "prefill_ms_per_layer": round(pre_ms / L, 3), "prefill_tflops": round(tf, 1),
             "append_ms_per_layer": round(app_ms / L, 4),
-            "pool_bytes_per_tensor": pool, "one_shot_pool_bytes_per_tensor": one_shot_pool}
+            "pool_bytes_per_tensor": pool, "one_shot_pool_bytes_per_tensor": one_shot_pool,
+            "pool_frac_of_dense_kv": round(pool / dense_bytes, 4),
+            "kv_saving_vs_dense": round(1 - pool / dense_bytes, 4)}
 
 
 def decode_loop_append(torch, W, sp, dev, stream, log):
@@ -799,11 +974,12 @@ def decode_form_build(torch, W, sp, dev, timed, log):
     gbs = 2 * 2 * D * 2 * tok / (ms * 1e-3) / 1e9
     log(f"long-prefill decode-form build: {ms:.3f} ms/layer, {2 * D * 2 * tok / 1e6:.0f} MB of "
         f"K/V kept, {gbs:.0f} GB/s")
+    kvt = _kv_tokens(plan, dspec)
     del plan, bufs, k, v
     torch.cuda.empty_cache()
     return {"workload": f"layers 0-3 of the long-prefill workload ({n} tokens) in decode form",
             "ms_per_layer": round(ms, 4), "kv_bytes_kept_per_layer": int(2 * D * 2 * tok),
-            "gbs_read_plus_write": round(gbs, 1)}
+            "gbs_read_plus_write": round(gbs, 1), "kv_tokens": kvt}
 
 
 def decode_context_sweep(torch, W, sp, dev, timed, log):
@@ -865,12 +1041,25 @@ def decode_context_sweep(torch, W, sp, dev, timed, log):
             "rows": rows}
 
 
-def dense_mask_baseline(torch, W, pspec, dspec, k0, v0, q0, dev, pre_ms_layer, dec_ms, args, log):
+def _sdpa_choice(torch, q, k, v, mask):
+    """The backend torch SDPA picks on its own for these arguments."""
+    try:
+        from torch.nn.attention import SDPBackend
+        return SDPBackend(int(torch._fused_sdp_choice(q, k, v, attn_mask=mask, dropout_p=0.0,
+                                                        is_causal=False))).name
+    except Exception as e:  # private API: report, do not fail
+        return f"unknown ({type(e).__name__})"
+
+
+def dense_mask_baseline(torch, W, pspec, dspec, k0, v0, q0, dev, pre_ms_layer, dec_ms, args, log,
+                        o_pre0, q_dec, o_dec):
     """The pages' comparison path: dense K/V plus a boolean attention mask through
     torch SDPA on the same GPU. The G query heads of a KV head share its mask, so
     they are folded into the query-length axis: SDPA reads each KV head once (no
     K/V repetition). Timed on a slice and scaled linearly: a dense-mask row costs
-    the same at every position."""
+    the same at every position. Its outputs are compared with SegPaged's on the
+    same inputs (o_pre0: layer 0 of the prefill workload; o_dec: the decode
+    workload's all-layer call), the equivalence check of the runtime explainer."""
     from torch.nn.attention import SDPBackend, sdpa_kernel
     import torch.nn.functional as F
     res = {}
@@ -890,9 +1079,10 @@ def dense_mask_baseline(torch, W, pspec, dspec, k0, v0, q0, dev, pre_ms_layer, d
     k = k0.permute(1, 0, 2)[None].contiguous()          # [1, Hkv, N, D]
     v = v0.permute(1, 0, 2)[None].contiguous()
     backend = "EFFICIENT_ATTENTION"
+    default = _sdpa_choice(torch, q, k, v, mask)
     with sdpa_kernel([SDPBackend.EFFICIENT_ATTENTION]):
         for _ in range(2):
-            F.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+            od = F.scaled_dot_product_attention(q, k, v, attn_mask=mask)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -902,10 +1092,29 @@ def dense_mask_baseline(torch, W, pspec, dspec, k0, v0, q0, dev, pre_ms_layer, d
         torch.cuda.synchronize()
     t_slice = e0.elapsed_time(e1) / 3
     t_layer = t_slice * N / R
+    # SDPA rows (KV head, position, head in group) -> [position, Q head, D]
+    od = od[0].view(Hkv, R, G, D).permute(1, 0, 2, 3).reshape(R, Hq, D)
+    agree = _acc(_to_f64(o_pre0[N - R:]), _to_f64(od), rows=f"{N - R}..{N - 1} of layer 0")
+    # the backend SDPA picks unforced, timed on the same slice
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    F.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(3):
+        F.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+    e1.record()
+    torch.cuda.synchronize()
+    t_default = e0.elapsed_time(e1) / 3
     res["prefill"] = {"backend": f"torch SDPA {backend}, bool mask, GQA group folded into rows",
+                      "default_backend": default,
+                      "default_backend_ms_slice": round(t_default, 3),
                       "rows_timed": R, "ms_slice": round(t_slice, 3),
                       "ms_per_layer_extrapolated": round(t_layer, 2),
-                      "speedup_vs_dense_mask": round(t_layer / pre_ms_layer, 2)}
+                      "speedup_vs_dense_mask": round(t_layer / pre_ms_layer, 2),
+                      "segpaged_vs_dense_mask": agree}
+    log(f"dense-mask prefill agreement: cos {agree['cos']:.8f}, max|diff| "
+        f"{agree['max_abs_err']:.3e}; SDPA picks {default} unforced")
+    del od
     del q, k, v, mask
     log(f"dense-mask prefill: {t_layer:.1f} ms/layer (extrapolated) vs {pre_ms_layer:.1f}")
     # the same layer through our own kernel with every head global: causal
@@ -936,11 +1145,15 @@ def dense_mask_baseline(torch, W, pspec, dspec, k0, v0, q0, dev, pre_ms_layer, d
     del gplan, gb, go
     torch.cuda.empty_cache()
     # decode: a few layers of the decode workload on dense K/V [B, Hkv, n, D]
+    # decode: layers 0-3 of the decode workload, the same K/V the pages hold, as
+    # dense [B, Hkv, n, D], and the same queries
     B, n = dspec.num_seqs, args.decode_n
     nl = 4
-    kd = [W.randn_bf16_device((B, Hkv, n, D), dspec.seed, 99, l, dev) for l in range(nl)]
-    vd = [W.randn_bf16_device((B, Hkv, n, D), dspec.seed, 98, l, dev) for l in range(nl)]
-    qd = W.randn_bf16_device((B, Hkv, G, D), dspec.seed, 97, 0, dev)
+    kd = [W.randn_bf16_device((B * n, Hkv, D), dspec.seed, W.TAG_K, l, dev)
+          .view(B, n, Hkv, D).permute(0, 2, 1, 3).contiguous() for l in range(nl)]
+    vd = [W.randn_bf16_device((B * n, Hkv, D), dspec.seed, W.TAG_V, l, dev)
+          .view(B, n, Hkv, D).permute(0, 2, 1, 3).contiguous() for l in range(nl)]
+    qd = [q_dec[l].view(B, Hkv, G, D).contiguous() for l in range(nl)]
     jj = torch.arange(n, device=dev)
     dmasks = []
     for l in range(nl):
@@ -952,30 +1165,44 @@ def dense_mask_baseline(torch, W, pspec, dspec, k0, v0, q0, dev, pre_ms_layer, d
                 m = m & ((jj < s) | (jj > n - 1 - w))
             mm.append(m)
         dmasks.append(torch.stack(mm)[None, :, None, :].expand(B, Hkv, G, n).contiguous())
+    ddefault = _sdpa_choice(torch, qd[0], kd[0], vd[0], dmasks[0])
+    agree = []
     with sdpa_kernel([SDPBackend.EFFICIENT_ATTENTION]):
         for l in range(nl):
-            F.scaled_dot_product_attention(qd, kd[l], vd[l], attn_mask=dmasks[l])
+            od = F.scaled_dot_product_attention(qd[l], kd[l], vd[l], attn_mask=dmasks[l])
+            agree.append(_acc(_to_f64(o_dec[l]), _to_f64(od.reshape(B, Hq, D))))
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for l in range(nl):
-            F.scaled_dot_product_attention(qd, kd[l], vd[l], attn_mask=dmasks[l])
+            F.scaled_dot_product_attention(qd[l], kd[l], vd[l], attn_mask=dmasks[l])
         e1.record()
         torch.cuda.synchronize()
     t_all = e0.elapsed_time(e1) / nl * args.decode_layers
     dense_bytes = 2 * B * Hkv * n * D * 2 * args.decode_layers
     res["decode"] = {"backend": f"torch SDPA {backend}, bool mask, GQA group folded into rows",
+                     "default_backend": ddefault,
                      "layers_timed": nl, "ms_all_layers_extrapolated": round(t_all, 3),
                      "dense_kv_gbs": round(dense_bytes / (t_all * 1e-3) / 1e9, 1),
-                     "speedup_vs_dense_mask": round(t_all / dec_ms, 2)}
+                     "speedup_vs_dense_mask": round(t_all / dec_ms, 2),
+                     "segpaged_vs_dense_mask": dict(_merge_acc(agree), layers="0-3")}
     log(f"dense-mask decode: {t_all:.2f} ms (80 layers, extrapolated) vs {dec_ms:.3f}")
     return res
 
 
-def cpu_baseline(torch, W, pspec, q0, k0, v0, args, log):
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return {d["internal_api"]: d["num_threads"] for d in threadpool_info()}
+    except Exception as e:
+        return f"unknown ({type(e).__name__})"
+
+
+def cpu_baseline(torch, W, pspec, q0, k0, v0, args, log, o_layer0):
     """The oracle as it stands (numpy fp64, dense scores + explicit mask), timed on
     the host cores on a bounded sample: rows of layer 0 at seeded positions, all
-    64 Q heads, against the full 131072-token context."""
+    64 Q heads, against the full 131072-token context. The same oracle rows check
+    the GPU's layer-0 output at those positions (returned under "accuracy")."""
     from oracle import attention as OA
     N = args.prefill_n
     kb = k0.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -984,24 +1211,35 @@ def cpu_baseline(torch, W, pspec, q0, k0, v0, args, log):
     cores = len(os.sched_getaffinity(0))
     done_rows, spent = 0, 0.0
     chunk = 2
+    acc = []
+    # edges first (sink, window and page boundaries, the last row), then seeded rows
+    edges = [0, 3, 4, 63, 64, 8191, 8192, 8195, 8196, N - 1]
     while spent < args.cpu_seconds:
-        pos = np.sort(rng.choice(N, size=chunk, replace=False))
-        qr = q0[torch.as_tensor(pos, device=q0.device)].view(torch.int16).cpu().numpy().view(np.uint16)
+        if done_rows < len(edges):
+            pos = np.array(edges[done_rows:done_rows + chunk])
+        else:
+            pos = np.sort(rng.choice(N, size=chunk, replace=False))
+        idx = torch.as_tensor(pos, device=q0.device)
+        qr = q0[idx].view(torch.int16).cpu().numpy().view(np.uint16)
         t0 = time.perf_counter()
-        OA.attention_rows(pspec, 0, 0, pos, qr, kb, vb)
+        ref, _ = OA.attention_rows(pspec, 0, 0, pos, qr, kb, vb)
         spent += time.perf_counter() - t0
         done_rows += chunk
+        acc.append(_acc(_to_f64(o_layer0[idx]), ref))
     head_rows_per_s = done_rows * pspec.num_q_heads / spent
     tok_s = head_rows_per_s / (pspec.num_q_heads * args.prefill_layers)
     log(f"oracle: {done_rows} rows x 64 heads in {spent:.1f} s -> {tok_s:.4f} tok/s")
-    return {"value": round(tok_s, 5), "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": (f"{done_rows} query rows of layer 0 at seeded positions, all "
-                       f"{pspec.num_q_heads} Q heads, full {N}-token context; scaled to "
-                       f"{args.prefill_layers} layers x {pspec.num_q_heads} heads per token"),
-            "seconds": round(spent, 2)}
+    return {"value": round(tok_s, 5), "unit": "tok/s", "cores": cores,
+            "blas_threads": _blas_threads(), "kind": "oracle",
+            "sample": (f"{done_rows} query rows of layer 0 (sink, window, page and last-row "
+                       f"edges, then seeded positions), all {pspec.num_q_heads} Q heads, full "
+                       f"{N}-token context; scaled to {args.prefill_layers} layers x "
+                       f"{pspec.num_q_heads} heads per token"),
+            "seconds": round(spent, 2),
+            "accuracy": dict(_merge_acc(acc), rows=done_rows, layer=0)}
 
 
-def cpu_baseline_decode(torch, W, dspec, dplan, q_dec, dev, args, log):
+def cpu_baseline_decode(torch, W, dspec, dplan, q_dec, dev, args, log, o_dec):
     """The oracle on the decode workload: the decode row of one (sequence, layer) at a
     time, against that sequence's whole dense K/V, until about a third of the
     prefill baseline's time has passed. Rate = K/V bytes of the keys the row sees
@@ -1011,6 +1249,7 @@ def cpu_baseline_decode(torch, W, dspec, dplan, q_dec, dev, args, log):
     Hkv, D = dspec.num_kv_heads, dspec.head_dim
     rng = np.random.default_rng([dspec.seed, 78])
     done, spent, nbytes = 0, 0.0, 0
+    acc = []
     while spent < args.cpu_seconds / 3:
         l, b = int(rng.integers(0, L)), int(rng.integers(0, B))
         kd = W.randn_bf16_device((B * n, Hkv, D), dspec.seed, W.TAG_K, l, dev)
@@ -1020,8 +1259,9 @@ def cpu_baseline_decode(torch, W, dspec, dplan, q_dec, dev, args, log):
         qr = q_dec[l, b:b + 1].view(torch.int16).cpu().numpy().view(np.uint16)
         del kd, vd
         t0 = time.perf_counter()
-        OA.attention_rows(dspec, l, b, [n - 1], qr, kb, vb)
+        ref, _ = OA.attention_rows(dspec, l, b, [n - 1], qr, kb, vb)
         spent += time.perf_counter() - t0
+        acc.append(_acc(_to_f64(o_dec[l, b:b + 1]), ref))
         nbytes += dplan.stats(l)["decode_tokens"] // B * 2 * D * 2
         done += 1
     gbs = nbytes / spent / 1e9
@@ -1029,7 +1269,8 @@ def cpu_baseline_decode(torch, W, dspec, dplan, q_dec, dev, args, log):
     return {"value": round(gbs, 4), "unit": "GB/s", "kind": "oracle",
             "sample": (f"the decode row of {done} seeded (sequence, layer) pairs of the "
                        f"{L}-layer decode workload, each against its {n}-token dense K/V"),
-            "seconds": round(spent, 2)}
+            "seconds": round(spent, 2),
+            "accuracy": dict(_merge_acc(acc), rows=done)}
 
 
 if __name__ == "__main__":
