@@ -1114,7 +1114,32 @@ __global__ __launch_bounds__(512) void prefill_kernel(
 
     // ---- prologue: blocks 0 .. NBUF - 2 in flight; blocks 0 and 1 landed; block
     // 0's scores and probabilities; operands of the first MFMA phase
-    for (int32_t k = 0; k < NBUF - 1; ++k) SEGPAGED_ISSUE(k);
+    if (!SMALLP) {
+      // the page ids of those blocks in one round trip, then their transfers
+      int32_t pid_[NBUF - 1], in_[NBUF - 1], kb32_[NBUF - 1], len_[NBUF - 1];
+#pragma unroll
+      for (int k = 0; k < NBUF - 1; ++k) {
+        int s_;
+        int32_t kb_;
+        runs.at(min(k, nblocks - 1), s_, kb_);
+        const int32_t first_ = (s_ ? sb1 : 0) + kb_ * BK;
+        pid_[k] = cpages[first_ >> log2P];
+        in_[k] = first_ & (P - 1);
+        kb32_[k] = kb_ * BK;
+        len_[k] = s_ ? sl1 : sl0;
+      }
+#pragma unroll
+      for (int k = 0; k < NBUF - 1; ++k) {
+        const int64_t pg0_ = (int64_t)pid_[k] * PD;
+        if (dma_wave) {
+          lds_dma16_s(kp + pg0_ + in_[k] * 8, k_off, lds_k + k * (TILE * 2));
+          lds_dma16_s(vp + pg0_ + (in_[k] >> 3) * (D * 8), v_off, lds_v + k * (TILE * 2));
+        }
+        if (gathered && wave == 0) lds_dma4(rpos + min(kb32_[k] + lane, len_[k] - 1), &sPos[k][0]);
+      }
+    } else {
+      for (int32_t k = 0; k < NBUF - 1; ++k) SEGPAGED_ISSUE(k);
+    }
     // issue sources of block NBUF - 1 (page base, byte offset within the page,
     // retrieval entries); the cursor then stays one block ahead, its page id
     // prefetched a phase before use
@@ -1141,7 +1166,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     // the previous tile's O while this tile's Q and first blocks are in flight
     SEGPAGED_EPILOGUE_PREV();
     // the next item; its return is waited for with the blocks below
-    if (tid == 0) it_next = (int32_t)prefill_fetch(ctr, gen, last_fetch);
+    if (tid == 0) it_next = (int32_t)(uint32_t)atomicAdd(ctr, 1ull);
     // Q and blocks 0 and 1 landed: vector loads complete in issue order and the
     // O stores can only lower the count
     WAIT_VM_LGKM0((NBUF - 3) * PER_BLOCK);
@@ -1273,7 +1298,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     }
   } else {
     SEGPAGED_EPILOGUE_PREV();
-    if (tid == 0) it_next = (int32_t)prefill_fetch(ctr, gen, last_fetch);
+    if (tid == 0) it_next = (int32_t)(uint32_t)atomicAdd(ctr, 1ull);
   }
 #undef SEGPAGED_PHASE_END
 #undef SEGPAGED_BLOCK_SOURCES
@@ -1292,7 +1317,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(
 #undef SEGPAGED_LOAD_V
 #undef SEGPAGED_LOAD_K
 #undef SEGPAGED_ISSUE
-  if (tid == 0) sItem[(round + 1) & 1] = it_next;
+  if (tid == 0) {
+    // the last fetch of the launch leaves the counter at (generation, 0)
+    if ((uint32_t)it_next == last_fetch) atomicExch(ctr, (unsigned long long)gen << 32);
+    sItem[(round + 1) & 1] = it_next;
+  }
   // every wave is done with the ring and sOverflow before the next tile's set-up
   __syncthreads();
   e_valid = true;
