@@ -95,11 +95,22 @@ typedef struct {
                                    0 = 1): local heads keep a ring of ceil((W + chunk - 1) / P) + 1
                                    pages, enough for every row of the newest chunk */
   int32_t reserved;             /* 0 */
+  /* Document chunks shared by several sequences at the same positions ([SUM]: identical
+   * document chunks reuse their KV; [RT section 1]: storage per layer x head x segment):
+   * sequences with the same doc_group >= 0 begin with the same doc_len tokens, whose
+   * K/V rows are identical in every layer and KV head (the caller's promise; the pool
+   * keeps the rows of the group's first sequence). A page whose positions all lie in
+   * [0, doc_len) is stored once per (layer, KV head, group) and its id is listed in
+   * the page list of every unit that holds the same positions with the same
+   * occupancy. Both NULL = no sharing. Not with append_capacity (EUNSUPPORTED). */
+  const int32_t* doc_group;     /* [B] group of each sequence, -1 = none */
+  const int32_t* doc_len;       /* [B] shared tokens, the same for all members of a group,
+                                   <= N_b (0 for sequences without a group) */
 } segpaged_spec;
 
 /* Sizes the caller allocates. */
 typedef struct {
-  int64_t num_pages;        /* pages the table uses */
+  int64_t num_pages;        /* distinct pages the table uses (shared document pages once) */
   int64_t pool_pages;       /* pages each pool tensor must hold (= capacity) */
   int64_t pool_bytes;       /* bytes of ONE pool tensor: pool_pages * P * D * 2 */
   int64_t table_int32s;     /* int32 elements of the device table (table + work lists) */
@@ -118,7 +129,7 @@ typedef struct {
  * and roofline accounting. */
 typedef struct {
   int64_t units;
-  int64_t pages;
+  int64_t pages;             /* distinct pages (a page shared by sequences counts once) */
   int64_t retained_tokens;   /* keys stored in the pool, summed over units (padding excluded) */
   int64_t decode_tokens;     /* keys the decode row (position N_b - 1) sees, summed over units */
   int64_t prefill_pairs;     /* visible (query row, key) pairs per KV-head unit over rows q0..N-1;
@@ -163,11 +174,13 @@ SEGPAGED_API int segpaged_plan_sizes(const segpaged_plan* plan, segpaged_sizes* 
  *           window, kv_len, nseg, seg0_pos, seg0_len, seg1_pos, seg1_len, page_off,
  *           retr_off (seg0_pos = -1 for a gathered RETRIEVAL segment; retr_off = -1
  *           for other classes; unused segment fields 0)
- *   pages   page id of each table page (a unit's pages start at page_off)
+ *   pages   page id of each table page (a unit's pages start at page_off); an id
+ *           repeats where sequences share a document page (doc_group)
  *   retr    positions of the RETRIEVAL segments, units in order
- * The ints after table_len are the kernels' work lists and, last, L + 1 lines of
- * 16 zero ints that prefill calls use as work counters (not part of the format;
- * segpaged_build uploads the lines of its layer and of all-layer calls).
+ * The ints after table_len are the build list (num_pages table page slots, in order:
+ * the slots that own a distinct page), the kernels' work lists and, last, L + 1
+ * lines of 16 zero ints that prefill calls use as work counters (not part of the
+ * format; segpaged_build uploads the lines of its layer and of all-layer calls).
  * ENOSPACE if n < table_int32s. */
 SEGPAGED_API int segpaged_plan_table_host(const segpaged_plan* plan, int32_t* out, int64_t n);
 
@@ -280,8 +293,9 @@ SEGPAGED_API int segpaged_select_topp(const segpaged_plan* plan, int32_t layer, 
  * for moving a cache to another device or process: prefill and decode on separate
  * machines move KV between them, and a SegPaged cache moves only what each head
  * keeps [SUM: KV transfer bytes in the disaggregated setting]. The stream holds the
- * table's pages of that range in table order, each in the pool page layout of
- * segpaged_build: stats(layer).pages * P * D bf16 per tensor (tail slots included).
+ * distinct pages of that range in table order of first use (a shared document page
+ * once), each in the pool page layout of segpaged_build: stats(layer).pages * P * D
+ * bf16 per tensor (tail slots included).
  *   d_table  device table image uploaded by segpaged_build or segpaged_import_pages
  *   k_out, v_out  device bf16 streams (written); pools are only read
  * The stream depends on the plan's units and segments, not on its page ids. */

@@ -17,6 +17,14 @@ only visible tokens; retrieval heads fetch pages on demand):
   page; unused tail slots hold zeros.
 * Page ids: units in order u = (l * B + b) * Hkv + h, segments in order, pages
   in order, each taking the next id of the free list (identity by default).
+* Shared documents (RedKnot summary: identical document chunks reuse their
+  KV; runtime explainer section 1: storage per layer x head x segment):
+  sequences of one document group begin with the same doc_len tokens. A page of
+  a member whose positions all lie in [0, doc_len) is the same page for every
+  member of the group whose page, in the same layer and KV head, holds exactly
+  the same positions: it takes an id once, at its first use in table order, and
+  the pool holds it once (written from that first use). Gathered (retrieval)
+  pages are never shared.
 
 Table format, version 1 (all int32):
     header  16 ints  magic 0x53475054, version 1, num_seqs, num_layers, Hq, Hkv,
@@ -98,12 +106,61 @@ def unit_segments(spec: Spec, b: int, l: int, h: int) -> List:
                              spec.retrieval.get((b, l, h)))
 
 
+def page_share_key(spec: Spec, b: int, l: int, h: int, seg, positions: np.ndarray):
+    """The identity of a page that sequences of a document group share, or None when
+    the page is the unit's own: (layer, KV head, group, its positions)."""
+    groups = spec.doc_group
+    if groups is None or groups[b] < 0 or seg[0] == "gathered":
+        return None
+    if len(positions) == 0 or int(positions[-1]) >= spec.doc_len[b]:
+        return None
+    return (l, h, groups[b], tuple(int(x) for x in positions))
+
+
+def unit_pages(spec: Spec):
+    """Every page slot of the table in order: (u, b, l, h, segment, positions, key)."""
+    P = spec.page_size
+    out = []
+    for (u, b, l, h) in units(spec):
+        for seg in unit_segments(spec, b, l, h):
+            pos = segment_positions(seg)
+            for p0 in range(0, len(pos), P):
+                pp = pos[p0:p0 + P]
+                out.append((u, b, l, h, seg, pp, page_share_key(spec, b, l, h, seg, pp)))
+    return out
+
+
+def page_assignment(spec: Spec) -> Tuple[List[int], List[int]]:
+    """(distinct page index of every page slot, the slots where a distinct page is
+    first used): a shared page takes its index at its first slot."""
+    index, first, seen = [], [], {}
+    for slot, (_, _, _, _, _, _, key) in enumerate(unit_pages(spec)):
+        if key is not None and key in seen:
+            index.append(seen[key])
+            continue
+        d = len(first)
+        if key is not None:
+            seen[key] = d
+        first.append(slot)
+        index.append(d)
+    return index, first
+
+
+def distinct_pages(spec: Spec, layer: int = None) -> int:
+    """Pages the pool holds (of one layer, or all)."""
+    if layer is None:
+        return len(page_assignment(spec)[1])
+    slots = unit_pages(spec)
+    return sum(1 for s in page_assignment(spec)[1] if slots[s][2] == layer)
+
+
 def table(spec: Spec) -> np.ndarray:
     """The expected table ints (int32)."""
     P = spec.page_size
     B = spec.num_seqs
     recs, page_ids, retr = [], [], []
     free = spec.free_list
+    index, _ = page_assignment(spec)
     nxt = 0
     for (u, b, l, h) in units(spec):
         kind, sink, window = spec.head_class(l, h)
@@ -124,7 +181,8 @@ def table(spec: Spec) -> np.ndarray:
             rec[11 + 2 * si] = ln
             kv_len += ln
             for _ in range(ceil_div(ln, P)):
-                page_ids.append(nxt if free is None else int(free[nxt]))
+                d = index[nxt]
+                page_ids.append(d if free is None else int(free[d]))
                 nxt += 1
         rec[8] = kv_len
         recs.append(rec)
@@ -181,6 +239,8 @@ def pool_loops(spec: Spec, layer: int, k_bits: np.ndarray, v_bits: np.ndarray,
         for h in range(spec.num_kv_heads):
             for pos, pids in unit_page_ids(spec, b, layer, h, tab):
                 for pi, pid in enumerate(pids):
+                    if written[pid]:
+                        continue  # a shared page, written by its first use
                     written[pid] = True
                     for slot in range(P):
                         t = pi * P + slot
@@ -208,6 +268,8 @@ def pool(spec: Spec, layer: int, k_bits: np.ndarray, v_bits: np.ndarray,
         for h in range(spec.num_kv_heads):
             for pos, pids in unit_page_ids(spec, b, layer, h, tab):
                 for pi, pid in enumerate(pids):
+                    if written[pid]:
+                        continue  # a shared page, written by its first use
                     written[pid] = True
                     rows = kvo[b] + pos[pi * P:(pi + 1) * P]
                     kt = np.zeros((P, D), dtype=np.uint16)
@@ -226,25 +288,27 @@ def transfer_stream(spec: Spec, layer: int, k_bits: np.ndarray, v_bits: np.ndarr
     """The pages of one layer as a transfer stream (K uint16 [pages, D/8, P, 8],
     V uint16 [pages, P/8, D, 8]): units in table order, their segments in order,
     each segment's pages in order, every page in the pool layout with zero tail
-    slots. Only what each head keeps is moved (RedKnot summary, system gains: KV
-    bytes moved between prefill and decode machines); the stream does not depend
+    slots; a page that sequences of a document group share comes once, at its
+    first use. Only what each head keeps is moved (RedKnot summary, system gains:
+    KV bytes moved between prefill and decode machines); the stream does not depend
     on page ids. k_bits/v_bits: that layer's dense K/V [T_total, Hkv, D]."""
     P, D = spec.page_size, spec.head_dim
     kvo = spec.kv_row_offsets()
-    ks, vs = [], []
-    for (u, b, l, h) in units(spec):
+    ks, vs, sent = [], [], set()
+    for (u, b, l, h, seg, pos, key) in unit_pages(spec):
         if l != layer:
             continue
-        for seg in unit_segments(spec, b, l, h):
-            pos = segment_positions(seg)
-            for p0 in range(0, len(pos), P):
-                rows = kvo[b] + pos[p0:p0 + P]
-                kt = np.zeros((P, D), dtype=np.uint16)
-                vt = np.zeros((P, D), dtype=np.uint16)
-                kt[:len(rows)] = k_bits[rows, h]
-                vt[:len(rows)] = v_bits[rows, h]
-                ks.append(kt.reshape(P, D // 8, 8).transpose(1, 0, 2))
-                vs.append(vt.reshape(P // 8, 8, D).transpose(0, 2, 1))
+        if key is not None:
+            if key in sent:
+                continue
+            sent.add(key)
+        rows = kvo[b] + pos
+        kt = np.zeros((P, D), dtype=np.uint16)
+        vt = np.zeros((P, D), dtype=np.uint16)
+        kt[:len(rows)] = k_bits[rows, h]
+        vt[:len(rows)] = v_bits[rows, h]
+        ks.append(kt.reshape(P, D // 8, 8).transpose(1, 0, 2))
+        vs.append(vt.reshape(P // 8, 8, D).transpose(0, 2, 1))
     if not ks:
         return (np.zeros((0, D // 8, P, 8), np.uint16), np.zeros((0, P // 8, D, 8), np.uint16))
     return np.stack(ks), np.stack(vs)

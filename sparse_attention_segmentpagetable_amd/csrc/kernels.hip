@@ -86,20 +86,23 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
 }
 
 // ---------------------------------------------------------------------------
-// build: one workgroup per page. Rows are read coalesced into LDS, then written
-// out in the K [D/8][P][8] and V [P/8][D][8] page layouts. Tail slots are zero.
+// build: one workgroup per distinct page (the table slots of the build list; a
+// page that sequences of a document group share is written once, from the slot
+// that owns it). Rows are read coalesced into LDS, then written out in the K
+// [D/8][P][8] and V [P/8][D][8] page layouts. Tail slots are zero.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void build_kernel(
     const int32_t* __restrict__ tab, int32_t off_seqs, int32_t off_units, int32_t off_pages,
-    int32_t off_retr, int32_t unit_b, int32_t unit_e, int32_t page_b, int32_t Hkv, int32_t P,
-    int32_t log2P, const uint16_t* __restrict__ kd, const uint16_t* __restrict__ vd,
-    int64_t dense_layer_stride, uint16_t* __restrict__ kp, uint16_t* __restrict__ vp) {
+    int32_t off_retr, int32_t off_bld, int32_t unit_b, int32_t unit_e, int32_t bld_b,
+    int32_t Hkv, int32_t P, int32_t log2P, const uint16_t* __restrict__ kd,
+    const uint16_t* __restrict__ vd, int64_t dense_layer_stride, uint16_t* __restrict__ kp,
+    uint16_t* __restrict__ vp) {
   constexpr int KCH = D / 8;        // 16-byte chunks per row
   constexpr int PITCH = D + 8;      // LDS row pitch (elements), breaks bank aliasing
   __shared__ __attribute__((aligned(16))) uint16_t rows[128 * PITCH];
 
-  const int32_t pg = page_b + (int32_t)blockIdx.x;  // page slot in the table
+  const int32_t pg = tab[off_bld + bld_b + (int32_t)blockIdx.x];  // page slot in the table
   // owning unit: last unit in [unit_b, unit_e) whose page_off <= pg
   int32_t lo = unit_b, hi = unit_e - 1;
   while (lo < hi) {
@@ -1339,7 +1342,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(
 // ids of a table. Grid-stride over 16-byte chunks; blockIdx.y picks K or V.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void page_copy_kernel(
-    const int32_t* __restrict__ tab, int32_t off_pages, int32_t page_b, int64_t npages,
+    const int32_t* __restrict__ tab, int32_t off_pages, int32_t off_bld, int32_t bld_b,
+    int64_t npages,
     int32_t log2c, const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src,
     uint16_t* __restrict__ k_dst, uint16_t* __restrict__ v_dst, int32_t to_stream) {
   const uint16_t* src = blockIdx.y ? v_src : k_src;
@@ -1347,7 +1351,7 @@ __global__ __launch_bounds__(256) void page_copy_kernel(
   const int64_t nchunks = npages << log2c, cmask = ((int64_t)1 << log2c) - 1;
   for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunks;
        c += (int64_t)gridDim.x * 256) {
-    const int64_t pid = tab[off_pages + page_b + (c >> log2c)];
+    const int64_t pid = tab[off_pages + tab[off_bld + bld_b + (c >> log2c)]];
     const int64_t pc = (pid << log2c) + (c & cmask);  // the chunk in the pool
     if (to_stream)
       st16(dst + c * 8, ld16(src + pc * 8));
@@ -1382,7 +1386,7 @@ int check_launch() {
 
 struct Span {
   int64_t unit_b, unit_e, page_b, page_e, retr_b, retr_e, dec_b, dec_e, pre_b, pre_e;
-  int64_t max_unit_items;
+  int64_t max_unit_items, bld_b, bld_e;
 };
 
 // The pools may be NULL when the plan has no pages (no head keeps a token).
@@ -1394,10 +1398,10 @@ Span span_of(const segpaged_plan* pl, int32_t layer) {
   if (layer >= 0) {
     const LayerRange& r = pl->layers[layer];
     return {r.unit_b, r.unit_e, r.page_b, r.page_e, r.retr_b, r.retr_e,
-            r.dec_b, r.dec_e, r.pre_b, r.pre_e, r.max_unit_items};
+            r.dec_b, r.dec_e, r.pre_b, r.pre_e, r.max_unit_items, r.bld_b, r.bld_e};
   }
-  return {0, pl->num_units, 0, pl->num_pages, 0, pl->num_retr, 0, pl->n_dec, 0, pl->n_pre,
-          pl->max_unit_items};
+  return {0, pl->num_units, 0, pl->num_slots, 0, pl->num_retr, 0, pl->n_dec, 0, pl->n_pre,
+          pl->max_unit_items, 0, pl->num_pages};
 }
 
 int upload(const segpaged_plan* pl, int32_t* d_table, int64_t off, int64_t count,
@@ -1421,6 +1425,7 @@ int upload_layer_table(const segpaged_plan* pl, int32_t layer, int32_t* d_table,
     return rc;
   if ((rc = upload(pl, d_table, pl->off_pages + sp.page_b, sp.page_e - sp.page_b, st))) return rc;
   if ((rc = upload(pl, d_table, pl->off_retr + sp.retr_b, sp.retr_e - sp.retr_b, st))) return rc;
+  if ((rc = upload(pl, d_table, pl->off_bld + sp.bld_b, sp.bld_e - sp.bld_b, st))) return rc;
   if ((rc = upload(pl, d_table, pl->off_decunits + 2 * sp.unit_b, 2 * (sp.unit_e - sp.unit_b),
                    st)))
     return rc;
@@ -1438,11 +1443,12 @@ int upload_layer_table(const segpaged_plan* pl, int32_t layer, int32_t* d_table,
   return upload(pl, d_table, pl->off_ctr + kCtrInts * pl->L, kCtrInts, st);
 }
 
-// Pages [page_b, page_e) of the table between a pool and a contiguous stream.
+// The distinct pages of a layer range (build list order) between a pool and a
+// contiguous stream.
 int launch_page_copy(const segpaged_plan* pl, const Span& sp, const int32_t* d_table,
                      const void* k_src, const void* v_src, void* k_dst, void* v_dst,
                      int32_t to_stream, hipStream_t st) {
-  const int64_t npages = sp.page_e - sp.page_b;
+  const int64_t npages = sp.bld_e - sp.bld_b;
   if (npages == 0) return SEGPAGED_OK;  // empty streams may be NULL
   if (!k_src || !v_src || !k_dst || !v_dst) return SEGPAGED_EINVAL;
   const int32_t log2c = pl->log2P + __builtin_ctz((unsigned)pl->D) - 3;  // 16-byte chunks per page
@@ -1450,7 +1456,7 @@ int launch_page_copy(const segpaged_plan* pl, const Span& sp, const int32_t* d_t
   const int64_t cus = std::max(device_cus(), 1);
   const dim3 grid((unsigned)std::min<int64_t>((nchunks + 255) / 256, cus * 64), 2), block(256);
   hipLaunchKernelGGL(page_copy_kernel, grid, block, 0, st, d_table, (int32_t)pl->off_pages,
-                     (int32_t)sp.page_b, npages, log2c, (const uint16_t*)k_src,
+                     (int32_t)pl->off_bld, (int32_t)sp.bld_b, npages, log2c, (const uint16_t*)k_src,
                      (const uint16_t*)v_src, (uint16_t*)k_dst, (uint16_t*)v_dst, to_stream);
   return check_launch();
 }
@@ -1494,7 +1500,7 @@ SEGPAGED_API int segpaged_build(const segpaged_plan* pl, int32_t layer, const vo
   const Span sp = span_of(pl, layer);
   const int rc = upload_layer_table(pl, layer, d_table, st);
   if (rc) return rc;
-  const int64_t npages = sp.page_e - sp.page_b;
+  const int64_t npages = sp.bld_e - sp.bld_b;
   if (npages == 0) return SEGPAGED_OK;
   const int64_t dstride = layer < 0 ? pl->kv_rows * pl->Hkv * pl->D : 0;
   auto* kd = (const uint16_t*)k_dense;
@@ -1505,13 +1511,13 @@ SEGPAGED_API int segpaged_build(const segpaged_plan* pl, int32_t layer, const vo
   if (pl->D == 128)
     hipLaunchKernelGGL(build_kernel<128>, grid, block, 0, st, d_table, (int32_t)pl->off_seqs,
                        (int32_t)pl->off_units, (int32_t)pl->off_pages, (int32_t)pl->off_retr,
-                       (int32_t)sp.unit_b, (int32_t)sp.unit_e, (int32_t)sp.page_b, pl->Hkv, pl->P,
-                       pl->log2P, kd, vd, dstride, kpp, vpp);
+                       (int32_t)pl->off_bld, (int32_t)sp.unit_b, (int32_t)sp.unit_e,
+                       (int32_t)sp.bld_b, pl->Hkv, pl->P, pl->log2P, kd, vd, dstride, kpp, vpp);
   else
     hipLaunchKernelGGL(build_kernel<64>, grid, block, 0, st, d_table, (int32_t)pl->off_seqs,
                        (int32_t)pl->off_units, (int32_t)pl->off_pages, (int32_t)pl->off_retr,
-                       (int32_t)sp.unit_b, (int32_t)sp.unit_e, (int32_t)sp.page_b, pl->Hkv, pl->P,
-                       pl->log2P, kd, vd, dstride, kpp, vpp);
+                       (int32_t)pl->off_bld, (int32_t)sp.unit_b, (int32_t)sp.unit_e,
+                       (int32_t)sp.bld_b, pl->Hkv, pl->P, pl->log2P, kd, vd, dstride, kpp, vpp);
   return check_launch();
 }
 
@@ -1525,7 +1531,7 @@ SEGPAGED_API int segpaged_export_pages(const segpaged_plan* pl, int32_t layer,
     return SEGPAGED_EINVAL;
   if (layer < -1 || layer >= pl->L) return SEGPAGED_ESTATE;
   const Span sp = span_of(pl, layer);
-  if (sp.page_e > sp.page_b && (!k_out || !v_out)) return SEGPAGED_EINVAL;
+  if (sp.bld_e > sp.bld_b && (!k_out || !v_out)) return SEGPAGED_EINVAL;
   return launch_page_copy(pl, sp, d_table, k_pool, v_pool, k_out, v_out, 1, (hipStream_t)stream);
 }
 
@@ -1538,7 +1544,7 @@ SEGPAGED_API int segpaged_import_pages(const segpaged_plan* pl, int32_t layer, c
     return SEGPAGED_EINVAL;
   if (layer < -1 || layer >= pl->L) return SEGPAGED_ESTATE;
   const Span sp = span_of(pl, layer);
-  if (sp.page_e > sp.page_b && (!k_in || !v_in)) return SEGPAGED_EINVAL;
+  if (sp.bld_e > sp.bld_b && (!k_in || !v_in)) return SEGPAGED_EINVAL;
   hipStream_t st = (hipStream_t)stream;
   const int rc = upload_layer_table(pl, layer, d_table, st);
   if (rc) return rc;

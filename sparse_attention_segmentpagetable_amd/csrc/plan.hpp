@@ -47,6 +47,7 @@ struct LayerRange {
   int64_t retr_b, retr_e;   // retrieval positions
   int64_t dec_b, dec_e;     // decode items
   int64_t pre_b, pre_e;     // prefill items
+  int64_t bld_b, bld_e;     // build list: the table page slots that own a distinct page
   int64_t max_unit_items;   // most decode items of one unit
 };
 
@@ -56,8 +57,10 @@ struct segpaged_plan {
   int32_t B = 0, L = 0, Hq = 0, Hkv = 0, D = 0, P = 0, G = 0, log2P = 0;
   int32_t split = 0;            // decode keys per item
   int64_t num_units = 0, num_pages = 0, pool_pages = 0, num_retr = 0;
+  int64_t num_slots = 0;        // page-list entries (num_pages of them own their page)
   int64_t q_rows = 0, kv_rows = 0;
   int64_t off_seqs = 0, off_units = 0, off_pages = 0, off_retr = 0, table_len = 0;
+  int64_t off_bld = 0;          // build list (page slots in order), after the table
   int64_t off_decunits = 0, off_dec = 0, off_pre = 0, off_ctr = 0, total_ints = 0;
   int64_t n_dec = 0, n_pre = 0, max_unit_items = 0;
   std::vector<int32_t> buf;                  // device image: table ++ work lists

@@ -9,8 +9,10 @@
 #include <algorithm>
 #include <cstring>
 #include <limits>
+#include <map>
 #include <new>
 #include <numeric>
+#include <tuple>
 #include <vector>
 
 #include "plan.hpp"
@@ -359,6 +361,25 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
         }
   }
 
+  // document groups: members share doc_len leading tokens (same for all members)
+  const bool share = s.doc_group != nullptr;
+  if (share != (s.doc_len != nullptr)) return SEGPAGED_EINVAL;
+  std::vector<int64_t> group_len;  // per group id: its doc_len, -1 = not seen
+  if (share) {
+    if (s.append_capacity > 0) return SEGPAGED_EUNSUPPORTED;  // appends could write shared pages
+    for (int64_t b = 0; b < B; ++b) {
+      const int64_t g = s.doc_group[b], c = s.doc_len[b];
+      if (g < -1 || g >= B || c < 0 || c > s.seq_len[b]) return SEGPAGED_EINVAL;
+      if (g < 0) {
+        if (c != 0) return SEGPAGED_EINVAL;
+        continue;
+      }
+      if ((int64_t)group_len.size() <= g) group_len.resize(g + 1, -1);
+      if (group_len[g] >= 0 && group_len[g] != c) return SEGPAGED_EINVAL;
+      group_len[g] = c;
+    }
+  }
+
   segpaged_plan* pl = new (std::nothrow) segpaged_plan();
   if (!pl) return SEGPAGED_ENOSPACE;
   pl->B = (int32_t)B; pl->L = (int32_t)L; pl->Hq = s.num_q_heads; pl->Hkv = (int32_t)Hkv;
@@ -414,6 +435,48 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
       }
   if (num_pages > kI32Max || num_retr > kI32Max) { delete pl; return SEGPAGED_EINVAL; }
 
+  // Distinct pages: every page slot owns a page of its own, except that a page of a
+  // document group member whose positions all lie in the group's shared prefix is
+  // the same page for every member holding the same positions (same first position
+  // and occupancy) in the same layer and KV head. slot_page: slot -> distinct page
+  // index (ids in order of first use); build: the slots that own their page.
+  const int64_t num_slots = num_pages;
+  std::vector<int32_t> slot_page(num_slots);
+  std::vector<int32_t> build;
+  build.reserve(num_slots);
+  {
+    std::map<std::tuple<int64_t, int64_t, int64_t, int64_t, int64_t>, int32_t> shared;
+    int64_t slot = 0, distinct = 0;
+    for (int64_t u = 0; u < U; ++u) {
+      const int64_t l = u / (B * Hkv), b = (u / Hkv) % B, h = u % Hkv;
+      const int64_t g = share ? s.doc_group[b] : -1;
+      const int64_t c = g >= 0 ? s.doc_len[b] : 0;
+      int64_t left = res_pages[u];
+      for (int k = 0; k < nseg[u]; ++k) {
+        const Seg& sg = segs[2 * u + k];
+        for (int64_t t = 0; t < ceil_div(sg.len, P) && left > 0; ++t, --left, ++slot) {
+          const int64_t first = sg.pos0 + t * P, occ = std::min(P, sg.len - t * P);
+          if (g >= 0 && sg.pos0 >= 0 && first + occ <= c) {
+            auto key = std::make_tuple(l, h, g, first, occ);
+            auto it = shared.find(key);
+            if (it != shared.end()) {
+              slot_page[slot] = it->second;
+              continue;
+            }
+            shared.emplace(key, (int32_t)distinct);
+          }
+          slot_page[slot] = (int32_t)distinct++;
+          build.push_back((int32_t)slot);
+        }
+      }
+      for (; left > 0; --left, ++slot) {  // reserved pages past the segments (growth)
+        slot_page[slot] = (int32_t)distinct++;
+        build.push_back((int32_t)slot);
+      }
+    }
+    num_pages = distinct;
+  }
+
   int64_t capacity = s.capacity_pages ? s.capacity_pages : num_pages;
   if (capacity < num_pages) { delete pl; return SEGPAGED_ENOSPACE; }
   if (capacity > kI32Max) { delete pl; return SEGPAGED_EINVAL; }
@@ -427,6 +490,7 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
     }
   }
   pl->num_pages = num_pages;
+  pl->num_slots = num_slots;
   pl->pool_pages = capacity;
   pl->num_retr = num_retr;
 
@@ -434,7 +498,7 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
   pl->off_seqs = kHeaderInts;
   pl->off_units = pl->off_seqs + kSeqInts * B;
   pl->off_pages = pl->off_units + kUnitInts * U;
-  pl->off_retr = pl->off_pages + num_pages;
+  pl->off_retr = pl->off_pages + num_slots;
   pl->table_len = pl->off_retr + num_retr;
 
   // decode split: automatic = enough items to fill the GPU several times over
@@ -454,13 +518,15 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
   pl->split = (int32_t)split;
 
   std::vector<int32_t>& t = pl->buf;
-  t.assign(pl->table_len, 0);
-  pl->off_decunits = pl->table_len;
+  pl->off_bld = pl->table_len;
+  t.assign(pl->off_bld + num_pages, 0);
+  std::copy(build.begin(), build.end(), t.begin() + pl->off_bld);
+  pl->off_decunits = pl->off_bld + num_pages;
 
   // header and sequences
   const int32_t hdr[kHeaderInts] = {kMagic, kVersion, (int32_t)B, (int32_t)L, s.num_q_heads,
                                     (int32_t)Hkv, s.head_dim, (int32_t)P, (int32_t)U,
-                                    (int32_t)num_pages, (int32_t)num_retr, (int32_t)pl->off_seqs,
+                                    (int32_t)num_slots, (int32_t)num_retr, (int32_t)pl->off_seqs,
                                     (int32_t)pl->off_units, (int32_t)pl->off_pages,
                                     (int32_t)pl->off_retr, (int32_t)pl->table_len};
   std::memcpy(t.data(), hdr, sizeof(hdr));
@@ -502,9 +568,10 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
           kv_len += sg.len;
         }
         r[U_KVLEN] = (int32_t)kv_len;
-        for (int64_t p = 0; p < res_pages[u]; ++p, ++page_cursor)
-          t[pl->off_pages + page_cursor] = s.free_list ? s.free_list[page_cursor]
-                                                        : (int32_t)page_cursor;
+        for (int64_t p = 0; p < res_pages[u]; ++p, ++page_cursor) {
+          const int32_t d = slot_page[page_cursor];
+          t[pl->off_pages + page_cursor] = s.free_list ? s.free_list[d] : d;
+        }
         if (grow) {  // most decode items this unit can ever need
           if (eff == SEGPAGED_LOCAL)
             dec_cap += ceil_div(s.sink[c], split) + ceil_div(s.window[c], split) + 2;
@@ -513,7 +580,10 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
         }
       }
     lr.page_e = page_cursor; lr.retr_e = retr_cursor;
-    pl->stats[l].pages = lr.page_e - lr.page_b;
+    // the build list is in slot order, so a layer's owners are contiguous
+    lr.bld_b = std::lower_bound(build.begin(), build.end(), (int32_t)lr.page_b) - build.begin();
+    lr.bld_e = std::lower_bound(build.begin(), build.end(), (int32_t)lr.page_e) - build.begin();
+    pl->stats[l].pages = lr.bld_e - lr.bld_b;
   }
 
   // ---- work lists after the table: decode units, decode items, prefill items,

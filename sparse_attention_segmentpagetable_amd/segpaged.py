@@ -41,7 +41,8 @@ class _Spec(ctypes.Structure):
                 ("retr_pos", _i32p), ("free_list", _i32p), ("free_list_len", ctypes.c_int64),
                 ("capacity_pages", ctypes.c_int64), ("decode_split_tokens", ctypes.c_int32),
                 ("append_capacity", ctypes.c_int32),
-                ("append_chunk", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("append_chunk", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("doc_group", _i32p), ("doc_len", _i32p)]
 
 
 class Sizes(ctypes.Structure):
@@ -167,6 +168,14 @@ class Plan:
         if fl is not None:
             keep["free"] = _arr32(fl)
             ptr_free, fl_len = keep["free"].ctypes.data_as(_i32p), len(keep["free"])
+        dg, dl = getattr(spec, "doc_group", None), getattr(spec, "doc_len", None)
+        ptr_dg = ptr_dl = None
+        if dg is not None:
+            keep["doc_group"] = _arr32(dg)
+            ptr_dg = keep["doc_group"].ctypes.data_as(_i32p)
+        if dl is not None:
+            keep["doc_len"] = _arr32(dl)
+            ptr_dl = keep["doc_len"].ctypes.data_as(_i32p)
         c = _Spec(num_seqs=B, num_layers=L, num_q_heads=spec.num_q_heads, num_kv_heads=Hkv,
                   head_dim=spec.head_dim, page_size=spec.page_size,
                   seq_len=keep["seq_len"].ctypes.data_as(_i32p),
@@ -177,7 +186,7 @@ class Plan:
                   retr_offsets=ptr_offs, retr_pos=ptr_pos, free_list=ptr_free,
                   free_list_len=fl_len, capacity_pages=int(getattr(spec, "capacity_pages", 0) or 0),
                   decode_split_tokens=decode_split_tokens, append_capacity=append_capacity,
-                  append_chunk=append_chunk, reserved=0)
+                  append_chunk=append_chunk, reserved=0, doc_group=ptr_dg, doc_len=ptr_dl)
         self._h = ctypes.c_void_p()
         self.sizes = Sizes()
         _check(_lib().segpaged_plan_create(ctypes.byref(c), ctypes.byref(self._h),

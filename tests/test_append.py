@@ -116,8 +116,9 @@ def test_decode_items_cover_visible_keys_after_appends():
         t = plan.table_host()
         z = plan.sizes
         U = z.num_units
-        du = t[z.table_len:z.table_len + 2 * U].reshape(U, 2)
-        items = t[z.table_len + 2 * U:z.table_len + 2 * U + 4 * z.decode_items].reshape(-1, 4)
+        w0 = z.table_len + z.num_pages  # work lists follow the build list
+        du = t[w0:w0 + 2 * U].reshape(U, 2)
+        items = t[w0 + 2 * U:w0 + 2 * U + 4 * z.decode_items].reshape(-1, 4)
         P = spec.page_size
         for (u, b, l, h) in OL.units(spec):
             kind, _, _ = spec.head_class(l, h)

@@ -208,3 +208,73 @@ def test_pool_round_trip_and_loops_agree():
                     for slot in range(8 - tail, 8) if tail else []:
                         assert not kp[pids[-1], :, slot, :].any()
                         assert not vp[pids[-1], slot // 8, :, slot % 8].any()
+
+
+def _doc_spec(form="prefill", P=64, n=(700, 900, 400), c=500):
+    """Sequences 0 and 1 share a 500-token document; sequence 2 has none. KV heads:
+    global, local (sink 4, window 100), retrieval."""
+    kind = [W.GLOBAL, W.LOCAL, W.RETRIEVAL]
+    retr = {(b, 0, 2): np.arange(0, nb, 7, dtype=np.int32) for b, nb in enumerate(n)}
+    s = W.Spec(name=f"doc-{form}", num_layers=1, num_q_heads=6, num_kv_heads=3, head_dim=64,
+               page_size=P, seq_len=list(n), first_query_pos=[0] * len(n), kind=kind,
+               sink=[0, 4, 0], window=[1, 100, 1], retrieval=retr, seed=44,
+               doc_group=[0, 0, -1], doc_len=[c, c, 0])
+    return s if form == "prefill" else W.decode_form(s)
+
+
+def test_shared_document_pages_closed_forms():
+    """Two sequences with one 500-token document, page 64: a global head (and a local
+    head whose prefill-form segment is the whole context) stores the 7 full pages
+    inside the document once, so 11 + 15 - 7 pages; the page holding positions
+    448..511 crosses the document's end and stays private. Retrieval pages are never
+    shared. In decode form the local head's sink page (positions 0..3) is shared and
+    its windows (600..699, 800..899) are not."""
+    spec = _doc_spec("prefill")
+    third = L.ceil_div(400, 64)
+    for h in (0, 1):
+        pages = {}
+        for slot, (u, b, l, hh, seg, pos, key) in enumerate(L.unit_pages(spec)):
+            if hh == h:
+                pages.setdefault(key if key is not None else ("own", slot), 0)
+        assert len(pages) == 11 + 15 - 7 + third, h
+    retr_keys = [k for (_, _, _, hh, _, _, k) in L.unit_pages(spec) if hh == 2]
+    assert all(k is None for k in retr_keys)
+    per_seq_retr = sum(L.ceil_div(len(range(0, nb, 7)), 64) for nb in spec.seq_len)
+    assert L.distinct_pages(spec) == 2 * (11 + 15 - 7 + third) + per_seq_retr
+    # the table lists every unit's pages, ids repeating where shared
+    assert L.num_pages(spec) == 2 * (11 + 15 + third) + per_seq_retr
+    dspec = _doc_spec("decode")
+    local = [k for (_, _, _, hh, _, _, k) in L.unit_pages(dspec) if hh == 1]
+    # sequences 0, 1, 2: sink page + 2 window pages each; the first two sinks are one page
+    assert len(local) == 9 and sum(k is not None for k in local) == 2
+    assert L.distinct_pages(dspec) == L.num_pages(dspec) - 1 - 7
+
+
+def test_shared_document_pool_round_trip():
+    """Gathering each unit's pages through the table gives back that sequence's own
+    dense K/V at every retained position (so a page is shared only where the
+    members' rows are identical), and the pool holds each shared page once."""
+    for form in ("prefill", "decode"):
+        spec = _doc_spec(form, P=32)
+        kb, vb = W.kv_bits(spec, 0)
+        kvo = spec.kv_row_offsets()
+        assert np.array_equal(kb[kvo[0]:kvo[0] + 500], kb[kvo[1]:kvo[1] + 500])
+        assert not np.array_equal(kb[kvo[0] + 500:kvo[0] + 600], kb[kvo[1] + 500:kvo[1] + 600])
+        tab = L.table(spec)
+        n_pool = L.distinct_pages(spec)
+        kp, vp, written = L.pool(spec, 0, kb, vb, n_pool)
+        assert written.sum() == n_pool
+        kl, vl, wl = L.pool_loops(spec, 0, kb, vb, n_pool)
+        assert np.array_equal(kp, kl) and np.array_equal(vp, vl) and np.array_equal(written, wl)
+        for b in range(spec.num_seqs):
+            for h in range(spec.num_kv_heads):
+                for pos, pids in L.unit_page_ids(spec, b, 0, h, tab):
+                    for i, p in enumerate(pos):
+                        pid, slot = pids[i // 32], i % 32
+                        k_el = kp[pid, :, slot, :].reshape(-1)
+                        v_el = vp[pid, slot // 8, :, slot % 8]
+                        assert np.array_equal(k_el, kb[kvo[b] + p, h])
+                        assert np.array_equal(v_el, vb[kvo[b] + p, h])
+        # the stream moves every distinct page once
+        ks, vs = L.transfer_stream(spec, 0, kb, vb)
+        assert len(ks) == n_pool

@@ -47,6 +47,22 @@ def _specs():
     yield replace(s, seq_len=[50, 0, 7], first_query_pos=[0, 0, 6])  # empty + ragged sequences
     for seed in range(100, 132):  # the first half of the GPU tests' random specs
         yield random_spec(seed)
+    yield from _doc_specs()
+
+
+def _doc_specs():
+    """Document groups: sequences 0 and 2 share 300 tokens, 1 and 3 share 64, 4 none."""
+    kind = [W.GLOBAL, W.LOCAL, W.RETRIEVAL, W.LOCAL, W.DENSE, W.GLOBAL]
+    n = [700, 333, 301, 64, 90]
+    retr = {(b, 1, 0): np.arange(1, nb, 5, dtype=np.int32) for b, nb in enumerate(n)}
+    base = W.Spec(name="doc", num_layers=3, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                  page_size=32, seq_len=n, first_query_pos=[0] * 5, kind=kind,
+                  sink=[0, 4, 0, 33, 0, 0], window=[1, 60, 1, 8, 1, 1], retrieval=retr, seed=7,
+                  doc_group=[0, 1, 0, 1, -1], doc_len=[300, 64, 300, 64, 0])
+    yield base
+    yield replace(W.decode_form(base), name="doc-decode")
+    yield replace(base, name="doc-p16-free", page_size=16,
+                  free_list=W.seeded_free_list(400, 3), capacity_pages=400)
 
 
 @pytest.mark.parametrize("spec", list(_specs()), ids=lambda s: f"{s.name}")
@@ -56,7 +72,7 @@ def test_table_bit_exact_vs_oracle(spec):
     ref = OL.table(spec)
     assert plan.sizes.table_len == len(ref)
     assert np.array_equal(got[:len(ref)], ref)
-    assert plan.sizes.num_pages == int(ref[9])
+    assert plan.sizes.num_pages == OL.distinct_pages(spec)  # the table lists ref[9] slots
     assert plan.sizes.q_rows == spec.total_q_rows and plan.sizes.kv_rows == spec.total_tokens
 
 
@@ -87,9 +103,10 @@ def _decode_items(plan):
     t = plan.table_host()
     z = plan.sizes
     U = z.num_units
-    du = t[z.table_len:z.table_len + 2 * U].reshape(U, 2)
-    items = t[z.table_len + 2 * U:z.table_len + 2 * U + 4 * z.decode_items].reshape(-1, 4)
-    p0 = z.table_len + 2 * U + 4 * z.decode_items
+    w0 = z.table_len + z.num_pages  # work lists follow the build list
+    du = t[w0:w0 + 2 * U].reshape(U, 2)
+    items = t[w0 + 2 * U:w0 + 2 * U + 4 * z.decode_items].reshape(-1, 4)
+    p0 = w0 + 2 * U + 4 * z.decode_items
     pre = t[p0:p0 + 2 * z.prefill_items].reshape(-1, 2)
     assert np.all(t[p0 + 2 * z.prefill_items:] == 0)  # work counters start at zero
     return t, du, items, pre
@@ -307,8 +324,9 @@ def test_counter_lines_aligned_and_zero(spec, cap):
     """The L + 1 prefill work-counter lines (16 ints each, the first 8 bytes a 64-bit
     counter) start 16-byte aligned in the image and are uploaded as zeros: the state
     a prefill call's generation claim starts from."""
-    if cap:  # growth plans reserve more pages than the spec's own free list holds
-        spec = replace(spec, free_list=None, capacity_pages=0)
+    if cap:  # growth plans reserve more pages than the spec's own free list holds,
+        # and share no document pages
+        spec = replace(spec, free_list=None, capacity_pages=0, doc_group=None, doc_len=None)
         if any(n - q0 > 1 for n, q0 in zip(spec.seq_len, spec.first_query_pos)):
             spec = W.decode_form(spec)
     plan = sp.Plan(spec, append_capacity=cap)
@@ -319,3 +337,38 @@ def test_counter_lines_aligned_and_zero(spec, cap):
     assert c0 % 4 == 0 and np.all(t[c0:c1] == 0)
     z = plan.sizes
     assert c0 >= z.table_len + 2 * z.num_units + 4 * z.decode_items + 2 * z.prefill_items
+
+
+@pytest.mark.parametrize("spec", list(_doc_specs()), ids=lambda s: s.name)
+def test_shared_document_pages_and_build_list(spec):
+    """Shared document pages: distinct pages and the build list (the table page
+    slots that own a page, first use in table order) as the oracle assigns them."""
+    plan = sp.Plan(spec)
+    z = plan.sizes
+    _, first = OL.page_assignment(spec)
+    assert z.num_pages == OL.distinct_pages(spec) == len(first)
+    assert z.num_pages < OL.num_pages(spec)  # some pages are shared
+    t = plan.table_host()
+    assert list(t[z.table_len:z.table_len + z.num_pages]) == first
+    for l in range(spec.num_layers):
+        assert plan.stats(l)["pages"] == OL.distinct_pages(spec, l)
+
+
+def test_shared_document_validation():
+    spec = next(_doc_specs())
+    def rc(**kw):
+        try:
+            sp.Plan(replace(spec, **kw))
+            return 0
+        except sp.SegPagedError as e:
+            return e.status
+    assert rc() == 0
+    assert rc(doc_len=[300, 64, 299, 64, 0]) == -1      # members disagree on the length
+    assert rc(doc_len=[300, 64, 300, 65, 0]) == -1      # longer than a member's sequence
+    assert rc(doc_len=[300, 64, 300, 64, 3]) == -1      # a length without a group
+    assert rc(doc_group=[0, 1, 0, 1, 5]) == -1          # group id out of range
+    assert rc(doc_len=None) == -1                        # groups without lengths
+    d = replace(W.decode_form(spec), name="g")
+    with pytest.raises(sp.SegPagedError) as e:
+        sp.Plan(d, append_capacity=4)
+    assert e.value.status == -2                          # growth plans share nothing

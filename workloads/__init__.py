@@ -38,6 +38,9 @@ class Spec:
     retrieval           {(b, l, h): sorted unique int32 positions} for RETRIEVAL heads
     free_list           page ids in allocation order (None = identity)
     capacity_pages      pool capacity in pages the caller provides (0 = exactly what is needed)
+    doc_group[b]        document group of sequence b (-1 = none): sequences of one group
+                        begin with the same doc_len[b] tokens (None = no groups)
+    doc_len[b]          tokens of that shared document (equal within a group)
     """
 
     name: str
@@ -55,6 +58,8 @@ class Spec:
     free_list: Optional[np.ndarray] = None
     capacity_pages: int = 0
     seed: int = 0
+    doc_group: Optional[List[int]] = None
+    doc_len: Optional[List[int]] = None
 
     @property
     def num_seqs(self) -> int:
@@ -247,6 +252,19 @@ def kv_bits(spec: Spec, layer: int, seed: Optional[int] = None) -> Tuple[np.ndar
     for b, nb in enumerate(spec.seq_len):
         ks.append(_normal_bits((nb, hk, d), seed, _TAG_K, layer, b))
         vs.append(_normal_bits((nb, hk, d), seed, _TAG_V, layer, b))
+    if spec.doc_group is not None:
+        # a shared document: every member's first doc_len rows are the first
+        # member's (the same tokens at the same positions)
+        first = {}
+        for b, g in enumerate(spec.doc_group):
+            if g < 0:
+                continue
+            if g not in first:
+                first[g] = b
+                continue
+            c, b0 = spec.doc_len[b], first[g]
+            ks[b][:c] = ks[b0][:c]
+            vs[b][:c] = vs[b0][:c]
     return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
 
 
