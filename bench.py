@@ -735,7 +735,52 @@ def extra_configs(torch, W, sp, dev, stream, log, samples):
     res["decode_loop_append"] = decode_loop_append(torch, W, sp, dev, stream, log)
     res["chunked_prefill"] = chunked_prefill(torch, W, sp, dev, stream, log)
     res["retrieval_selection"] = retrieval_selection(torch, W, sp, dev, timed, log)
+    res["shared_document"] = shared_document(torch, W, sp, dev, timed, log)
     return res
+
+
+def shared_document(torch, W, sp, dev, timed, log):
+    """Sequences that begin with one shared document (the same tokens at the same
+    positions): the Llama-shaped decode, 8 layers x 8 sequences x 32768 tokens, all 8
+    sequences sharing their first 16384 tokens. The pool stores each page inside the
+    document once per (layer, KV head); decode reads every unit's pages as before.
+    Pool bytes against the same cache without sharing, build and decode time."""
+    from dataclasses import replace as _replace
+    n, c, L = 32768, 16384, 8
+    base = W.llama70b_decode(num_layers=L, n=n)
+    B, Hq, Hkv, D = base.num_seqs, base.num_q_heads, base.num_kv_heads, base.head_dim
+    spec = _replace(base, doc_group=[0] * B, doc_len=[c] * B)
+    plan = sp.Plan(spec)
+    own_pool = sp.Plan(base).sizes.pool_bytes
+    bufs = plan.allocate(dev)
+    k = W.randn_bf16_device((B * n, Hkv, D), spec.seed, W.TAG_K, 0, dev)
+    v = W.randn_bf16_device((B * n, Hkv, D), spec.seed, W.TAG_V, 0, dev)
+    kv = k.view(B, n, Hkv, D)
+    vv = v.view(B, n, Hkv, D)
+    kv[1:, :c] = kv[0, :c]  # the shared document: the same rows in every sequence
+    vv[1:, :c] = vv[0, :c]
+    bms = []
+    for l in range(L):
+        ms, _ = timed(lambda: sp.build(plan, l, k, v, bufs["table"], bufs["k_pool"],
+                                       bufs["v_pool"]), 3)
+        bms.append(ms)
+    q = W.randn_bf16_device((L, B, Hq, D), spec.seed, W.TAG_Q, 0, dev)
+    o = torch.empty_like(q)
+    med, _ = timed(lambda: sp.decode(plan, -1, q, bufs["table"], bufs["k_pool"], bufs["v_pool"],
+                                     1.0 / math.sqrt(D), o, workspace=bufs["workspace"]), 10)
+    kv_bytes = plan.stats(-1)["decode_tokens"] * 2 * D * 2
+    pool = plan.sizes.pool_bytes
+    log(f"shared document: pool {pool / 1e6:.0f} MB vs {own_pool / 1e6:.0f} MB unshared, "
+        f"decode {med:.3f} ms ({kv_bytes / (med * 1e-3) / 1e9:.0f} GB/s of K/V the rows see)")
+    del plan, bufs, k, v, q, o
+    torch.cuda.empty_cache()
+    return {"workload": f"llama70b-shaped decode {B} x {n} x {L} layers, every sequence "
+                        f"beginning with the same {c}-token document",
+            "pool_bytes_per_tensor": pool, "unshared_pool_bytes_per_tensor": own_pool,
+            "pool_saving": round(1 - pool / own_pool, 4),
+            "build_ms_per_layer": round(float(np.mean(bms)), 4),
+            "decode_ms": round(med, 4), "decode_kv_bytes_seen": kv_bytes,
+            "decode_gbs_of_keys_seen": round(kv_bytes / (med * 1e-3) / 1e9, 1)}
 
 
 def tiny_config(torch, W, sp, dev, timed, log, samples):

@@ -1203,7 +1203,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     for (int32_t j = 0; j < nfast; ++j) {
       // ---- MFMA phase (its operands were read before the barrier; waiting for
       // them here keeps the scalar loads below from being waited on mid-phase)
-      __builtin_amdgcn_s_setprio(1);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       SEGPAGED_QK_PV_STEP(0, kf, s, vf, pf);
       __builtin_amdgcn_sched_barrier(0);
@@ -1219,9 +1218,13 @@ __global__ __launch_bounds__(512) void prefill_kernel(
         SEGPAGED_ISSUE(j + NBUF - 1);
       }
       __builtin_amdgcn_sched_barrier(0);
-      // the other step pairs, with the cursors' scalar work in the MFMAs' shadow
+      // the other step pairs, with the cursors' scalar work in the MFMAs' shadow;
+      // each pair in issue order, so no two dependent QK MFMAs follow each other
 #pragma unroll
-      for (int ks = 1; ks < KSTEP / 2; ++ks) SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
+      for (int ks = 1; ks < KSTEP / 2; ++ks) {
+        SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (!SMALLP) {
         SEGPAGED_BLOCK_SOURCES(ic_pid);
@@ -1230,21 +1233,29 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = KSTEP / 2; ks < 3 * KSTEP / 4; ++ks) SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
+      for (int ks = KSTEP / 2; ks < 3 * KSTEP / 4; ++ks) {
+        SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       __builtin_amdgcn_sched_barrier(0);
       // mask parameters of block j + 1 for the softmax phase, then block j + 2's
       const int32_t c_pos = m_pos, c_rem = m_rem, c_flags = m_flags;
       SEGPAGED_MC_NEXT();
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 3 * KSTEP / 4; ks < KSTEP; ++ks) SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
+      for (int ks = 3 * KSTEP / 4; ks < KSTEP; ++ks) {
+        SEGPAGED_QK_PV_STEP(ks, kf, s, vf, pf);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // computed here, not sunk below the barrier; every MFMA issued before it
       pin_vgpr(s);
 #pragma unroll
       for (int md = 0; md < MD; ++md) pin_vgpr(oacc[md]);
-      __builtin_amdgcn_s_setprio(0);
       SEGPAGED_PHASE_END();
-      // ---- softmax phase: operand reads first, their latency under the exps
+      // ---- softmax phase: operand reads first, their latency under the exps. It
+      // is the longer phase, so its wave issues first (raised priority; measured
+      // +1.6% on the 128K layers over raising the MFMA phase's)
+      __builtin_amdgcn_s_setprio(1);
       SEGPAGED_LOAD_K((j + 2) % NBUF, kf);
       SEGPAGED_LOAD_V((j + 1) % NBUF, vf);
       if (!SMALLP && __builtin_expect(gathered, 0) && wave == 0)
@@ -1258,6 +1269,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
         }
         SEGPAGED_EXP(s, pf);
       }
+      __builtin_amdgcn_s_setprio(0);
       SEGPAGED_PHASE_END();
     }
     if (!late) SEGPAGED_PHASE_END();
