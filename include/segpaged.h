@@ -324,11 +324,12 @@ SEGPAGED_API int segpaged_import_pages(const segpaged_plan* plan, int32_t layer,
  *   lse   device fp32 [B][Hq] ([L][B][Hq]), or NULL
  *   workspace  device memory of at least decode_workspace_bytes (ENOSPACE otherwise)
  * Works on any plan form; a decode-form plan (q0 = N-1) stores only what the row sees.
- * A launch with fewer than 4096 items (one layer of a plan whose split was sized for
- * all its layers) deals each item's keys to up to 16 waves, each writing its own
- * partial, as long as a wave keeps >= 256 keys and workspace_bytes holds the extra
- * partials: the all-layer workspace of a plan of >= 16 layers holds them for any of
- * its layers. */
+ * A launch with fewer items than the device holds decode waves at once (2048 on an
+ * MI355X; one layer of a plan whose split was sized for all its layers) deals each
+ * item's keys to up to 16 waves, as many as fit in that one round, each writing its
+ * own partial, as long as a wave keeps >= 256 keys and workspace_bytes holds the
+ * extra partials: the all-layer workspace of a plan of >= 16 layers holds them for
+ * any of its layers. */
 SEGPAGED_API int segpaged_decode(const segpaged_plan* plan, int32_t layer, const void* q,
                                  const int32_t* d_table, const void* k_pool, const void* v_pool,
                                  float scale, void* o, float* lse, void* workspace,

@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256) void append_kernel(
 
 // ---------------------------------------------------------------------------
 // decode, split-K. One wave per part of a work item (unit, slots [lo, hi)), all
-// of which the decode row sees: an item's 32-slot steps are dealt to 2^sub_log2
+// of which the decode row sees: an item's 32-slot steps are dealt to nparts
 // consecutive parts (one part unless a launch has too few items to fill the
 // chip), each writing its own partial. Per 32-key step, with
 // v_mfma_f32_16x16x32_bf16:
@@ -222,33 +222,36 @@ __global__ __launch_bounds__(256) void append_kernel(
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
-    const int32_t* __restrict__ tab, int32_t off_units, int32_t off_pages, int32_t off_dec,
-    int32_t item_b, int32_t item_e, int32_t sub_log2, const uint16_t* __restrict__ q,
+    const int32_t* __restrict__ tab, int32_t off_pages, int32_t off_dec,
+    int32_t item_b, int32_t item_e, int32_t nparts, const uint16_t* __restrict__ q,
     int64_t q_layer_stride, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     float* __restrict__ ws, int32_t G, int32_t Hq, int32_t P, int32_t log2P, float c) {
   constexpr int KS = D / 32;  // k-steps of the QK^T contraction
   constexpr int DT = D / 16;  // 16-row tiles of O^T
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int32_t wid = (int32_t)blockIdx.x * 4 + wave;
-  const int32_t it = item_b + (wid >> sub_log2), part = wid & ((1 << sub_log2) - 1);
+  const int32_t it = item_b + wid / nparts, part = wid % nparts;
   if (it >= item_e) return;
-  const int32_t* item = tab + off_dec + kDecItemInts * it;
+  // the item record through the constant address space (scalar loads; the table
+  // is not written while a kernel runs): it carries the unit's fields, so the
+  // page ids are the next read
+  typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+  const cint_ptr item = (cint_ptr)(tab + off_dec + (int64_t)kDecItemInts * it);
   // slots [lo, hi) minus the gap [gap_lo, gap_hi): the zero tail of a sink page
   // between a local head's sink segment and its window segment
-  const int32_t u = item[0], gap_lo = item[3];
+  const int32_t gap_lo = item[3];
   int32_t lo = item[1], hi = item[2];
-  const int32_t* ur = tab + off_units + kUnitInts * u;
-  const int32_t b = ur[U_B], l = ur[U_L], h = ur[U_H];
-  const int32_t* pages = tab + off_pages + ur[U_PAGEOFF];
+  const int32_t b = item[4], l = item[5], h = item[6];
+  const int32_t* pages = tab + off_pages + item[7];
   const int n = lane & 15, g = lane >> 4;
   const int64_t PD = (int64_t)P * D;
   const int32_t gap_hi = gap_lo > 0 ? ((gap_lo + P - 1) >> log2P) << log2P : 0;
-  // this part's steps: the item's steps of 32 slots from lo & ~7, dealt in equal runs
+  // this part's steps: the item's steps of 32 slots from lo & ~7, dealt in runs
+  // whose lengths differ by at most one
   int32_t s_first = lo & ~7;
   {
     const int32_t nst = (hi - s_first + 31) >> 5;
-    const int32_t per = (nst + (1 << sub_log2) - 1) >> sub_log2;
-    const int32_t st0 = min(part * per, nst), st1 = min(st0 + per, nst);
+    const int32_t st0 = part * nst / nparts, st1 = (part + 1) * nst / nparts;
     hi = min(hi, s_first + 32 * st1);
     s_first += 32 * st0;
     lo = max(lo, s_first);
@@ -399,7 +402,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
   if (n < G) {  // a part without keys writes m = -inf, l = 0, O = 0
-    float* w = ws + ((((int64_t)(it - item_b) << sub_log2) + part) * G + n) * kWsStride<D>;
+    float* w = ws + (((int64_t)(it - item_b) * nparts + part) * G + n) * kWsStride<D>;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       *reinterpret_cast<f32x4*>(w + 16 * dt + 4 * g) = acc[dt];  // dims 16dt + 4g + i
@@ -413,52 +416,59 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 // Merge the item partials of each (unit, query head of its group) pair by their
 // log-sum-exp weights. WPP waves work on one pair (WPP = 1: four pairs per
 // workgroup; WPP = 4: one). Inside a wave, groups of D/4 lanes each take one
-// item (a float4 of O per lane), so a wave has 64/(D/4) items and, unrolled,
-// several times that many loads in flight: the partials are L2-resident and the
-// merge is bound by load latency, not bytes.
+// record (a float4 of O per lane, plus m and l) and fold it into a running max,
+// normaliser and O, so every record load is issued in one pass (four unrolled);
+// the partials are L2-resident and the merge is bound by load latency, not bytes.
+// The groups, then the waves of a pair, meet at their common max.
 template <int D, int WPP>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
-    const int32_t* __restrict__ tab, int32_t off_units, int32_t off_decunits, int32_t unit_b,
-    int32_t unit_e, int32_t item_b, int32_t sub_log2, const float* __restrict__ ws, int32_t G,
-    int32_t Hq, int32_t B, uint16_t* __restrict__ o, float* __restrict__ lse, int32_t all_layers) {
-  constexpr int LPI = D / 4;        // lanes per item
-  constexpr int IPW = 64 / LPI;     // items per wave at a time
-  constexpr int NS = IPW * WPP;     // items per pair at a time
+    const int32_t* __restrict__ tab, int32_t off_decunits, int32_t unit_b, int32_t unit_e,
+    int32_t item_b, int32_t nparts, const float* __restrict__ ws, int32_t G, int32_t Hq,
+    int32_t B, uint16_t* __restrict__ o, float* __restrict__ lse, int32_t all_layers) {
+  constexpr int LPI = D / 4;        // lanes per record
+  constexpr int IPW = 64 / LPI;     // records per wave at a time
+  constexpr int NS = IPW * WPP;     // records per pair at a time
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wp = wave % WPP;        // wave within its pair
   const int64_t idx = (int64_t)blockIdx.x * (4 / WPP) + wave / WPP;
   const int64_t u = unit_b + idx / G;
   const int j = (int)(idx % G);
   if (u >= unit_e) return;          // uniform over the waves of a pair
-  const int32_t* ur = tab + off_units + kUnitInts * u;
-  const int32_t b = ur[U_B], l = ur[U_L], h = ur[U_H];
-  // the unit's partial records: 2^sub_log2 per item
-  const int32_t ib = (tab[off_decunits + 2 * u] - item_b) << sub_log2;
-  const int32_t ie = (tab[off_decunits + 2 * u + 1] - item_b) << sub_log2;
-  const int64_t row = (all_layers ? (int64_t)l * B * Hq : 0) + (int64_t)b * Hq + h * G + j;
-  // record of (item it, query column j): D floats of O, then m (log2 units) and l
+  // the unit's record: item range, first output row within its layer, layer
+  const int32_t* du = tab + off_decunits + (int64_t)kDecUnitInts * u;
+  const int32_t ib = (du[0] - item_b) * nparts, ie = (du[1] - item_b) * nparts;  // nparts per item
+  const int64_t row = (all_layers ? (int64_t)du[3] * B * Hq : 0) + du[2] + j;
+  // record of (item part t, query column j): D floats of O, then m (log2 units) and l
   const float* rec0 = ws + ((int64_t)ib * G + j) * kWsStride<D>;
   const int64_t rstride = (int64_t)G * kWsStride<D>;
-  // the unit's max over its items, one item per lane (every wave of the pair alike)
-  float m = -INFINITY;
-  for (int32_t t = lane; t < ie - ib; t += 64) m = fmaxf(m, rec0[t * rstride + D]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  float m = -INFINITY, lsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float lsum = 0.f;
-  if (m != -INFINITY) {
+  {
     const int slot = wp * IPW + lane / LPI, d0 = 4 * (lane % LPI);
 #pragma unroll 4
     for (int32_t t = slot; t < ie - ib; t += NS) {
       const float* w = rec0 + t * rstride;
       const f32x4 v = *reinterpret_cast<const f32x4*>(w + d0);
       const float2 ml = *reinterpret_cast<const float2*>(w + D);
-      const float sc = fast_exp2(ml.x - m);
-      lsum += ml.y * sc;
-      acc += v * sc;
+      // a part without keys (m = -inf, l = 0, O = 0) adds nothing
+      const float m_new = fmaxf(m, ml.x);
+      const float s_old = m_new == m ? 1.f : fast_exp2(m - m_new);  // m = -inf: 0
+      const float s_new = ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - m_new);
+      acc = acc * s_old + v * s_new;
+      lsum = lsum * s_old + ml.y * s_new;
+      m = m_new;
     }
   }
-  // the wave's item groups
+  // the wave's record groups at their common max
+  {
+    float mw = m;
+#pragma unroll
+    for (int off = LPI; off < 64; off <<= 1) mw = fmaxf(mw, __shfl_xor(mw, off, 64));
+    const float f = m == -INFINITY ? 0.f : fast_exp2(m - mw);
+    acc *= f;
+    lsum *= f;
+    m = mw;
+  }
 #pragma unroll
   for (int off = LPI; off < 64; off <<= 1) {
     lsum += __shfl_xor(lsum, off, 64);
@@ -467,16 +477,23 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   }
   if constexpr (WPP > 1) {
     __shared__ f32x4 sAcc[WPP][LPI];
-    __shared__ float sL[WPP];
+    __shared__ float sL[WPP], sM[WPP];
     if (lane < LPI) sAcc[wp][lane] = acc;
-    if (lane == 0) sL[wp] = lsum;
+    if (lane == 0) { sL[wp] = lsum; sM[wp] = m; }
     __syncthreads();
     if (wp != 0) return;
-    if (lane < LPI)
+    float mp = sM[0];
 #pragma unroll
-      for (int w2 = 1; w2 < WPP; ++w2) acc += sAcc[w2][lane];
+    for (int w2 = 1; w2 < WPP; ++w2) mp = fmaxf(mp, sM[w2]);
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    lsum = 0.f;
 #pragma unroll
-    for (int w2 = 1; w2 < WPP; ++w2) lsum += sL[w2];
+    for (int w2 = 0; w2 < WPP; ++w2) {
+      const float f = sM[w2] == -INFINITY ? 0.f : fast_exp2(sM[w2] - mp);
+      if (lane < LPI) acc += sAcc[w2][lane] * f;
+      lsum += sL[w2] * f;
+    }
+    m = mp;
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   if (lane < LPI) {
@@ -1391,6 +1408,26 @@ int device_cus() {
   return n;
 }
 
+// Waves of decode_partial_kernel<D> the current device holds at once (its
+// resident workgroups per compute unit x 4 waves x compute units; cached per
+// device id; at least 4).
+int64_t decode_resident_waves(int D) {
+  static int cached[64][2] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 4;
+  int& c = cached[dev][D == 128 ? 1 : 0];
+  if (c == 0) {
+    int per_cu = 0;
+    const hipError_t e =
+        D == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                       &per_cu, reinterpret_cast<const void*>(&decode_partial_kernel<128>), 256, 0)
+                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                       &per_cu, reinterpret_cast<const void*>(&decode_partial_kernel<64>), 256, 0);
+    c = std::max(1, e == hipSuccess ? per_cu : 1) * 4 * std::max(device_cus(), 1);
+  }
+  return c;
+}
+
 int check_launch() {
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? SEGPAGED_OK : SEGPAGED_EHIP;
@@ -1438,8 +1475,8 @@ int upload_layer_table(const segpaged_plan* pl, int32_t layer, int32_t* d_table,
   if ((rc = upload(pl, d_table, pl->off_pages + sp.page_b, sp.page_e - sp.page_b, st))) return rc;
   if ((rc = upload(pl, d_table, pl->off_retr + sp.retr_b, sp.retr_e - sp.retr_b, st))) return rc;
   if ((rc = upload(pl, d_table, pl->off_bld + sp.bld_b, sp.bld_e - sp.bld_b, st))) return rc;
-  if ((rc = upload(pl, d_table, pl->off_decunits + 2 * sp.unit_b, 2 * (sp.unit_e - sp.unit_b),
-                   st)))
+  if ((rc = upload(pl, d_table, pl->off_decunits + kDecUnitInts * sp.unit_b,
+                   kDecUnitInts * (sp.unit_e - sp.unit_b), st)))
     return rc;
   if ((rc = upload(pl, d_table, pl->off_dec + kDecItemInts * sp.dec_b,
                    kDecItemInts * (sp.dec_e - sp.dec_b), st)))
@@ -1680,16 +1717,19 @@ SEGPAGED_API int segpaged_decode(const segpaged_plan* pl, int32_t layer, const v
   const int64_t need = nitems * rec_bytes;
   if (need > 0 && (!workspace || !aligned16(workspace))) return SEGPAGED_EINVAL;
   if (workspace_bytes < need) return SEGPAGED_ENOSPACE;
-  // Parts per item: a launch with too few items to fill the chip (one layer of a
-  // plan whose split was sized for all layers) deals each item's steps to up to
-  // 16 waves, while a part keeps >= 256 keys and the workspace holds the partials.
-  int sub_log2 = 0;
-  {
+  // Parts per item: a launch with fewer items than the chip holds waves at once
+  // (one layer of a plan whose split was sized for all layers) deals each item's
+  // steps to up to 16 waves, as many as fit in one round of resident waves, while
+  // a part keeps >= 256 keys and the workspace holds the partials. A second round
+  // of short waves would cost more than it spreads.
+  int64_t nparts = 1;
+  if (nitems > 0) {
     const int64_t keys = layer < 0 ? pl->total.decode_tokens : pl->stats[layer].decode_tokens;
     const int64_t recs = workspace_bytes / rec_bytes;
-    while (nitems > 0 && sub_log2 < kDecMaxPartsLog2 && (nitems << sub_log2) < kDecFillWaves &&
-           (nitems << (sub_log2 + 1)) <= recs && keys / (nitems << (sub_log2 + 1)) >= 256)
-      ++sub_log2;
+    const int64_t resident = decode_resident_waves(pl->D);
+    nparts = std::min<int64_t>({kDecMaxParts, resident / nitems, recs / nitems,
+                                keys / (nitems * 256)});
+    nparts = std::max<int64_t>(nparts, 1);
   }
   const int64_t nunits = sp.unit_e - sp.unit_b;
   if (nunits == 0) return SEGPAGED_OK;
@@ -1701,16 +1741,16 @@ SEGPAGED_API int segpaged_decode(const segpaged_plan* pl, int32_t layer, const v
   auto* vpp = (const uint16_t*)v_pool;
   auto* ws = (float*)workspace;
   if (nitems > 0) {
-    const dim3 grid((unsigned)(((nitems << sub_log2) + 3) / 4)), block(256);
+    const dim3 grid((unsigned)((nitems * nparts + 3) / 4)), block(256);
     if (pl->D == 128)
       hipLaunchKernelGGL(decode_partial_kernel<128>, grid, block, 0, st, d_table,
-                         (int32_t)pl->off_units, (int32_t)pl->off_pages, (int32_t)pl->off_dec,
-                         (int32_t)sp.dec_b, (int32_t)sp.dec_e, sub_log2, qq, qstride, kpp, vpp,
+                         (int32_t)pl->off_pages, (int32_t)pl->off_dec,
+                         (int32_t)sp.dec_b, (int32_t)sp.dec_e, (int32_t)nparts, qq, qstride, kpp, vpp,
                          ws, pl->G, pl->Hq, pl->P, pl->log2P, c);
     else
       hipLaunchKernelGGL(decode_partial_kernel<64>, grid, block, 0, st, d_table,
-                         (int32_t)pl->off_units, (int32_t)pl->off_pages, (int32_t)pl->off_dec,
-                         (int32_t)sp.dec_b, (int32_t)sp.dec_e, sub_log2, qq, qstride, kpp, vpp,
+                         (int32_t)pl->off_pages, (int32_t)pl->off_dec,
+                         (int32_t)sp.dec_b, (int32_t)sp.dec_e, (int32_t)nparts, qq, qstride, kpp, vpp,
                          ws, pl->G, pl->Hq, pl->P, pl->log2P, c);
     int rc = check_launch();
     if (rc) return rc;
@@ -1718,14 +1758,14 @@ SEGPAGED_API int segpaged_decode(const segpaged_plan* pl, int32_t layer, const v
   // Four waves per pair when some unit has many items and the pairs alone leave
   // the chip short of waves (under 64 per CU); otherwise four pairs per workgroup.
   const int64_t pairs = nunits * pl->G;
-  const int wpp = (sp.max_unit_items << sub_log2) > 16 && pairs < 64 * 256 ? 4 : 1;
+  const int wpp = sp.max_unit_items * nparts > 16 && pairs < 64 * 256 ? 4 : 1;
   const int64_t per_wg = 4 / wpp;
   const dim3 grid((unsigned)((pairs + per_wg - 1) / per_wg)), block(256);
   auto* oo = (uint16_t*)o;
 #define SEGPAGED_LAUNCH_COMBINE(DD, WW)                                                          \
   hipLaunchKernelGGL((decode_combine_kernel<DD, WW>), grid, block, 0, st, d_table,               \
-                     (int32_t)pl->off_units, (int32_t)pl->off_decunits, (int32_t)sp.unit_b,     \
-                     (int32_t)sp.unit_e, (int32_t)sp.dec_b, sub_log2, ws, pl->G, pl->Hq, pl->B, \
+                     (int32_t)pl->off_decunits, (int32_t)sp.unit_b, (int32_t)sp.unit_e,         \
+                     (int32_t)sp.dec_b, (int32_t)nparts, ws, pl->G, pl->Hq, pl->B,              \
                      oo, lse,                                                                   \
                      (int32_t)(layer < 0))
   if (pl->D == 128) {

@@ -25,7 +25,12 @@ enum UnitField {
 };
 
 // Work lists that follow the table in the device image.
-constexpr int kDecItemInts = 4;   // unit, slot_lo, slot_hi, 0
+// decode item: unit, slot_lo, slot_hi, gap_lo (0: none), then the unit's b, l, h and
+// page_off, so a wave reads one record before its page ids
+constexpr int kDecItemInts = 8;
+// decode unit: first item, end item, the unit's first output row within its layer
+// (b * Hq + h * G), layer
+constexpr int kDecUnitInts = 4;
 constexpr int kPreItemInts = 2;   // unit, first query position of the tile | kPrecise
 // Prefill tiles whose first row sees fewer keys than this take the precise path
 // (softmax weights as a sum of two bf16 terms); bit 31 of the item's row marks them.
@@ -37,8 +42,7 @@ constexpr int kMaxGroup = 16;     // Q heads per KV head the decode kernel suppo
 constexpr int kSelChunk = 2048;   // keys per workgroup of the top-p masses and first radix pass
 constexpr int kCtrInts = 16;      // prefill work counter line per layer (+1 for all layers);
                                   // its first 8 bytes: (launch generation << 32) | next item
-constexpr int kDecMaxPartsLog2 = 4;     // a decode item is dealt to at most 16 waves
-constexpr int64_t kDecFillWaves = 4096; // decode waves a launch aims for (16 per compute unit)
+constexpr int64_t kDecMaxParts = 16;     // a decode item is dealt to at most 16 waves
 constexpr int64_t kNoAllocScratchBytes = SEGPAGED_NOALLOC_SCRATCH_BYTES;  // see segpaged.h
 
 struct LayerRange {

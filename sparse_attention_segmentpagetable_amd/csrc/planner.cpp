@@ -170,7 +170,7 @@ void make_work_lists(const segpaged_plan* pl, const int32_t* unit_recs, WorkList
   const int32_t* t = pl->buf.data();
   const int64_t B = pl->B, L = pl->L, Hkv = pl->Hkv, P = pl->P, U = pl->num_units;
   const int64_t split = pl->split, BQ = kPrefillRows / pl->G;
-  wl.decunits.assign(2 * U, 0);
+  wl.decunits.assign(kDecUnitInts * U, 0);
   wl.dec.clear();
   wl.pre.clear();
   wl.ranges.assign(L, LayerRange{});
@@ -205,8 +205,15 @@ void make_work_lists(const segpaged_plan* pl, const int32_t* unit_recs, WorkList
       }
 
       // decode items: visible slot ranges of row n - 1, cut into <= split keys
-      int32_t* du = &wl.decunits[2 * u];
+      int32_t* du = &wl.decunits[kDecUnitInts * u];
       du[0] = (int32_t)wl.n_dec();
+      du[2] = r[U_B] * (int32_t)pl->Hq + r[U_H] * (int32_t)pl->G;
+      du[3] = r[U_L];
+      auto push_item = [&](int64_t unit, int64_t lo, int64_t hi, int64_t gap) {
+        const int32_t rec[kDecItemInts] = {(int32_t)unit, (int32_t)lo, (int32_t)hi, (int32_t)gap,
+                                           r[U_B], r[U_L], r[U_H], r[U_PAGEOFF]};
+        wl.dec.insert(wl.dec.end(), rec, rec + kDecItemInts);
+      };
       SlotRange rr[4];
       const int nr = decode_ranges(eff, sink, win, n, sg, ns, P, rr);
       for (int k = 0; k < nr; ++k) st.decode_tokens += rr[k].hi - rr[k].lo;
@@ -216,19 +223,13 @@ void make_work_lists(const segpaged_plan* pl, const int32_t* unit_recs, WorkList
         // a short first range (a sink) and a range starting on the next page: one
         // item covers both, the zero tail of the first range's last page is a gap
         const int64_t hi0 = std::min(rr[1].lo + split, rr[1].hi);
-        wl.dec.push_back((int32_t)u);
-        wl.dec.push_back((int32_t)rr[0].lo);
-        wl.dec.push_back((int32_t)hi0);
-        wl.dec.push_back((int32_t)rr[0].hi);
+        push_item(u, rr[0].lo, hi0, rr[0].hi);
         rr[1].lo = hi0;
         k0 = 1;
       }
       for (int k = k0; k < nr; ++k) {
         for (int64_t lo = rr[k].lo; lo < rr[k].hi; lo += split) {
-          wl.dec.push_back((int32_t)u);
-          wl.dec.push_back((int32_t)lo);
-          wl.dec.push_back((int32_t)std::min(lo + split, rr[k].hi));
-          wl.dec.push_back(0);
+          push_item(u, lo, std::min(lo + split, rr[k].hi), 0);
         }
       }
       du[1] = (int32_t)wl.n_dec();
@@ -593,7 +594,7 @@ SEGPAGED_API int segpaged_plan_create(const segpaged_spec* spec, segpaged_plan**
   pl->dec_cap = grow ? std::max<int64_t>(dec_cap, wl.n_dec()) : wl.n_dec();
   pl->pre_cap = grow ? std::max<int64_t>(U * ceil_div(chunk, kPrefillRows / G), wl.n_pre())
                      : wl.n_pre();
-  pl->off_dec = pl->off_decunits + 2 * U;
+  pl->off_dec = pl->off_decunits + kDecUnitInts * U;
   pl->off_pre = pl->off_dec + kDecItemInts * pl->dec_cap;
   // counter lines 16-byte aligned in the image (64-bit atomics)
   pl->off_ctr = (pl->off_pre + kPreItemInts * pl->pre_cap + 3) / 4 * 4;

@@ -11,6 +11,7 @@ import pytest
 import workloads as W
 from oracle import attention as OA
 from oracle import layout as OL
+from tests.table_image import work_lists
 
 sp = pytest.importorskip("sparse_attention_segmentpagetable_amd")
 
@@ -115,10 +116,7 @@ def test_decode_items_cover_visible_keys_after_appends():
         n = [a + x for a, x in zip(n, add)]
         t = plan.table_host()
         z = plan.sizes
-        U = z.num_units
-        w0 = z.table_len + z.num_pages  # work lists follow the build list
-        du = t[w0:w0 + 2 * U].reshape(U, 2)
-        items = t[w0 + 2 * U:w0 + 2 * U + 4 * z.decode_items].reshape(-1, 4)
+        du, items, _, _ = work_lists(t, z, spec.group, spec.num_q_heads)
         P = spec.page_size
         for (u, b, l, h) in OL.units(spec):
             kind, _, _ = spec.head_class(l, h)

@@ -13,6 +13,7 @@ import pytest
 import workloads as W
 from oracle import attention as OA
 from oracle import layout as OL
+from tests.table_image import DI_INTS, DU_INTS, PI_INTS, work_lists
 from tests.random_specs import random_spec
 
 sp = pytest.importorskip("sparse_attention_segmentpagetable_amd")
@@ -99,16 +100,11 @@ def test_stats_vs_bruteforce(spec):
     assert tot["retained_tokens"] == OL.kv_len_total(spec)
 
 
-def _decode_items(plan):
+def _decode_items(plan, spec):
     t = plan.table_host()
     z = plan.sizes
-    U = z.num_units
-    w0 = z.table_len + z.num_pages  # work lists follow the build list
-    du = t[w0:w0 + 2 * U].reshape(U, 2)
-    items = t[w0 + 2 * U:w0 + 2 * U + 4 * z.decode_items].reshape(-1, 4)
-    p0 = w0 + 2 * U + 4 * z.decode_items
-    pre = t[p0:p0 + 2 * z.prefill_items].reshape(-1, 2)
-    assert np.all(t[p0 + 2 * z.prefill_items:] == 0)  # work counters start at zero
+    du, items, pre, end = work_lists(t, z, spec.group, spec.num_q_heads)
+    assert np.all(t[end:] == 0)  # work counters start at zero
     return t, du, items, pre
 
 
@@ -116,7 +112,7 @@ def _decode_items(plan):
 @pytest.mark.parametrize("split", [0, 64, 192])
 def test_decode_items_cover_visible_keys_once(spec, split):
     plan = sp.Plan(spec, decode_split_tokens=split)
-    t, du, items, _ = _decode_items(plan)
+    t, du, items, _ = _decode_items(plan, spec)
     P = spec.page_size
     for (u, b, l, h) in OL.units(spec):
         n = spec.seq_len[b]
@@ -145,7 +141,7 @@ def test_decode_items_cover_visible_keys_once(spec, split):
 @pytest.mark.parametrize("spec", list(_specs()), ids=lambda s: f"{s.name}")
 def test_prefill_items_tile_every_row_once(spec):
     plan = sp.Plan(spec)
-    _, _, _, pre = _decode_items(plan)
+    _, _, _, pre = _decode_items(plan, spec)
     G = spec.group
     bq = 256 // G
     got = {}
@@ -336,7 +332,8 @@ def test_counter_lines_aligned_and_zero(spec, cap):
     c0 = c1 - 16 * (spec.num_layers + 1)
     assert c0 % 4 == 0 and np.all(t[c0:c1] == 0)
     z = plan.sizes
-    assert c0 >= z.table_len + 2 * z.num_units + 4 * z.decode_items + 2 * z.prefill_items
+    assert c0 >= (z.table_len + DU_INTS * z.num_units + DI_INTS * z.decode_items
+                  + PI_INTS * z.prefill_items)
 
 
 @pytest.mark.parametrize("spec", list(_doc_specs()), ids=lambda s: s.name)
