@@ -455,3 +455,76 @@ def test_prefill_work_counter_left_raised():
         parity(to_f64(o), ref, "prefill back to back")
         gens.append(int(table[off_ctr + 1].item()))
     assert len(set(gens)) == len(gens)
+
+
+def test_graph_replay_of_prefill_and_decode():
+    """HIP graphs captured from segpaged_prefill and segpaged_decode replay the
+    captured calls exactly. The captured prefill launch keeps the generation it was
+    given at capture; its last work-counter fetch leaves (generation, 0) for the next
+    replay, and an eager call on the same counter line in between (another
+    generation) is claimed over. Every replay is compared bit for bit with the eager
+    result, with eager work and synchronisations between the replays."""
+    scale = 1 / np.sqrt(128)
+    spec = _long_mixed("prefill")
+    plan = sp.Plan(spec)
+    bufs = plan.allocate(DEV)
+    kb, vb = W.kv_bits(spec, 0)
+    qb = W.q_bits(spec, 0)
+    table, kpool, vpool = bufs["table"], bufs["k_pool"], bufs["v_pool"]
+    sp.build(plan, 0, to_dev(kb), to_dev(vb), table, kpool, vpool)
+    q = to_dev(qb)
+    o_ref = torch.empty_like(q)
+    lse_ref = torch.empty(q.shape[:2], dtype=torch.float32, device=DEV)
+    sp.prefill(plan, 0, q, table, kpool, vpool, scale, o_ref, lse_ref)
+    torch.cuda.synchronize()
+    ref, ref_lse = OA.attention(spec, 0, qb, kb, vb)
+    parity(to_f64(o_ref), ref, "prefill eager before graph")
+    lse_parity(lse_ref.cpu().numpy(), ref_lse, "prefill eager before graph")
+
+    o_g = torch.empty_like(q)
+    lse_g = torch.empty_like(lse_ref)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sp.prefill(plan, 0, q, table, kpool, vpool, scale, o_g, lse_g)
+    torch.cuda.synchronize()
+    off_ctr = counter_lines(plan)[0]
+    for step, eager_between in enumerate([False, True, False, True]):
+        o_g.fill_(float("nan"))
+        lse_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(o_g), to_bits(o_ref)), f"prefill replay {step}"
+        assert np.array_equal(lse_g.cpu().numpy().view(np.int32), lse_ref.cpu().numpy().view(np.int32)), step
+        assert int(table[off_ctr].item()) == 0  # (generation, 0) after the replay
+        if eager_between:
+            o_e = torch.full_like(q, float("nan"))
+            sp.prefill(plan, 0, q, table, kpool, vpool, scale, o_e)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_bits(o_e), to_bits(o_ref)), f"prefill eager after replay {step}"
+    del graph
+
+    dspec = W.decode_form(spec)
+    dplan = sp.Plan(dspec)
+    dbufs = dplan.allocate(DEV)
+    sp.build(dplan, 0, to_dev(kb), to_dev(vb), dbufs["table"], dbufs["k_pool"], dbufs["v_pool"])
+    dq = to_dev(W.q_bits(dspec, 0))
+    args = (dbufs["table"], dbufs["k_pool"], dbufs["v_pool"], scale)
+    od_ref = torch.empty_like(dq)
+    sp.decode(dplan, 0, dq, *args, od_ref, workspace=dbufs["workspace"])
+    torch.cuda.synchronize()
+    od_g = torch.empty_like(dq)
+    dgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(dgraph):
+        sp.decode(dplan, 0, dq, *args, od_g, workspace=dbufs["workspace"])
+    torch.cuda.synchronize()
+    for step in range(3):
+        od_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        dgraph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(od_g), to_bits(od_ref)), f"decode replay {step}"
+        o_e = torch.empty_like(dq)
+        sp.decode(dplan, 0, dq, *args, o_e, workspace=dbufs["workspace"])
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(o_e), to_bits(od_ref)), f"decode eager after replay {step}"
