@@ -1396,15 +1396,19 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 inline bool aligned8(const void* p) { return ((uintptr_t)p & 7u) == 0; }
 
-// Compute units of the current device (cached per device id; 0 on error).
+// Compute units of the current device (cached per device id; 0 on error). The
+// caches are atomics: host threads may call on one device at once.
 int device_cus() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev >= 0 && dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64) cached[dev] = n;
+  if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -1412,10 +1416,11 @@ int device_cus() {
 // resident workgroups per compute unit x 4 waves x compute units; cached per
 // device id; at least 4).
 int64_t decode_resident_waves(int D) {
-  static int cached[64][2] = {};
+  static std::atomic<int> cached[64][2] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 4;
-  int& c = cached[dev][D == 128 ? 1 : 0];
+  std::atomic<int>& slot = cached[dev][D == 128 ? 1 : 0];
+  int c = slot.load(std::memory_order_relaxed);
   if (c == 0) {
     int per_cu = 0;
     const hipError_t e =
@@ -1424,6 +1429,7 @@ int64_t decode_resident_waves(int D) {
                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(
                        &per_cu, reinterpret_cast<const void*>(&decode_partial_kernel<64>), 256, 0);
     c = std::max(1, e == hipSuccess ? per_cu : 1) * 4 * std::max(device_cus(), 1);
+    slot.store(c, std::memory_order_relaxed);
   }
   return c;
 }
