@@ -120,7 +120,8 @@ typedef struct {
   int64_t kv_rows;          /* T_total = sum_b N_b: rows of one layer's dense K / V */
   int64_t decode_items;     /* decode work items, all layers */
   int64_t prefill_items;    /* prefill work items, all layers */
-  int64_t decode_workspace_bytes;  /* workspace a decode call over all layers needs */
+  int64_t decode_workspace_bytes;  /* workspace for any decode call of the plan, with room
+                                      for the extra partials of shared items (see decode) */
   int64_t prefill_workspace_bytes; /* workspace a prefill call needs (0 in this version) */
   int64_t select_workspace_bytes;  /* workspace segpaged_select_topp needs (largest lengths) */
 } segpaged_sizes;
@@ -322,14 +323,18 @@ SEGPAGED_API int segpaged_import_pages(const segpaged_plan* plan, int32_t layer,
  *   q     device bf16 [B][Hq][D] ([L][B][Hq][D] when layer = -1)
  *   o     device bf16, same shape (written)
  *   lse   device fp32 [B][Hq] ([L][B][Hq]), or NULL
- *   workspace  device memory of at least decode_workspace_bytes (ENOSPACE otherwise)
+ *   workspace  device memory for the call's partials: one record of G * (D + 4) floats
+ *              per item of the call at least (ENOSPACE otherwise); decode_workspace_bytes
+ *              is enough for any call of the plan
  * Works on any plan form; a decode-form plan (q0 = N-1) stores only what the row sees.
- * A launch with fewer items than the device holds decode waves at once (2048 on an
- * MI355X; one layer of a plan whose split was sized for all its layers) deals each
- * item's keys to up to 16 waves, as many as fit in that one round, each writing its
- * own partial, as long as a wave keeps >= 256 keys and workspace_bytes holds the
- * extra partials: the all-layer workspace of a plan of >= 16 layers holds them for
- * any of its layers. */
+ * Items may be shared by several waves, each writing its own partial, as long as a
+ * wave keeps >= 256 keys and workspace_bytes holds the extra partials. A launch with
+ * fewer items than the device holds decode waves at once (2048 on an MI355X; one
+ * layer of a plan whose split was sized for all its layers) deals each item's keys
+ * to up to 16 waves, as many as fit in that one round: the all-layer workspace of a
+ * plan of >= 16 layers holds them for any of its layers. A launch of several rounds
+ * deals its last items, one round of waves' worth (up to 512), to 4 waves each, so
+ * that it ends on short waves; decode_workspace_bytes includes those 1536 partials. */
 SEGPAGED_API int segpaged_decode(const segpaged_plan* plan, int32_t layer, const void* q,
                                  const int32_t* d_table, const void* k_pool, const void* v_pool,
                                  float scale, void* o, float* lse, void* workspace,

@@ -208,11 +208,23 @@ __global__ __launch_bounds__(256) void append_kernel(
     vpage[((int64_t)(ts >> 3) * D + d) * 8 + (ts & 7)] = vn[src + d];
 }
 
+// How a decode launch deals its items to waves: the first `head` items to `nh`
+// consecutive waves each, the others to `nt` each. Partial records follow the
+// wave order, so record = wave index.
+struct DecParts {
+  int32_t head, nh, nt;
+  // waves (and records) of the launch's items [0, i)
+  __host__ __device__ int32_t waves_before(int32_t i) const {
+    return i <= head ? i * nh : head * nh + (i - head) * nt;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // decode, split-K. One wave per part of a work item (unit, slots [lo, hi)), all
-// of which the decode row sees: an item's 32-slot steps are dealt to nparts
-// consecutive parts (one part unless a launch has too few items to fill the
-// chip), each writing its own partial. Per 32-key step, with
+// of which the decode row sees: an item's 32-slot steps are dealt to its parts
+// (one part unless a launch has too few items to fill the chip, or the item is
+// among the last of a launch of several rounds, see DecParts), each writing its
+// own partial. Per 32-key step, with
 // v_mfma_f32_16x16x32_bf16:
 //   S^T[16 keys][16 cols] = K[keys][D] . Q^T[D][cols]   (cols = the G query heads)
 //   O^T[16 dims][16 cols] += V^T[dims][32 keys] . P^T[32 keys][cols]
@@ -223,14 +235,23 @@ __global__ __launch_bounds__(256) void append_kernel(
 template <int D>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
     const int32_t* __restrict__ tab, int32_t off_pages, int32_t off_dec,
-    int32_t item_b, int32_t item_e, int32_t nparts, const uint16_t* __restrict__ q,
+    int32_t item_b, int32_t item_e, DecParts dp, const uint16_t* __restrict__ q,
     int64_t q_layer_stride, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     float* __restrict__ ws, int32_t G, int32_t Hq, int32_t P, int32_t log2P, float c) {
   constexpr int KS = D / 32;  // k-steps of the QK^T contraction
   constexpr int DT = D / 16;  // 16-row tiles of O^T
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int32_t wid = (int32_t)blockIdx.x * 4 + wave;
-  const int32_t it = item_b + wid / nparts, part = wid % nparts;
+  int32_t rel, part, np;  // item within the launch, its part, its parts
+  {
+    const int32_t hw = dp.head * dp.nh;
+    if (wid < hw) {
+      rel = wid / dp.nh; part = wid % dp.nh; np = dp.nh;
+    } else {
+      rel = dp.head + (wid - hw) / dp.nt; part = (wid - hw) % dp.nt; np = dp.nt;
+    }
+  }
+  const int32_t it = item_b + rel;
   if (it >= item_e) return;
   // the item record through the constant address space (scalar loads; the table
   // is not written while a kernel runs): it carries the unit's fields, so the
@@ -251,7 +272,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   int32_t s_first = lo & ~7;
   {
     const int32_t nst = (hi - s_first + 31) >> 5;
-    const int32_t st0 = part * nst / nparts, st1 = (part + 1) * nst / nparts;
+    const int32_t st0 = part * nst / np, st1 = (part + 1) * nst / np;
     hi = min(hi, s_first + 32 * st1);
     s_first += 32 * st0;
     lo = max(lo, s_first);
@@ -402,7 +423,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
   if (n < G) {  // a part without keys writes m = -inf, l = 0, O = 0
-    float* w = ws + (((int64_t)(it - item_b) * nparts + part) * G + n) * kWsStride<D>;
+    float* w = ws + ((int64_t)wid * G + n) * kWsStride<D>;  // record = wave
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       *reinterpret_cast<f32x4*>(w + 16 * dt + 4 * g) = acc[dt];  // dims 16dt + 4g + i
@@ -423,7 +444,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 template <int D, int WPP>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const int32_t* __restrict__ tab, int32_t off_decunits, int32_t unit_b, int32_t unit_e,
-    int32_t item_b, int32_t nparts, const float* __restrict__ ws, int32_t G, int32_t Hq,
+    int32_t item_b, DecParts dp, const float* __restrict__ ws, int32_t G, int32_t Hq,
     int32_t B, uint16_t* __restrict__ o, float* __restrict__ lse, int32_t all_layers) {
   constexpr int LPI = D / 4;        // lanes per record
   constexpr int IPW = 64 / LPI;     // records per wave at a time
@@ -436,7 +457,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   if (u >= unit_e) return;          // uniform over the waves of a pair
   // the unit's record: item range, first output row within its layer, layer
   const int32_t* du = tab + off_decunits + (int64_t)kDecUnitInts * u;
-  const int32_t ib = (du[0] - item_b) * nparts, ie = (du[1] - item_b) * nparts;  // nparts per item
+  const int32_t ib = dp.waves_before(du[0] - item_b), ie = dp.waves_before(du[1] - item_b);
   const int64_t row = (all_layers ? (int64_t)du[3] * B * Hq : 0) + du[2] + j;
   // record of (item part t, query column j): D floats of O, then m (log2 units) and l
   const float* rec0 = ws + ((int64_t)ib * G + j) * kWsStride<D>;
@@ -1723,19 +1744,28 @@ SEGPAGED_API int segpaged_decode(const segpaged_plan* pl, int32_t layer, const v
   const int64_t need = nitems * rec_bytes;
   if (need > 0 && (!workspace || !aligned16(workspace))) return SEGPAGED_EINVAL;
   if (workspace_bytes < need) return SEGPAGED_ENOSPACE;
-  // Parts per item: a launch with fewer items than the chip holds waves at once
-  // (one layer of a plan whose split was sized for all layers) deals each item's
-  // steps to up to 16 waves, as many as fit in one round of resident waves, while
-  // a part keeps >= 256 keys and the workspace holds the partials. A second round
-  // of short waves would cost more than it spreads.
-  int64_t nparts = 1;
+  // Parts per item, while a part keeps >= 256 keys and the workspace holds the
+  // partials. A launch with fewer items than the chip holds waves at once (one
+  // layer of a plan whose split was sized for all layers) deals each item's steps
+  // to up to 16 waves, as many as fit in one round of resident waves (a second
+  // round of short waves would cost more than it spreads). A launch of several
+  // rounds deals its last items, one round of waves' worth, to kDecTailParts
+  // waves each: the waves dispatched last are short, so the launch does not end
+  // on a few long waves that cannot keep HBM busy.
+  DecParts dp{(int32_t)nitems, 1, 1};
   if (nitems > 0) {
     const int64_t keys = layer < 0 ? pl->total.decode_tokens : pl->stats[layer].decode_tokens;
     const int64_t recs = workspace_bytes / rec_bytes;
     const int64_t resident = decode_resident_waves(pl->D);
-    nparts = std::min<int64_t>({kDecMaxParts, resident / nitems, recs / nitems,
-                                keys / (nitems * 256)});
-    nparts = std::max<int64_t>(nparts, 1);
+    if (nitems < resident) {
+      const int64_t nparts = std::min<int64_t>({kDecMaxParts, resident / nitems, recs / nitems,
+                                                keys / (nitems * 256)});
+      dp.nh = (int32_t)std::max<int64_t>(nparts, 1);
+    } else if (recs > nitems && keys / (nitems * kDecTailParts) >= 256) {
+      const int64_t x = std::min<int64_t>({nitems, resident / kDecTailParts,
+                                           (recs - nitems) / (kDecTailParts - 1)});
+      dp = DecParts{(int32_t)(nitems - x), 1, kDecTailParts};
+    }
   }
   const int64_t nunits = sp.unit_e - sp.unit_b;
   if (nunits == 0) return SEGPAGED_OK;
@@ -1747,16 +1777,16 @@ SEGPAGED_API int segpaged_decode(const segpaged_plan* pl, int32_t layer, const v
   auto* vpp = (const uint16_t*)v_pool;
   auto* ws = (float*)workspace;
   if (nitems > 0) {
-    const dim3 grid((unsigned)((nitems * nparts + 3) / 4)), block(256);
+    const dim3 grid((unsigned)((dp.waves_before((int32_t)nitems) + 3) / 4)), block(256);
     if (pl->D == 128)
       hipLaunchKernelGGL(decode_partial_kernel<128>, grid, block, 0, st, d_table,
                          (int32_t)pl->off_pages, (int32_t)pl->off_dec,
-                         (int32_t)sp.dec_b, (int32_t)sp.dec_e, (int32_t)nparts, qq, qstride, kpp, vpp,
+                         (int32_t)sp.dec_b, (int32_t)sp.dec_e, dp, qq, qstride, kpp, vpp,
                          ws, pl->G, pl->Hq, pl->P, pl->log2P, c);
     else
       hipLaunchKernelGGL(decode_partial_kernel<64>, grid, block, 0, st, d_table,
                          (int32_t)pl->off_pages, (int32_t)pl->off_dec,
-                         (int32_t)sp.dec_b, (int32_t)sp.dec_e, (int32_t)nparts, qq, qstride, kpp, vpp,
+                         (int32_t)sp.dec_b, (int32_t)sp.dec_e, dp, qq, qstride, kpp, vpp,
                          ws, pl->G, pl->Hq, pl->P, pl->log2P, c);
     int rc = check_launch();
     if (rc) return rc;
@@ -1764,14 +1794,14 @@ SEGPAGED_API int segpaged_decode(const segpaged_plan* pl, int32_t layer, const v
   // Four waves per pair when some unit has many items and the pairs alone leave
   // the chip short of waves (under 64 per CU); otherwise four pairs per workgroup.
   const int64_t pairs = nunits * pl->G;
-  const int wpp = sp.max_unit_items * nparts > 16 && pairs < 64 * 256 ? 4 : 1;
+  const int wpp = sp.max_unit_items * std::max(dp.nh, dp.nt) > 16 && pairs < 64 * 256 ? 4 : 1;
   const int64_t per_wg = 4 / wpp;
   const dim3 grid((unsigned)((pairs + per_wg - 1) / per_wg)), block(256);
   auto* oo = (uint16_t*)o;
 #define SEGPAGED_LAUNCH_COMBINE(DD, WW)                                                          \
   hipLaunchKernelGGL((decode_combine_kernel<DD, WW>), grid, block, 0, st, d_table,               \
                      (int32_t)pl->off_decunits, (int32_t)sp.unit_b, (int32_t)sp.unit_e,         \
-                     (int32_t)sp.dec_b, (int32_t)nparts, ws, pl->G, pl->Hq, pl->B,              \
+                     (int32_t)sp.dec_b, dp, ws, pl->G, pl->Hq, pl->B,                           \
                      oo, lse,                                                                   \
                      (int32_t)(layer < 0))
   if (pl->D == 128) {

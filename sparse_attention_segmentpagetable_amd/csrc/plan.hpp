@@ -43,6 +43,11 @@ constexpr int kSelChunk = 2048;   // keys per workgroup of the top-p masses and 
 constexpr int kCtrInts = 16;      // prefill work counter line per layer (+1 for all layers);
                                   // its first 8 bytes: (launch generation << 32) | next item
 constexpr int64_t kDecMaxParts = 16;     // a decode item is dealt to at most 16 waves
+// A decode launch of several rounds of waves deals its last items to this many
+// waves each; the plan's decode workspace has room for the extra partials of
+// one round of 2048 waves (MI355X: 256 compute units x 8 resident waves).
+constexpr int32_t kDecTailParts = 4;
+constexpr int64_t kDecTailRecords = (2048 / kDecTailParts) * (kDecTailParts - 1);
 constexpr int64_t kNoAllocScratchBytes = SEGPAGED_NOALLOC_SCRATCH_BYTES;  // see segpaged.h
 
 struct LayerRange {

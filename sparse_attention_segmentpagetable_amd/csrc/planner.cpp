@@ -626,7 +626,7 @@ SEGPAGED_API int segpaged_plan_sizes(const segpaged_plan* pl, segpaged_sizes* z)
   z->kv_rows = pl->kv_rows;
   z->decode_items = pl->n_dec;
   z->prefill_items = pl->n_pre;
-  z->decode_workspace_bytes = pl->dec_cap * (int64_t)pl->G * (pl->D + 4) * 4;
+  z->decode_workspace_bytes = (pl->dec_cap + kDecTailRecords) * (int64_t)pl->G * (pl->D + 4) * 4;
   z->prefill_workspace_bytes = 0;
   {  // scores, masses and block partials of segpaged_select_topp at the largest lengths
     int64_t t_max = 0, n_max = 0;

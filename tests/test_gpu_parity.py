@@ -528,3 +528,43 @@ def test_graph_replay_of_prefill_and_decode():
         sp.decode(dplan, 0, dq, *args, o_e, workspace=dbufs["workspace"])
         torch.cuda.synchronize()
         assert np.array_equal(to_bits(o_e), to_bits(od_ref)), f"decode eager after replay {step}"
+
+
+def test_decode_last_items_in_four_parts():
+    """An all-layer decode launch of 4096 items of 1024 keys (16 layers x 2 sequences x
+    8 global KV heads x 16K keys; one K/V shared by the layers, Q per layer): two rounds
+    of the chip's resident decode waves, so the launch deals its last items (up to
+    512, the last layers') to 4 waves each and merges 4 partials for each of them.
+    Layer 0 and the last four layers (whose items hold the split ones) against the
+    oracle; every layer against the same layers launched one at a time (one round,
+    items dealt evenly)."""
+    L, B, Hkv, G, D, N = 16, 2, 8, 2, 128, 16384
+    spec = W.decode_form(W.Spec(name="tail", num_layers=L, num_q_heads=G * Hkv, num_kv_heads=Hkv,
+                                head_dim=D, page_size=64, seq_len=[N] * B, first_query_pos=[0] * B,
+                                kind=[W.GLOBAL] * (L * Hkv), sink=[0] * (L * Hkv),
+                                window=[1] * (L * Hkv), seed=31))
+    plan = sp.Plan(spec)
+    st = plan.stats(-1)
+    assert st["decode_items"] == 4096 and st["decode_tokens"] == 4096 * 1024
+    bufs = plan.allocate(DEV)
+    kb, vb = W.kv_bits(spec, 0)
+    kd, vd = to_dev(kb), to_dev(vb)
+    for l in range(L):
+        sp.build(plan, l, kd, vd, bufs["table"], bufs["k_pool"], bufs["v_pool"])
+    qs = [W.q_bits(spec, l) for l in range(L)]
+    q = to_dev(np.stack(qs))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    scale = 1 / np.sqrt(D)
+    args = (bufs["table"], bufs["k_pool"], bufs["v_pool"], scale)
+    sp.decode(plan, -1, q, *args, o, lse, workspace=bufs["workspace"])
+    o1 = torch.empty_like(q)
+    for l in range(L):
+        sp.decode(plan, l, q[l], *args, o1[l], workspace=bufs["workspace"])
+    torch.cuda.synchronize()
+    for l in range(L):
+        if l == 0 or l >= L - 4:
+            ref, ref_lse = OA.attention(spec, l, qs[l], kb, vb, scale=scale)
+            parity(to_f64(o[l]), ref, f"decode last items in 4 parts L{l}")
+            lse_parity(lse[l].cpu().numpy(), ref_lse, f"decode last items in 4 parts L{l}")
+        assert np.max(np.abs(to_f64(o[l]) - to_f64(o1[l]))) <= 2 ** -7  # fp32 merge order only

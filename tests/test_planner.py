@@ -164,7 +164,9 @@ def test_split_and_workspace_sizes():
     spec = W.tiny("decode")
     plan = sp.Plan(spec, decode_split_tokens=64)
     z = plan.sizes
-    assert z.decode_workspace_bytes == z.decode_items * spec.group * (spec.head_dim + 4) * 4
+    # one partial per item, plus the 1536 extra partials of the items a launch of
+    # several rounds deals to 4 waves each (512 items)
+    assert z.decode_workspace_bytes == (z.decode_items + 1536) * spec.group * (spec.head_dim + 4) * 4
     # global unit: 513 keys -> 9 items of <= 64; local: sink 4 + window 64 in one item
     # (the sink page's zero tail is a gap inside it)
     assert z.decode_items == 9 + 3 * 1
@@ -218,8 +220,10 @@ def test_call_validation_without_gpu():
                                 fake, None, None, 0, None) == -5
     assert lib.segpaged_prefill(plan.handle, 0, fake, fake, fake, fake, ctypes.c_float(-1.0),
                                 fake, None, None, 0, None) == -1
-    dplan = sp.Plan(W.tiny("decode"))
-    need = dplan.sizes.decode_workspace_bytes
+    dspec = W.tiny("decode")
+    dplan = sp.Plan(dspec)
+    need = dplan.stats(0)["decode_items"] * dspec.group * (dspec.head_dim + 4) * 4  # the call's items
+    assert need < dplan.sizes.decode_workspace_bytes
     assert lib.segpaged_decode(dplan.handle, 0, fake, fake, fake, fake, ctypes.c_float(0.1),
                                fake, None, fake, need - 1, None) == -3
     assert lib.segpaged_decode(dplan.handle, 0, fake, fake, fake, fake, ctypes.c_float(0.1),
