@@ -266,6 +266,18 @@ def _need(t, numel, name):
         raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
 
 
+def _pools(plan: Plan, k_pool, v_pool):
+    """Both pools bf16 and of the plan's size (NULL allowed when the plan has no pages)."""
+    import torch
+    for t, nm in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        if t is None:
+            if plan.sizes.pool_pages > 0:
+                raise ValueError(f"{nm} is needed: the plan has {plan.sizes.pool_pages} pages")
+            continue
+        _ptr(t, nm, torch.bfloat16)
+        _need(t, plan.sizes.pool_bytes // 2, nm)
+
+
 def _stream(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -351,6 +363,7 @@ def prefill(plan: Plan, layer: int, q, table, k_pool, v_pool, scale: float, o, l
         _need(lse, rows, "lse")
     _ptr(table, "table", torch.int32)
     _need(table, z.table_int32s, "table")
+    _pools(plan, k_pool, v_pool)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib().segpaged_prefill(plan.handle, layer, _ptr(q, "q"), _ptr(table, "t"),
                                    _ptr(k_pool, "kp", torch.bfloat16),
@@ -371,6 +384,7 @@ def append(plan: Plan, layer: int, k_new, v_new, table, k_pool, v_pool, stream=N
             _need(t, nl * t_new * plan.num_kv_heads * plan.head_dim, nm)
     _ptr(table, "table", torch.int32)
     _need(table, plan.sizes.table_int32s, "table")
+    _pools(plan, k_pool, v_pool)
     _check(_lib().segpaged_append(plan.handle, layer, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
                                   _ptr(table, "t"), _ptr(k_pool, "kp", torch.bfloat16),
                                   _ptr(v_pool, "vp", torch.bfloat16), _stream(stream)),
@@ -413,6 +427,7 @@ def decode(plan: Plan, layer: int, q, table, k_pool, v_pool, scale: float, o, ls
         _need(lse, rows, "lse")
     _ptr(table, "table", torch.int32)
     _need(table, plan.sizes.table_int32s, "table")
+    _pools(plan, k_pool, v_pool)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib().segpaged_decode(plan.handle, layer, _ptr(q, "q"), _ptr(table, "t"),
                                   _ptr(k_pool, "kp", torch.bfloat16),
@@ -439,6 +454,7 @@ def decode_noalloc(plan: Plan, layer: int, q, table, k_pool, v_pool, scale: floa
         _need(lse, rows, "lse")
     _ptr(table, "table", torch.int32)
     _need(table, plan.sizes.table_int32s, "table")
+    _pools(plan, k_pool, v_pool)
     _check(_lib().segpaged_decode_noalloc(plan.handle, layer, _ptr(q, "q"), _ptr(table, "t"),
                                           _ptr(k_pool, "kp", torch.bfloat16),
                                           _ptr(v_pool, "vp", torch.bfloat16), float(scale),

@@ -62,12 +62,12 @@ def test_decode_noalloc_rejects_partials_beyond_its_array():
     plan = sp.Plan(spec, decode_split_tokens=64)
     need = plan.sizes.decode_workspace_bytes
     assert need > sp.NOALLOC_SCRATCH_BYTES
-    small = torch.empty(4096, dtype=torch.int32, device=DEV)
+    # The call is refused before any launch, so the pools are never read.
+    pool = torch.empty(plan.sizes.pool_bytes // 2, dtype=torch.bfloat16, device=DEV)
     q = torch.zeros((4, 8, 64, 128), dtype=torch.bfloat16, device=DEV)
     o = torch.empty_like(q)
     table = torch.zeros(plan.sizes.table_int32s, dtype=torch.int32, device=DEV)
     with pytest.raises(sp.SegPagedError) as e:
-        sp.decode_noalloc(plan, -1, q, table, small.view(torch.bfloat16),
-                          small.view(torch.bfloat16), 0.1, o)
+        sp.decode_noalloc(plan, -1, q, table, pool, pool, 0.1, o)
     assert e.value.status == -3
     torch.cuda.synchronize()
