@@ -1071,7 +1071,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     run_push(rl, runs.a1, runs.n1, 0);
     run_push(rl, runs.a2, runs.n2, 1);
     run_push(rl, runs.a3, runs.n3, 1);
-    if (tid == 0) {
+    // Every wave writes its own copy (the same values): the issue cursor reads the
+    // list in the prologue, before any barrier, so a wave must not depend on
+    // another wave's write.
+    if (lane == 0) {
       sRun[0][0] = rl.k0; sRun[0][1] = rl.n0; sRun[0][2] = rl.s0;
       sRun[1][0] = rl.k1; sRun[1][1] = rl.n1; sRun[1][2] = rl.s1;
       sRun[2][0] = rl.k2; sRun[2][1] = rl.n2; sRun[2][2] = rl.s2;
