@@ -530,17 +530,18 @@ def test_graph_replay_of_prefill_and_decode():
         assert np.array_equal(to_bits(o_e), to_bits(od_ref)), f"decode eager after replay {step}"
 
 
-def test_decode_last_items_in_four_parts():
+@pytest.mark.parametrize("D,P,G", [(128, 64, 2), (64, 16, 4)])
+def test_decode_last_items_in_four_parts(D, P, G):
     """An all-layer decode launch of 4096 items of 1024 keys (16 layers x 2 sequences x
-    8 global KV heads x 16K keys; one K/V shared by the layers, Q per layer): two rounds
-    of the chip's resident decode waves, so the launch deals its last items (up to
-    512, the last layers') to 4 waves each and merges 4 partials for each of them.
-    Layer 0 and the last four layers (whose items hold the split ones) against the
-    oracle; every layer against the same layers launched one at a time (one round,
-    items dealt evenly)."""
-    L, B, Hkv, G, D, N = 16, 2, 8, 2, 128, 16384
+    8 global KV heads x 16K keys; one K/V shared by the layers, Q per layer): more
+    items than the chip holds decode waves at once (2048 at head dim 128, 3072 at 64),
+    so the launch deals its last items (up to 512, the last layers') to 4 waves each
+    and merges 4 partials for each of them. Layer 0 and the last four layers (whose
+    items hold the split ones) against the oracle; every layer against the same
+    layers launched one at a time (one round, items dealt evenly)."""
+    L, B, Hkv, N = 16, 2, 8, 16384
     spec = W.decode_form(W.Spec(name="tail", num_layers=L, num_q_heads=G * Hkv, num_kv_heads=Hkv,
-                                head_dim=D, page_size=64, seq_len=[N] * B, first_query_pos=[0] * B,
+                                head_dim=D, page_size=P, seq_len=[N] * B, first_query_pos=[0] * B,
                                 kind=[W.GLOBAL] * (L * Hkv), sink=[0] * (L * Hkv),
                                 window=[1] * (L * Hkv), seed=31))
     plan = sp.Plan(spec)
@@ -565,6 +566,6 @@ def test_decode_last_items_in_four_parts():
     for l in range(L):
         if l == 0 or l >= L - 4:
             ref, ref_lse = OA.attention(spec, l, qs[l], kb, vb, scale=scale)
-            parity(to_f64(o[l]), ref, f"decode last items in 4 parts L{l}")
-            lse_parity(lse[l].cpu().numpy(), ref_lse, f"decode last items in 4 parts L{l}")
+            parity(to_f64(o[l]), ref, f"decode last items in 4 parts D{D} P{P} L{l}")
+            lse_parity(lse[l].cpu().numpy(), ref_lse, f"decode last items in 4 parts D{D} L{l}")
         assert np.max(np.abs(to_f64(o[l]) - to_f64(o1[l]))) <= 2 ** -7  # fp32 merge order only
